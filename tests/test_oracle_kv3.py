@@ -1,0 +1,86 @@
+"""Pins for the oracle's 3-bit KV codec."""
+import json
+import os
+
+import numpy as np
+
+from oracle import kv3
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _g():
+    with open(os.path.join(GOLD, "kv_worked.json")) as f:
+        return json.load(f)
+
+
+def test_worked_example():
+    g = _g()
+    x = np.array(g["x"], dtype=np.float32)
+    q3, s3 = kv3.quantize(x, 3, -4, 3)
+    assert q3.tolist() == g["codes3"] and s3 == np.float32(g["scale3"])
+    q4, s4 = kv3.quantize(x, 7, -8, 7)
+    assert q4.tolist() == g["codes4"] and hex(np.float32(s4).view(np.uint32)) == g["scale4_f32_bits"]
+
+
+def test_plane_layout_single_codes():
+    D = 64
+    for pos, code in [(0, 1), (0, -1), (31, -4), (32, 3), (45, -2), (63, 2)]:
+        q = np.zeros(D, dtype=np.int8)
+        q[pos] = code
+        p = kv3.planes_encode(q)
+        assert p.size == 3 * D // 8
+        words = p.view("<u4")
+        g, i = divmod(pos, 32)
+        u = code & 7
+        expect = np.zeros(6, dtype=np.uint32)
+        for j in range(3):
+            if (u >> j) & 1:
+                expect[3 * g + j] = 1 << i
+        assert np.array_equal(words, expect), (pos, code)
+        assert np.array_equal(kv3.planes_decode(p, D), q)
+
+
+def _case(seed, B=2, S=9, H=3, D=64):
+    rs = np.random.default_rng(seed)
+    x = (rs.standard_normal((B, S, H, D)) * rs.lognormal(0, 0.5, size=(1, 1, H, 1))).astype(np.float32)
+    slot_of = np.full((B, S), -1, dtype=np.int32)
+    slot_of[0, 0], slot_of[0, 4], slot_of[1, 0] = 0, 1, 2
+    return x, slot_of, 3
+
+
+def test_roundtrip_error_bounds_and_specials():
+    x, slot_of, ns = _case(30)
+    p3, s3, p4, s4 = kv3.kv_pack3(x, slot_of, ns)
+    y = kv3.kv_unpack3(p3, s3, p4, s4, slot_of, x.shape[-1])
+    a = np.abs(x).max(axis=-1)
+    err = np.abs(y.astype(np.float64) - x)
+    special = slot_of >= 0
+    bound3 = (a / 3)[..., None] * (0.5 + 2.0**-19)
+    bound4 = (a / 7)[..., None] * (0.5 + 2.0**-19)
+    assert np.all(err[~special] <= bound3[~special])
+    assert np.all(err[special] <= bound4[special])
+    q3 = kv3.planes_decode(p3, x.shape[-1])
+    assert q3.min() >= -3 and q3.max() <= 3
+    q4 = kv3.nibbles_decode(p4)
+    assert q4.min() >= -7 and q4.max() <= 7
+    # special positions are strictly better than their 3-bit codes would be on average
+    y3 = q3.astype(np.float32) * s3[..., None]
+    assert np.abs(y3[special] - x[special]).mean() > err[special].mean()
+
+
+def test_idempotence():
+    x, slot_of, ns = _case(31)
+    p3, s3, p4, s4 = kv3.kv_pack3(x, slot_of, ns)
+    y = kv3.kv_unpack3(p3, s3, p4, s4, slot_of, x.shape[-1])
+    p3b, s3b, p4b, s4b = kv3.kv_pack3(y, slot_of, ns)
+    # ordinary positions: the 3-bit codes reproduce exactly
+    ordinary = slot_of < 0
+    assert np.array_equal(p3b[ordinary], p3[ordinary])
+    assert np.array_equal(p4b, p4)
+
+
+def test_zero_vector():
+    x = np.zeros((1, 1, 1, 32), dtype=np.float32)
+    p3, s3, p4, s4 = kv3.kv_pack3(x, np.full((1, 1), -1, np.int32), 0)
+    assert np.all(p3 == 0) and s3[0, 0, 0] == np.float32(1e-5) / np.float32(3)
