@@ -1,0 +1,218 @@
+/*
+ * bw.h -- C ABI of the BitNet a4.8 hybrid-quantized BitLinear library for
+ * AMD MI355X (gfx950).  Library: ternary_weight_bit_amd/libbw.so.
+ *
+ * What the calls compute is stated on the BitNet a4.8 pages:
+ *   - "BitNet a4.8: 4-bit Activations for 1-bit LLMs", abstract (arXiv
+ *     2411.04965v1): ternary-weight layers take 4-bit activations at the
+ *     inputs of attention and FFN (INT4/FP4 kernels) and sparsified, then
+ *     8-bit, intermediate states; the model supports a 3-bit KV cache;
+ *   - toshoseti review of the paper, «Метод»: 4-bit activations for the
+ *     q/k/v/gate/up inputs only, top-k sparsification (50 %) of the out
+ *     projection input, ReLU^2 in place of swish in the FFN gate, FP4 as the
+ *     wide-range alternative to INT4; opening lines: ternary weights,
+ *     absmax INT8 activations (b1.58); «Эксперименты»: 3-bit KV caches with
+ *     bos/eos tokens kept at 4 bits.
+ * The pages give no formula; the exact arithmetic each call follows is stated
+ * in its comment below.
+ *
+ * Conventions (all calls):
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller allocates
+ *     and owns every buffer; the library allocates nothing and keeps no
+ *     device state.  Device pointers must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue work
+ *     on it and return without waiting.
+ *   - Arguments are validated on the host before anything is launched.  A
+ *     status other than BW_OK means nothing was enqueued and the outputs are
+ *     untouched; bw_last_error() (host, per thread) then holds a message.
+ *     A HIP launch failure returns BW_ERR_HIP.  No C++ exception crosses
+ *     this interface.
+ *   - M == 0 (or B*S == 0) is a valid empty call: BW_OK, nothing launched.
+ *   - Arithmetic: IEEE fp32 with round-half-to-even, one correctly-rounded
+ *     operation at a time (no fused multiply-add) wherever a float decides a
+ *     code; a' = max(absmax, 1e-5).
+ *   - Calls that overlap on one stream-ordered buffer race; calls on
+ *     different buffers are independent.
+ */
+#ifndef BW_H_
+#define BW_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BW_ABI_VERSION 1
+#define BW_PACK_LAYOUT_VERSION 1
+
+typedef enum {
+  BW_OK = 0,
+  BW_ERR_NULL = 1,        /* a required pointer is NULL */
+  BW_ERR_SHAPE = 2,       /* a size breaks the shape rules of the call */
+  BW_ERR_ALIGN = 3,       /* a device pointer is not 16-byte aligned */
+  BW_ERR_DTYPE = 4,       /* unknown dtype / format / role enum */
+  BW_ERR_ARG = 5,         /* other bad argument (k_keep, workspace size, ...) */
+  BW_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
+  BW_ERR_UNSUPPORTED = 7  /* valid request this build does not implement */
+} bw_status;
+
+typedef enum { BW_F32 = 0, BW_BF16 = 1 } bw_dtype;
+
+typedef enum {
+  BW_ACT_INT4 = 0,     /* two's-complement 4-bit integers, absmax scale a'/7 */
+  BW_ACT_FP4_E2M1 = 1  /* e2m1 floats (magnitudes 0,.5,1,1.5,2,3,4,6), scale a'/6 */
+} bw_act4_fmt;
+
+/* Which activations a packed weight meets; selects the within-word order of
+ * the 2-bit codes (both orders are 2 bits per weight, same tile structure). */
+typedef enum {
+  BW_ROLE_A4 = 0, /* q/k/v/gate/up: meets 4-bit activations (bw_bitlinear_a4) */
+  BW_ROLE_A8 = 1  /* out_proj/down_proj: meets 8-bit codes (bw_bitlinear_sparse_a8) */
+} bw_weight_role;
+
+/* host */ int bw_abi_version(void);
+/* host */ int bw_pack_layout_version(void);
+/* host: message for the last non-OK status returned on this thread ("" if none) */
+const char* bw_last_error(void);
+
+/* ------------------------------------------------------------------------ *
+ * Ternary weights (offline, once per weight tensor).
+ * Source: toshoseti review, opening lines -- BitNet b1.58 (whose weights
+ * BitNet a4.8 keeps) uses ternary {-1, 0, +1} weights.
+ *
+ * Computes, for one tensor W[N][K] (nn.Linear out x in, row-major):
+ *   beta  = fp32( fp64(sum |w|) / (N*K) ), with the sum over all N*K
+ *           magnitudes formed exactly and rounded once to fp64;
+ *   beta' = max(beta, 1e-5);
+ *   t     = sign(w) * [2|w| > beta']   (RoundClip(w/beta', -1, 1), ties to 0)
+ * and writes t packed at 2 bits per weight, codes 00 = 0, 01 = +1, 11 = -1:
+ *   tiles of 16 output channels x 64 inputs, 256 bytes each, at byte offset
+ *   (nb*(K/64) + kb)*256; inside a tile channel c owns bytes [16c, 16c+16) as
+ *   four little-endian uint32 words, word j covering inputs 64kb+16j+(0..15);
+ *   code slot i (bits 2i..2i+1) holds input offset
+ *     BW_ROLE_A4: (i odd ? 8 : 0) + i/2
+ *     BW_ROLE_A8: 4*(i%4) + i/4
+ * beta[N] (fp32) receives beta' in every entry, so the packed bytes and beta
+ * arrays of separately-scaled tensors (fused q/k/v, gate/up) concatenate
+ * along N.
+ *
+ * Shapes: N % 16 == 0, K % 64 == 0, N, K >= 1, N*K < 2^40.  W dtype BW_F32
+ * or BW_BF16.  Non-finite weights are not supported.
+ * workspace: device, >= bw_pack_ternary_workspace_bytes(N, K) bytes; its
+ * contents on entry are ignored (the call clears what it uses).
+ * ------------------------------------------------------------------------ */
+/* host */ size_t bw_ternary_packed_bytes(int64_t N, int64_t K);
+/* host */ size_t bw_pack_ternary_workspace_bytes(int64_t N, int64_t K);
+bw_status bw_pack_ternary(const void* W, bw_dtype w_dtype, int64_t N, int64_t K,
+                          bw_weight_role role, uint8_t* w_packed, float* beta,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * 4-bit activation quantizer (inputs of q/k/v/gate/up).
+ * Source: BitNet a4.8 abstract (4-bit activations for the attention and FFN
+ * inputs, INT4/FP4 kernels); toshoseti review «Метод» (only q/k/v/gate/up
+ * get 4 bits; FP4 considered for its wider range).
+ *
+ * Per token (row) m of x[M][K]: a' = max(max_k |x|, 1e-5);
+ *   BW_ACT_INT4:     inv = fl(7/a'), s = fl(a'/7), q = clamp(rne(fl(x*inv)), -8, 7)
+ *   BW_ACT_FP4_E2M1: inv = fl(6/a'), s = fl(a'/6), t = fl(x*inv) rounded to the
+ *                    nearest e2m1 magnitude (ties to the even code, saturate
+ *                    at 6), sign bit copied from t.
+ * codes[M][K/2] (uint8): two codes per byte, even k in the low nibble.
+ * scales[M] (fp32): s.
+ * Shapes: K % 64 == 0, K <= 131072.  x dtype BW_F32 or BW_BF16.
+ * ------------------------------------------------------------------------ */
+bw_status bw_quantize(const void* x, bw_dtype x_dtype, int64_t M, int64_t K, bw_act4_fmt fmt,
+                      uint8_t* codes, float* scales, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * W1.58A4 BitLinear: 4-bit activation codes x ternary weights.
+ * Source: BitNet a4.8 abstract (ternary layers on 4-bit activations, run by
+ * INT4/FP4 kernels).
+ *
+ *   acc[m][n] = sum_k v(codes[m][k]) * t[n][k]   (v = integer code, or the
+ *               e2m1 value; exact: int32, resp. fp32 multiples of 1/2)
+ *   y[m][n]   = fl( fl(acc * x_scales[m]) * beta[n] )
+ * codes/x_scales: as written by bw_quantize with the same fmt.  w_packed:
+ * BW_ROLE_A4 layout of t[N][K].  y: fp32 [M][N] row-major.
+ * acc_dbg: NULL, or [M][N] receiving acc (int32 for BW_ACT_INT4, fp32 for
+ * BW_ACT_FP4_E2M1), for exactness checks.
+ * Shapes: K % 64 == 0, K <= 131072, N % 16 == 0.
+ * ------------------------------------------------------------------------ */
+bw_status bw_bitlinear_a4(const uint8_t* codes, const float* x_scales, int64_t M, int64_t K,
+                          bw_act4_fmt fmt, const uint8_t* w_packed, const float* beta,
+                          int64_t N, float* y, void* acc_dbg, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Sparsified 8-bit activations (inputs of out_proj and down_proj).
+ * Source: BitNet a4.8 abstract (intermediate states sparsified, then 8-bit);
+ * toshoseti review «Метод» (top-k at 50 % for the out projection input;
+ * ReLU^2 gate to sparsify the down projection input); 9pt.com article,
+ * methodology (low-magnitude entries are the ones dropped); toshoseti
+ * review, opening lines (absmax INT8).
+ *
+ * Per token m: h = up ? fl(fl(r*r) * up) with r = max(gate, 0) : x;
+ * survivors = the k_keep entries first in the order (|h| descending, index
+ * ascending); a' = max(max |h| over survivors, 1e-5); inv = fl(127/a');
+ * codes = clamp(rne(fl(h*inv)), -128, 127) for survivors, 0 otherwise;
+ * scales[m] = fl(a'/127).
+ * up: NULL selects the plain-input front end (out_proj).  k_keep = K turns
+ * the sparsifier off (the b1.58 INT8 path).
+ * codes: int8 [M][K].  mask_dbg: NULL, or uint32 [M][K/32] with bit i of
+ * word w set when entry 32w+i survives.
+ * Shapes: K % 64 == 0, K <= 16384, 1 <= k_keep <= K.  dtype BW_F32 or BW_BF16
+ * (gate and up share it).
+ * ------------------------------------------------------------------------ */
+bw_status bw_quantize_sparse_a8(const void* gate_or_x, const void* up, bw_dtype dtype,
+                                int64_t M, int64_t K, int64_t k_keep, int8_t* codes,
+                                float* scales, uint32_t* mask_dbg, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * W1.58A8 BitLinear on the sparsified INT8 codes.
+ * Source: as bw_quantize_sparse_a8 (8-bit codes feeding ternary layers).
+ *   acc[m][n] = sum_k codes[m][k] * t[n][k]  (int32, exact)
+ *   y[m][n]   = fl( fl(acc * x_scales[m]) * beta[n] )
+ * w_packed: BW_ROLE_A8 layout.  acc_dbg: NULL or int32 [M][N].
+ * Shapes: K % 64 == 0, K <= 131072, N % 16 == 0.
+ * ------------------------------------------------------------------------ */
+bw_status bw_bitlinear_sparse_a8(const int8_t* codes, const float* x_scales, int64_t M, int64_t K,
+                                 const uint8_t* w_packed, const float* beta, int64_t N, float* y,
+                                 int32_t* acc_dbg, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * 3-bit KV cache with 4-bit special tokens.
+ * Source: toshoseti review «Эксперименты» (3-bit KV caches; bos/eos tokens
+ * kept at 4 bits); BitNet a4.8 abstract (3-bit KV cache).
+ *
+ * kv: [B][S][H][D] (BW_F32 or BW_BF16).  Per vector v = kv[b][s][h][:]:
+ *   a' = max(max |v|, 1e-5);
+ *   3-bit: s3 = fl(a'/3), q = clamp(rne(fl(v*fl(3/a'))), -4, 3) (always written);
+ *   if 0 <= slot_of[b][s] < n_special (a special token): also
+ *          s4 = fl(a'/7), q4 = clamp(rne(fl(v*fl(7/a'))), -8, 7) into that slot.
+ * p3: uint8 [B][S][H][3*D/8]; per group of 32 codes three little-endian
+ *     uint32 bit planes, plane j holding bit j of each code's 3-bit two's
+ *     complement at bit (index mod 32).  s3: fp32 [B][S][H].
+ * p4: uint8 [n_special][H][D/2], even d in the low nibble.  s4: fp32
+ *     [n_special][H].  Slots no position names are left untouched.
+ * slot_of: int32 [B][S]; values outside [0, n_special) mark ordinary tokens.
+ *     Two positions naming one slot race.
+ * unpack: out[b][s][h][d] = fl(q * s) from the side slot for special tokens,
+ *     from the 3-bit slab otherwise; BW_BF16 output is that fp32 value
+ *     rounded half-to-even.
+ * Shapes: D in {32, 64, 128, 256, 512}; n_special >= 0 (p4/s4 may be NULL
+ * when n_special == 0).
+ * ------------------------------------------------------------------------ */
+bw_status bw_kv_pack3(const void* kv, bw_dtype dtype, int64_t B, int64_t S, int64_t H, int64_t D,
+                      const int32_t* slot_of, int64_t n_special, uint8_t* p3, float* s3,
+                      uint8_t* p4, float* s4, void* stream);
+bw_status bw_kv_unpack3(const uint8_t* p3, const float* s3, const uint8_t* p4, const float* s4,
+                        const int32_t* slot_of, int64_t B, int64_t S, int64_t H, int64_t D,
+                        int64_t n_special, bw_dtype out_dtype, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BW_H_ */

@@ -19,15 +19,29 @@ import numpy as np
 from . import act4
 
 
+def _exact_int_matmul(a: np.ndarray, b_t: np.ndarray) -> np.ndarray:
+    """a @ b_t^T for integer matrices, returned as int64.  Computed with an fp64
+    matmul, which is exact whatever the summation order because every product
+    and partial sum is an integer of magnitude at most max|a| * max|b| * K,
+    checked here to stay below 2^53."""
+    a = np.asarray(a)
+    b_t = np.asarray(b_t)
+    K = a.shape[1]
+    bound = float(np.abs(a).max(initial=0)) * float(np.abs(b_t).max(initial=0)) * K
+    if bound >= 2.0**53:
+        raise ValueError("integer contraction too large for exact fp64 evaluation")
+    return (a.astype(np.float64) @ b_t.astype(np.float64).T).astype(np.int64)
+
+
 def contract(q: np.ndarray, t: np.ndarray) -> np.ndarray:
-    """acc = q @ t^T as exact int64 (q [M][K] ints, t [N][K] ternary)."""
-    return np.asarray(q, dtype=np.int64) @ np.asarray(t, dtype=np.int64).T
+    """acc = q @ t^T as exact integers (q [M][K] ints, t [N][K] ternary), int64."""
+    return _exact_int_matmul(q, t)
 
 
 def contract_e2m1_doubled(codes: np.ndarray, t: np.ndarray) -> np.ndarray:
-    """2 * sum_k e2m1(codes[m][k]) * t[n][k] as exact int64."""
+    """2 * sum_k e2m1(codes[m][k]) * t[n][k] as exact int64 (doubled values are integers)."""
     twice = np.rint(2.0 * act4.e2m1_decode(codes)).astype(np.int64)
-    return twice @ np.asarray(t, dtype=np.int64).T
+    return _exact_int_matmul(twice, t)
 
 
 def epilogue(acc: np.ndarray, s_x: np.ndarray, beta: np.ndarray) -> np.ndarray:

@@ -1,0 +1,247 @@
+"""Python binding of libbw, the gfx950 BitNet a4.8 BitLinear library.
+
+The functions carry the names of the C entry points declared in
+include/bw.h and only marshal arguments: they check tensor dtype, shape,
+device and contiguity, allocate missing outputs with torch, and pass raw
+device pointers plus torch's current HIP stream to the library.  Every step
+of the computation runs in the library's HIP kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "BW_OK", "BW_F32", "BW_BF16", "BW_ACT_INT4", "BW_ACT_FP4_E2M1", "BW_ROLE_A4", "BW_ROLE_A8",
+    "BwError", "lib_path", "bw_abi_version", "bw_pack_layout_version", "bw_last_error",
+    "bw_ternary_packed_bytes", "bw_pack_ternary_workspace_bytes", "bw_pack_ternary", "bw_quantize",
+    "bw_bitlinear_a4", "bw_quantize_sparse_a8", "bw_bitlinear_sparse_a8", "bw_kv_pack3", "bw_kv_unpack3",
+]
+
+BW_OK = 0
+STATUS_NAMES = {
+    0: "BW_OK", 1: "BW_ERR_NULL", 2: "BW_ERR_SHAPE", 3: "BW_ERR_ALIGN", 4: "BW_ERR_DTYPE",
+    5: "BW_ERR_ARG", 6: "BW_ERR_HIP", 7: "BW_ERR_UNSUPPORTED",
+}
+BW_F32, BW_BF16 = 0, 1
+BW_ACT_INT4, BW_ACT_FP4_E2M1 = 0, 1
+BW_ROLE_A4, BW_ROLE_A8 = 0, 1
+
+lib_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbw.so")
+
+
+class BwError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(lib_path):
+        raise ImportError(
+            f"{lib_path} is not built; run `python -m ternary_weight_bit_amd._build` (hipcc, gfx950)"
+        )
+    lib = ctypes.CDLL(lib_path)
+    P, I64, SZ, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+    sig = {
+        "bw_abi_version": ([], I),
+        "bw_pack_layout_version": ([], I),
+        "bw_last_error": ([], ctypes.c_char_p),
+        "bw_ternary_packed_bytes": ([I64, I64], SZ),
+        "bw_pack_ternary_workspace_bytes": ([I64, I64], SZ),
+        "bw_pack_ternary": ([P, I, I64, I64, I, P, P, P, SZ, P], I),
+        "bw_quantize": ([P, I, I64, I64, I, P, P, P], I),
+        "bw_bitlinear_a4": ([P, P, I64, I64, I, P, P, I64, P, P, P], I),
+        "bw_quantize_sparse_a8": ([P, P, I, I64, I64, I64, P, P, P, P], I),
+        "bw_bitlinear_sparse_a8": ([P, P, I64, I64, P, P, I64, P, P, P], I),
+        "bw_kv_pack3": ([P, I, I64, I64, I64, I64, P, I64, P, P, P, P, P], I),
+        "bw_kv_unpack3": ([P, P, P, P, P, I64, I64, I64, I64, I64, I, P, P], I),
+    }
+    for name, (argt, rest) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = argt
+        fn.restype = rest
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status: int) -> None:
+    if status != BW_OK:
+        raise BwError(status, _lib.bw_last_error().decode())
+
+
+def _dev(t: torch.Tensor, name: str, dtypes=None, shape=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _opt(t, name, dtypes=None, shape=None) -> int | None:
+    return None if t is None else _dev(t, name, dtypes, shape)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _fdtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return BW_F32
+    if t.dtype == torch.bfloat16:
+        return BW_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
+
+
+_FLOATS = (torch.float32, torch.bfloat16)
+
+
+def bw_abi_version() -> int:
+    return _lib.bw_abi_version()
+
+
+def bw_pack_layout_version() -> int:
+    return _lib.bw_pack_layout_version()
+
+
+def bw_last_error() -> str:
+    return _lib.bw_last_error().decode()
+
+
+def bw_ternary_packed_bytes(N: int, K: int) -> int:
+    return _lib.bw_ternary_packed_bytes(N, K)
+
+
+def bw_pack_ternary_workspace_bytes(N: int, K: int) -> int:
+    return _lib.bw_pack_ternary_workspace_bytes(N, K)
+
+
+def bw_pack_ternary(W: torch.Tensor, role: int, w_packed=None, beta=None, workspace=None):
+    """Absmean-ternarize W [N][K] and pack it; returns (w_packed uint8 [N*K/4], beta fp32 [N])."""
+    N, K = W.shape
+    dev = W.device
+    if w_packed is None:
+        w_packed = torch.empty(bw_ternary_packed_bytes(N, K), dtype=torch.uint8, device=dev)
+    if beta is None:
+        beta = torch.empty(N, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(bw_pack_ternary_workspace_bytes(N, K), dtype=torch.uint8, device=dev)
+    _check(_lib.bw_pack_ternary(
+        _dev(W, "W", _FLOATS), _fdtype(W), N, K, role,
+        _dev(w_packed, "w_packed", (torch.uint8,), (N * K // 4,)),
+        _dev(beta, "beta", (torch.float32,), (N,)),
+        _dev(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(W)))
+    return w_packed, beta
+
+
+def bw_quantize(x: torch.Tensor, fmt: int, codes=None, scales=None):
+    """Per-token 4-bit quantizer; returns (codes uint8 [M][K/2], scales fp32 [M])."""
+    M, K = x.shape
+    if codes is None:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(M, dtype=torch.float32, device=x.device)
+    _check(_lib.bw_quantize(
+        _dev(x, "x", _FLOATS), _fdtype(x), M, K, fmt,
+        _dev(codes, "codes", (torch.uint8,), (M, K // 2)),
+        _dev(scales, "scales", (torch.float32,), (M,)), _stream(x)))
+    return codes, scales
+
+
+def bw_bitlinear_a4(codes: torch.Tensor, x_scales: torch.Tensor, fmt: int, w_packed: torch.Tensor,
+                    beta: torch.Tensor, y=None, acc_dbg=None):
+    """y [M][N] fp32 = ternary(W) applied to 4-bit activations (codes from bw_quantize)."""
+    M, Kh = codes.shape
+    K = 2 * Kh
+    N = beta.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=codes.device)
+    acc_dt = (torch.int32,) if fmt == BW_ACT_INT4 else (torch.float32,)
+    _check(_lib.bw_bitlinear_a4(
+        _dev(codes, "codes", (torch.uint8,)), _dev(x_scales, "x_scales", (torch.float32,), (M,)), M, K, fmt,
+        _dev(w_packed, "w_packed", (torch.uint8,), (N * K // 4,)),
+        _dev(beta, "beta", (torch.float32,), (N,)), N,
+        _dev(y, "y", (torch.float32,), (M, N)),
+        _opt(acc_dbg, "acc_dbg", acc_dt, (M, N)), _stream(codes)))
+    return y
+
+
+def bw_quantize_sparse_a8(gate_or_x: torch.Tensor, up=None, k_keep=None, codes=None, scales=None,
+                          mask_dbg=None):
+    """ReLU^2 gate (when up is given) + per-token top-k + INT8; returns (codes int8 [M][K], scales fp32 [M])."""
+    M, K = gate_or_x.shape
+    if k_keep is None:
+        k_keep = K // 2
+    if up is not None and (up.dtype != gate_or_x.dtype or up.shape != gate_or_x.shape):
+        raise ValueError("up must match gate in dtype and shape")
+    if codes is None:
+        codes = torch.empty((M, K), dtype=torch.int8, device=gate_or_x.device)
+    if scales is None:
+        scales = torch.empty(M, dtype=torch.float32, device=gate_or_x.device)
+    _check(_lib.bw_quantize_sparse_a8(
+        _dev(gate_or_x, "gate_or_x", _FLOATS), _opt(up, "up", _FLOATS), _fdtype(gate_or_x), M, K, k_keep,
+        _dev(codes, "codes", (torch.int8,), (M, K)), _dev(scales, "scales", (torch.float32,), (M,)),
+        _opt(mask_dbg, "mask_dbg", (torch.int32, torch.uint32), (M, K // 32)), _stream(gate_or_x)))
+    return codes, scales
+
+
+def bw_bitlinear_sparse_a8(codes: torch.Tensor, x_scales: torch.Tensor, w_packed: torch.Tensor,
+                           beta: torch.Tensor, y=None, acc_dbg=None):
+    """y [M][N] fp32 = ternary(W) applied to INT8 codes (from bw_quantize_sparse_a8)."""
+    M, K = codes.shape
+    N = beta.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=codes.device)
+    _check(_lib.bw_bitlinear_sparse_a8(
+        _dev(codes, "codes", (torch.int8,)), _dev(x_scales, "x_scales", (torch.float32,), (M,)), M, K,
+        _dev(w_packed, "w_packed", (torch.uint8,), (N * K // 4,)),
+        _dev(beta, "beta", (torch.float32,), (N,)), N,
+        _dev(y, "y", (torch.float32,), (M, N)), _opt(acc_dbg, "acc_dbg", (torch.int32,), (M, N)),
+        _stream(codes)))
+    return y
+
+
+def bw_kv_pack3(kv: torch.Tensor, slot_of: torch.Tensor, n_special: int, p3=None, s3=None, p4=None, s4=None):
+    """3-bit KV pack; returns (p3 uint8 [B][S][H][3D/8], s3 fp32 [B][S][H], p4 uint8 [n][H][D/2], s4 fp32 [n][H])."""
+    B, S, H, D = kv.shape
+    dev = kv.device
+    if p3 is None:
+        p3 = torch.empty((B, S, H, 3 * D // 8), dtype=torch.uint8, device=dev)
+    if s3 is None:
+        s3 = torch.empty((B, S, H), dtype=torch.float32, device=dev)
+    if p4 is None:
+        p4 = torch.zeros((max(n_special, 1), H, D // 2), dtype=torch.uint8, device=dev)
+    if s4 is None:
+        s4 = torch.zeros((max(n_special, 1), H), dtype=torch.float32, device=dev)
+    _check(_lib.bw_kv_pack3(
+        _dev(kv, "kv", _FLOATS), _fdtype(kv), B, S, H, D,
+        _dev(slot_of, "slot_of", (torch.int32,), (B, S)), n_special,
+        _dev(p3, "p3", (torch.uint8,), (B, S, H, 3 * D // 8)), _dev(s3, "s3", (torch.float32,), (B, S, H)),
+        _dev(p4, "p4", (torch.uint8,)), _dev(s4, "s4", (torch.float32,)), _stream(kv)))
+    return p3, s3, p4, s4
+
+
+def bw_kv_unpack3(p3: torch.Tensor, s3: torch.Tensor, p4: torch.Tensor, s4: torch.Tensor,
+                  slot_of: torch.Tensor, n_special: int, out_dtype=torch.float32, out=None):
+    """Dequantize the 3-bit KV cache; returns out [B][S][H][D] (fp32 or bf16)."""
+    B, S, H, pd = p3.shape
+    D = pd * 8 // 3
+    if out is None:
+        out = torch.empty((B, S, H, D), dtype=out_dtype, device=p3.device)
+    _check(_lib.bw_kv_unpack3(
+        _dev(p3, "p3", (torch.uint8,)), _dev(s3, "s3", (torch.float32,), (B, S, H)),
+        _dev(p4, "p4", (torch.uint8,)), _dev(s4, "s4", (torch.float32,)),
+        _dev(slot_of, "slot_of", (torch.int32,), (B, S)), B, S, H, D, n_special, _fdtype(out),
+        _dev(out, "out", _FLOATS, (B, S, H, D)), _stream(p3)))
+    return out

@@ -1,0 +1,191 @@
+// C ABI of libbw: host-side argument validation and dispatch to the gfx950
+// kernels.  Every check runs before anything is enqueued, so a non-OK status
+// leaves the outputs untouched.  See include/bw.h for the contract.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/bw.h"
+#include "bw_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+bw_status fail(bw_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bw_status ok() {
+  g_err[0] = '\0';
+  return BW_OK;
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+bw_status hip_status(hipError_t e, const char* where) {
+  if (e != hipSuccess) return fail(BW_ERR_HIP, "%s: HIP error %d (%s)", where, static_cast<int>(e), hipGetErrorString(e));
+  return ok();
+}
+
+#define BW_REQUIRE(cond, st, ...) \
+  do {                            \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+constexpr int64_t kMaxK = 131072;
+constexpr int64_t kMaxKSparse = 16384;
+
+}  // namespace
+
+extern "C" {
+
+int bw_abi_version(void) { return BW_ABI_VERSION; }
+int bw_pack_layout_version(void) { return BW_PACK_LAYOUT_VERSION; }
+const char* bw_last_error(void) { return g_err; }
+
+size_t bw_ternary_packed_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0) return 0;
+  return static_cast<size_t>(N) * static_cast<size_t>(K) / 4;
+}
+
+size_t bw_pack_ternary_workspace_bytes(int64_t N, int64_t K) {
+  (void)N;
+  (void)K;
+  return bw::kPackWorkspaceBytes;
+}
+
+bw_status bw_pack_ternary(const void* W, bw_dtype w_dtype, int64_t N, int64_t K, bw_weight_role role,
+                          uint8_t* w_packed, float* beta, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  BW_REQUIRE(W && w_packed && beta && workspace, BW_ERR_NULL, "bw_pack_ternary: NULL pointer");
+  BW_REQUIRE(w_dtype == BW_F32 || w_dtype == BW_BF16, BW_ERR_DTYPE, "bw_pack_ternary: bad dtype %d", (int)w_dtype);
+  BW_REQUIRE(role == BW_ROLE_A4 || role == BW_ROLE_A8, BW_ERR_DTYPE, "bw_pack_ternary: bad role %d", (int)role);
+  BW_REQUIRE(N >= 1 && K >= 1 && N % 16 == 0 && K % 64 == 0, BW_ERR_SHAPE,
+             "bw_pack_ternary: need N %% 16 == 0 and K %% 64 == 0 (N=%lld K=%lld)", (long long)N, (long long)K);
+  BW_REQUIRE(N <= (int64_t(1) << 40) / K, BW_ERR_SHAPE, "bw_pack_ternary: N*K must be below 2^40");
+  BW_REQUIRE(!misaligned(W) && !misaligned(w_packed) && !misaligned(beta) && !misaligned(workspace),
+             BW_ERR_ALIGN, "bw_pack_ternary: device pointers must be 16-byte aligned");
+  BW_REQUIRE(workspace_bytes >= bw::kPackWorkspaceBytes, BW_ERR_ARG,
+             "bw_pack_ternary: workspace needs %zu bytes, got %zu", bw::kPackWorkspaceBytes, workspace_bytes);
+  return hip_status(bw::launch_pack_ternary(W, w_dtype == BW_BF16, N, K, role, w_packed, beta, workspace,
+                                            static_cast<hipStream_t>(stream)),
+                    "bw_pack_ternary");
+}
+
+bw_status bw_quantize(const void* x, bw_dtype x_dtype, int64_t M, int64_t K, bw_act4_fmt fmt, uint8_t* codes,
+                      float* scales, void* stream) {
+  BW_REQUIRE(x_dtype == BW_F32 || x_dtype == BW_BF16, BW_ERR_DTYPE, "bw_quantize: bad dtype %d", (int)x_dtype);
+  BW_REQUIRE(fmt == BW_ACT_INT4 || fmt == BW_ACT_FP4_E2M1, BW_ERR_DTYPE, "bw_quantize: bad format %d", (int)fmt);
+  BW_REQUIRE(M >= 0 && K >= 64 && K % 64 == 0 && K <= kMaxK, BW_ERR_SHAPE,
+             "bw_quantize: need M >= 0, K %% 64 == 0, 64 <= K <= %lld (M=%lld K=%lld)", (long long)kMaxK,
+             (long long)M, (long long)K);
+  if (M == 0) return ok();
+  BW_REQUIRE(x && codes && scales, BW_ERR_NULL, "bw_quantize: NULL pointer");
+  BW_REQUIRE(!misaligned(x) && !misaligned(codes) && !misaligned(scales), BW_ERR_ALIGN,
+             "bw_quantize: device pointers must be 16-byte aligned");
+  return hip_status(bw::launch_quantize_act4(x, x_dtype == BW_BF16, M, K, static_cast<int>(fmt), codes, scales,
+                                             static_cast<hipStream_t>(stream)),
+                    "bw_quantize");
+}
+
+static bw_status check_gemm(const char* who, const void* codes, const float* sx, int64_t M, int64_t K,
+                            const uint8_t* w, const float* beta, int64_t N, const float* y, const void* acc) {
+  BW_REQUIRE(M >= 0 && K >= 64 && K % 64 == 0 && K <= kMaxK && N >= 16 && N % 16 == 0, BW_ERR_SHAPE,
+             "%s: need M >= 0, K %% 64 == 0, 64 <= K <= %lld, N %% 16 == 0, N >= 16 (M=%lld K=%lld N=%lld)", who,
+             (long long)kMaxK, (long long)M, (long long)K, (long long)N);
+  if (M == 0) return ok();
+  BW_REQUIRE(codes && sx && w && beta && y, BW_ERR_NULL, "%s: NULL pointer", who);
+  BW_REQUIRE(!misaligned(codes) && !misaligned(sx) && !misaligned(w) && !misaligned(beta) && !misaligned(y) &&
+                 !misaligned(acc),
+             BW_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", who);
+  return ok();
+}
+
+bw_status bw_bitlinear_a4(const uint8_t* codes, const float* x_scales, int64_t M, int64_t K, bw_act4_fmt fmt,
+                          const uint8_t* w_packed, const float* beta, int64_t N, float* y, void* acc_dbg,
+                          void* stream) {
+  BW_REQUIRE(fmt == BW_ACT_INT4 || fmt == BW_ACT_FP4_E2M1, BW_ERR_DTYPE, "bw_bitlinear_a4: bad format %d", (int)fmt);
+  bw_status st = check_gemm("bw_bitlinear_a4", codes, x_scales, M, K, w_packed, beta, N, y, acc_dbg);
+  if (st != BW_OK || M == 0) return st;
+  return hip_status(bw::launch_bitlinear(fmt == BW_ACT_INT4 ? 0 : 1, codes, x_scales, M, K, w_packed, beta, N, y,
+                                         acc_dbg, static_cast<hipStream_t>(stream)),
+                    "bw_bitlinear_a4");
+}
+
+bw_status bw_quantize_sparse_a8(const void* gate_or_x, const void* up, bw_dtype dtype, int64_t M, int64_t K,
+                                int64_t k_keep, int8_t* codes, float* scales, uint32_t* mask_dbg, void* stream) {
+  BW_REQUIRE(dtype == BW_F32 || dtype == BW_BF16, BW_ERR_DTYPE, "bw_quantize_sparse_a8: bad dtype %d", (int)dtype);
+  BW_REQUIRE(M >= 0 && K >= 64 && K % 64 == 0 && K <= kMaxKSparse, BW_ERR_SHAPE,
+             "bw_quantize_sparse_a8: need M >= 0, K %% 64 == 0, 64 <= K <= %lld (M=%lld K=%lld)",
+             (long long)kMaxKSparse, (long long)M, (long long)K);
+  BW_REQUIRE(k_keep >= 1 && k_keep <= K, BW_ERR_ARG, "bw_quantize_sparse_a8: need 1 <= k_keep <= K (k_keep=%lld)",
+             (long long)k_keep);
+  if (M == 0) return ok();
+  BW_REQUIRE(gate_or_x && codes && scales, BW_ERR_NULL, "bw_quantize_sparse_a8: NULL pointer");
+  BW_REQUIRE(!misaligned(gate_or_x) && !misaligned(up) && !misaligned(codes) && !misaligned(scales) &&
+                 !misaligned(mask_dbg),
+             BW_ERR_ALIGN, "bw_quantize_sparse_a8: device pointers must be 16-byte aligned");
+  return hip_status(bw::launch_sparse_a8(gate_or_x, up, dtype == BW_BF16, M, K, k_keep, codes, scales, mask_dbg,
+                                         static_cast<hipStream_t>(stream)),
+                    "bw_quantize_sparse_a8");
+}
+
+bw_status bw_bitlinear_sparse_a8(const int8_t* codes, const float* x_scales, int64_t M, int64_t K,
+                                 const uint8_t* w_packed, const float* beta, int64_t N, float* y, int32_t* acc_dbg,
+                                 void* stream) {
+  bw_status st = check_gemm("bw_bitlinear_sparse_a8", codes, x_scales, M, K, w_packed, beta, N, y, acc_dbg);
+  if (st != BW_OK || M == 0) return st;
+  return hip_status(bw::launch_bitlinear(2, codes, x_scales, M, K, w_packed, beta, N, y, acc_dbg,
+                                         static_cast<hipStream_t>(stream)),
+                    "bw_bitlinear_sparse_a8");
+}
+
+static bw_status check_kv(const char* who, int64_t B, int64_t S, int64_t H, int64_t D, int64_t n_special) {
+  BW_REQUIRE(B >= 0 && S >= 0 && H >= 1 && n_special >= 0, BW_ERR_SHAPE,
+             "%s: need B, S >= 0, H >= 1, n_special >= 0", who);
+  BW_REQUIRE(D == 32 || D == 64 || D == 128 || D == 256 || D == 512, BW_ERR_SHAPE,
+             "%s: head_dim must be 32, 64, 128, 256 or 512 (D=%lld)", who, (long long)D);
+  BW_REQUIRE(B == 0 || S == 0 || (B <= (int64_t(1) << 40) / S / H / D), BW_ERR_SHAPE, "%s: tensor too large", who);
+  return ok();
+}
+
+bw_status bw_kv_pack3(const void* kv, bw_dtype dtype, int64_t B, int64_t S, int64_t H, int64_t D,
+                      const int32_t* slot_of, int64_t n_special, uint8_t* p3, float* s3, uint8_t* p4, float* s4,
+                      void* stream) {
+  BW_REQUIRE(dtype == BW_F32 || dtype == BW_BF16, BW_ERR_DTYPE, "bw_kv_pack3: bad dtype %d", (int)dtype);
+  bw_status st = check_kv("bw_kv_pack3", B, S, H, D, n_special);
+  if (st != BW_OK) return st;
+  if (B == 0 || S == 0) return ok();
+  BW_REQUIRE(kv && slot_of && p3 && s3, BW_ERR_NULL, "bw_kv_pack3: NULL pointer");
+  BW_REQUIRE(n_special == 0 || (p4 && s4), BW_ERR_NULL, "bw_kv_pack3: p4/s4 required when n_special > 0");
+  BW_REQUIRE(!misaligned(kv) && !misaligned(slot_of) && !misaligned(p3) && !misaligned(s3) && !misaligned(p4) &&
+                 !misaligned(s4),
+             BW_ERR_ALIGN, "bw_kv_pack3: device pointers must be 16-byte aligned");
+  return hip_status(bw::launch_kv_pack3(kv, dtype == BW_BF16, B, S, H, D, slot_of, n_special, p3, s3, p4, s4,
+                                        static_cast<hipStream_t>(stream)),
+                    "bw_kv_pack3");
+}
+
+bw_status bw_kv_unpack3(const uint8_t* p3, const float* s3, const uint8_t* p4, const float* s4,
+                        const int32_t* slot_of, int64_t B, int64_t S, int64_t H, int64_t D, int64_t n_special,
+                        bw_dtype out_dtype, void* out, void* stream) {
+  BW_REQUIRE(out_dtype == BW_F32 || out_dtype == BW_BF16, BW_ERR_DTYPE, "bw_kv_unpack3: bad dtype %d",
+             (int)out_dtype);
+  bw_status st = check_kv("bw_kv_unpack3", B, S, H, D, n_special);
+  if (st != BW_OK) return st;
+  if (B == 0 || S == 0) return ok();
+  BW_REQUIRE(p3 && s3 && slot_of && out, BW_ERR_NULL, "bw_kv_unpack3: NULL pointer");
+  BW_REQUIRE(n_special == 0 || (p4 && s4), BW_ERR_NULL, "bw_kv_unpack3: p4/s4 required when n_special > 0");
+  BW_REQUIRE(!misaligned(p3) && !misaligned(s3) && !misaligned(p4) && !misaligned(s4) && !misaligned(slot_of) &&
+                 !misaligned(out),
+             BW_ERR_ALIGN, "bw_kv_unpack3: device pointers must be 16-byte aligned");
+  return hip_status(bw::launch_kv_unpack3(p3, s3, p4, s4, slot_of, B, S, H, D, n_special, out_dtype == BW_BF16,
+                                          out, static_cast<hipStream_t>(stream)),
+                    "bw_kv_unpack3");
+}
+
+}  // extern "C"

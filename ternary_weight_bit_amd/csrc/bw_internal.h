@@ -1,0 +1,36 @@
+// Host-side launchers behind the C ABI of libbw (include/bw.h).  Each returns
+// the HIP error of its launches; shapes have been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bw {
+
+// Byte size of the scratch words bw_pack_ternary needs in its workspace.
+constexpr size_t kPackWorkspaceBytes = 4096;
+
+hipError_t launch_quantize_act4(const void* x, bool bf16, int64_t M, int64_t K, int fmt,
+                                uint8_t* codes, float* scales, hipStream_t s);
+
+hipError_t launch_pack_ternary(const void* W, bool bf16, int64_t N, int64_t K, int role,
+                               uint8_t* packed, float* beta, void* ws, hipStream_t s);
+
+// mode: 0 = INT4 codes, 1 = e2m1 codes, 2 = INT8 codes
+hipError_t launch_bitlinear(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
+                            const uint8_t* w_packed, const float* beta, int64_t N, float* y,
+                            void* acc_dbg, hipStream_t s);
+
+hipError_t launch_sparse_a8(const void* g, const void* u, bool bf16, int64_t M, int64_t K,
+                            int64_t k_keep, int8_t* codes, float* scales, uint32_t* mask,
+                            hipStream_t s);
+
+hipError_t launch_kv_pack3(const void* kv, bool bf16, int64_t B, int64_t S, int64_t H, int64_t D,
+                           const int32_t* slot_of, int64_t n_special, uint8_t* p3, float* s3,
+                           uint8_t* p4, float* s4, hipStream_t s);
+
+hipError_t launch_kv_unpack3(const uint8_t* p3, const float* s3, const uint8_t* p4, const float* s4,
+                             const int32_t* slot_of, int64_t B, int64_t S, int64_t H, int64_t D,
+                             int64_t n_special, bool out_bf16, void* out, hipStream_t s);
+
+}  // namespace bw

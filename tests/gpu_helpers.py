@@ -1,0 +1,50 @@
+"""Helpers for the GPU parity tests: host<->device transfer and comparisons."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+DEV = "cuda:0"
+
+
+def bf16_dev(b) -> torch.Tensor:
+    """synth.Bf16 -> torch.bfloat16 device tensor with identical bits."""
+    return torch.from_numpy(np.ascontiguousarray(b.bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def f32_dev(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def assert_rel(y_gpu: np.ndarray, y_ref: np.ndarray, rtol: float = 1e-5, what: str = "y"):
+    """|y_gpu - y_ref| <= rtol * |y_ref| elementwise (so y_ref == 0 demands an exact 0)."""
+    y_gpu = np.asarray(y_gpu, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    err = np.abs(y_gpu - y_ref)
+    bad = err > rtol * np.abs(y_ref)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(
+            f"{what}: {int(bad.sum())} of {bad.size} outside rtol={rtol}; first {idx.tolist()}: "
+            f"gpu {[y_gpu[tuple(i)] for i in idx]} ref {[y_ref[tuple(i)] for i in idx]}"
+        )
+
+
+def assert_same(a: np.ndarray, b: np.ndarray, what: str):
+    a = np.asarray(a)
+    b = np.asarray(b)
+    if a.shape != b.shape:
+        raise AssertionError(f"{what}: shape {a.shape} vs {b.shape}")
+    if not np.array_equal(a, b):
+        bad = np.argwhere(a != b)
+        raise AssertionError(
+            f"{what}: {len(bad)} of {a.size} differ; first {bad[:5].tolist()}: "
+            f"gpu {[a[tuple(i)] for i in bad[:5]]} ref {[b[tuple(i)] for i in bad[:5]]}"
+        )

@@ -1,0 +1,99 @@
+"""C-ABI boundary tests that need no GPU: the library loads, exports what
+include/bw.h declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import ternary_weight_bit_amd as bw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bw.h")
+
+lib = bw._lib
+A = 0x10000  # aligned fake device address: validation fails before it could be touched
+MIS = 0x10004  # 4-byte aligned only
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bw_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) == 12, names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_versions():
+    assert bw.bw_abi_version() == 1
+    assert bw.bw_pack_layout_version() == 1
+    assert bw.bw_ternary_packed_bytes(4096, 4096) == 4096 * 4096 // 4
+    assert bw.bw_ternary_packed_bytes(0, 64) == 0
+    assert bw.bw_pack_ternary_workspace_bytes(16, 64) >= 2048 + 4
+
+
+def q(x, dt, M, K, fmt, c, s):
+    return lib.bw_quantize(x, dt, M, K, fmt, c, s, None)
+
+
+def test_quantize_validation():
+    assert q(A, 1, 4, 100, 0, A, A) == 2  # K % 64
+    assert q(A, 1, 4, 0, 0, A, A) == 2
+    assert q(A, 1, 4, 262144, 0, A, A) == 2  # K too large
+    assert q(A, 1, -1, 64, 0, A, A) == 2
+    assert q(A, 7, 4, 64, 0, A, A) == 4  # dtype
+    assert q(A, 1, 4, 64, 9, A, A) == 4  # fmt
+    assert q(None, 1, 4, 64, 0, A, A) == 1
+    assert q(A, 1, 4, 64, 0, None, A) == 1
+    assert q(MIS, 1, 4, 64, 0, A, A) == 3
+    assert "16-byte" in bw.bw_last_error()
+    assert q(None, 1, 0, 64, 0, None, None) == 0  # empty call
+    assert bw.bw_last_error() == ""
+
+
+def test_bitlinear_validation():
+    f = lib.bw_bitlinear_a4
+    assert f(A, A, 8, 4096, 0, A, A, 100, A, None, None) == 2  # N % 16
+    assert f(A, A, 8, 4000, 0, A, A, 128, A, None, None) == 2  # K % 64
+    assert f(A, A, 8, 4096, 3, A, A, 128, A, None, None) == 4
+    assert f(A, A, 8, 4096, 0, None, A, 128, A, None, None) == 1
+    assert f(A, A, 8, 4096, 0, A, A, 128, MIS, None, None) == 3
+    assert f(A, A, 8, 4096, 0, A, A, 128, A, MIS, None) == 3  # acc_dbg alignment
+    assert f(None, None, 0, 4096, 0, None, None, 128, None, None, None) == 0
+    g = lib.bw_bitlinear_sparse_a8
+    assert g(A, A, 8, 11008, A, A, 4095, A, None, None) == 2
+    assert g(A, None, 8, 11008, A, A, 4096, A, None, None) == 1
+
+
+def test_sparse_validation():
+    f = lib.bw_quantize_sparse_a8
+    assert f(A, A, 1, 8, 11008, 0, A, A, None, None) == 5  # k_keep
+    assert f(A, A, 1, 8, 11008, 11009, A, A, None, None) == 5
+    assert f(A, A, 1, 8, 32768, 100, A, A, None, None) == 2  # K above the row-resident limit
+    assert f(A, MIS, 1, 8, 11008, 5504, A, A, None, None) == 3
+    assert f(None, None, 1, 8, 11008, 5504, A, A, None, None) == 1
+    assert f(A, None, 2, 8, 11008, 5504, A, A, None, None) == 4
+
+
+def test_pack_validation():
+    f = lib.bw_pack_ternary
+    assert f(A, 0, 100, 64, 0, A, A, A, 4096, None) == 2
+    assert f(A, 0, 16, 64, 5, A, A, A, 4096, None) == 4
+    assert f(A, 0, 16, 64, 0, A, A, A, 16, None) == 5  # workspace too small
+    assert f(A, 0, 16, 64, 0, A, A, None, 4096, None) == 1
+    assert f(A, 0, 16, 64, 0, A, MIS, A, 4096, None) == 3
+
+
+def test_kv_validation():
+    f = lib.bw_kv_pack3
+    assert f(A, 1, 8, 16, 4, 100, A, 2, A, A, A, A, None) == 2  # head_dim
+    assert f(A, 1, 8, 16, 4, 128, A, 2, A, A, None, None, None) == 1  # side slab missing
+    assert f(A, 1, 0, 16, 4, 128, None, 0, None, None, None, None, None) == 0  # empty
+    g = lib.bw_kv_unpack3
+    assert g(A, A, A, A, A, 8, 16, 4, 128, 2, 5, A, None) == 4
+    assert g(A, A, A, A, A, 8, 16, 0, 128, 2, 1, A, None) == 2  # H = 0

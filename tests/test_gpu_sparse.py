@@ -1,0 +1,82 @@
+"""GPU parity: ReLU^2 + top-k + INT8 front end (bw_quantize_sparse_a8) vs the oracle, bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import ternary_weight_bit_amd as bw
+from oracle import sparse8
+from tests.gpu_helpers import assert_same, bf16_dev, f32_dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def run(g_dev, u_dev, k, M, K):
+    mask = torch.empty((M, K // 32), dtype=torch.int32, device="cuda:0")
+    codes, scales = bw.bw_quantize_sparse_a8(g_dev, u_dev, k, mask_dbg=mask)
+    return host(codes), host(scales), host(mask).view(np.uint32)
+
+
+def check(g_dev, u_dev, g32, u32, k, label):
+    M, K = g32.shape
+    c, s, m = run(g_dev, u_dev, k, M, K)
+    _, keep, q, rs = sparse8.sparse_a8(g32, u32, k)
+    assert_same(m, sparse8.mask_words(keep), f"{label} mask")
+    assert_same(c, q, f"{label} codes")
+    assert_same(s.view(np.uint32), rs.view(np.uint32), f"{label} scales")
+    assert np.all(np.unpackbits(m.view(np.uint8), axis=1).sum(axis=1) == k)
+
+
+@pytest.mark.parametrize("M,K", [(64, 11008), (7, 64), (33, 4096), (5, 16384), (3, 320)])
+def test_relu2_gate_bf16(M, K):
+    g, u = synth.gate_up(seed=M * 31 + K, M=M, K=K)
+    check(bf16_dev(g), bf16_dev(u), g.f32, u.f32, K // 2, f"relu2 {M}x{K}")
+
+
+@pytest.mark.parametrize("M,K", [(64, 4096), (9, 192)])
+def test_out_proj_student_t(M, K):
+    x = synth.heavy_tailed(seed=M + K, M=M, K=K)
+    check(bf16_dev(x), None, x.f32, None, K // 2, f"out_proj {M}x{K}")
+
+
+@pytest.mark.parametrize("k", [1, 2, 63, 64, 65, 2047, 4095, 4096])
+def test_k_keep_range(k):
+    M, K = 6, 4096
+    x = synth.heavy_tailed(seed=k, M=M, K=K)
+    check(bf16_dev(x), None, x.f32, None, k, f"k={k}")
+
+
+def test_fp32_inputs_and_ties():
+    M, K = 12, 1024
+    rs = np.random.default_rng(3)
+    g = rs.integers(-3, 4, size=(M, K)).astype(np.float32)  # heavy exact ties in |h|
+    u = rs.integers(-2, 3, size=(M, K)).astype(np.float32)
+    g[0] = 0.0  # all-zero row
+    g[1] = 1.0
+    u[1] = 1.0  # constant row: every key ties
+    g[2] = -1.0  # ReLU kills the whole row
+    for k in (1, K // 2, K - 1, K):
+        check(f32_dev(g), f32_dev(u), g, u, k, f"ties k={k}")
+
+
+def test_full_down_proj_shape_sampled():
+    """M=2048, K=11008 bf16 (the benchmark's launch), 64 sampled rows vs the oracle."""
+    M, K = 2048, 11008
+    g, u = synth.gate_up(M=M, K=K)
+    c, s, m = run(bf16_dev(g), bf16_dev(u), K // 2, M, K)
+    rows = np.sort(np.random.default_rng(8).choice(M, 64, replace=False))
+    _, keep, q, rs = sparse8.sparse_a8(g.f32[rows], u.f32[rows], K // 2)
+    assert_same(c[rows], q, "down codes")
+    assert_same(s[rows].view(np.uint32), rs.view(np.uint32), "down scales")
+    assert_same(m[rows], sparse8.mask_words(keep), "down mask")
+    # property at every row: exactly K/2 survivors
+    assert np.all(np.unpackbits(m.view(np.uint8), axis=1).sum(axis=1) == K // 2)
+
+
+def test_determinism():
+    g, u = synth.gate_up(seed=4, M=128, K=11008)
+    gd, ud = bf16_dev(g), bf16_dev(u)
+    a, sa = bw.bw_quantize_sparse_a8(gd, ud, 5504)
+    b, sb = bw.bw_quantize_sparse_a8(gd, ud, 5504)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(sa, sb)
