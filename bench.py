@@ -1,0 +1,385 @@
+#!/usr/bin/env python3
+"""Benchmark of the BitNet a4.8 hybrid-quantized BitLinear hot path on one MI355X.
+
+One step is one pass of every hot-path kernel over synthetic 7B-shape inputs
+that are resident in HBM before timing starts:
+
+  prefill, M=2048 tokens, K=4096:    INT4 quantizer -> W1.58A4 GEMMs (N=11008, N=4096)
+                                     FP4 quantizer  -> W1.58.FP4 GEMMs (N=11008, N=4096)
+  sparse path, M=2048:               ReLU^2.up + top-k 50% + INT8 (K=11008) -> W1.58A8 down_proj (N=4096)
+                                     top-k 50% + INT8 of a Student-t(3) input (K=4096) -> W1.58A8 out_proj
+  decode, M = 1, 2, 4, 8 tokens:     INT4 quantizer -> W1.58A4 GEMV over 32 layers of fused q/k/v
+                                     (N=12288) and gate/up (N=22016) weights (1.12 GB, > 4x the
+                                     256 MB Infinity Cache, so weights stream from HBM)
+  KV cache, one layer (8x4096x32x128): 3-bit pack of K and V, unpack of both to bf16
+  weights:                           absmean ternary pack of one 4096x4096 fp32 tensor
+
+Each decode row's 32-64 launches are recorded once into a HIP graph; the other
+rows are single launches.  A step runs the rows in order, each bracketed by HIP
+events on the stream it runs on.  The host enqueues far faster than the GPU
+drains, so an event pair measures GPU time only.
+The printed line's `value` is the W1.58A4 prefill throughput (int ops of the
+two GEMMs over the time of quantizer + GEMMs); `decode_gbs` is the decode
+GEMV rate in algorithmic bytes; `roofline` covers the N=11008 prefill GEMM.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0  # dense int8 MFMA, MI355X
+FP4_PEAK_TOPS = 10100.0  # dense fp4/fp6 MFMA, MI355X
+
+M_PREFILL, HIDDEN, FFN = 2048, 4096, 11008
+DECODE_MS = (1, 2, 4, 8)
+LAYERS = 32
+KV_SHAPE = (8, 4096, 32, 128)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle leg")
+    p.add_argument("--rows", action="store_true", help="also print a per-row table to stderr")
+    return p.parse_args()
+
+
+class Bench:
+    """Holds device inputs/outputs and the launch list of one step."""
+
+    def __init__(self):
+        import torch
+
+        import synth
+        import ternary_weight_bit_amd as bw
+
+        self.torch, self.bw = torch, bw
+        dev = "cuda:0"
+        t = torch
+
+        def bf16(b):
+            return t.from_numpy(np.ascontiguousarray(b.bits).view(np.int16)).to(dev).view(t.bfloat16)
+
+        def f32(a):
+            return t.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+        S = synth.SEED_BASE
+        # ---------------- prefill
+        self.x_pre = bf16(synth.prefill_activations(S + 2, M_PREFILL, HIDDEN))
+        self.w_up = f32(synth.weight_tensor(S + 12, FFN, HIDDEN))
+        self.wp_11008, self.b_11008 = bw.bw_pack_ternary(self.w_up, bw.BW_ROLE_A4)
+        w_q = f32(synth.weight_tensor(S + 11, HIDDEN, HIDDEN))
+        self.w_q = w_q
+        self.wp_4096, self.b_4096 = bw.bw_pack_ternary(w_q, bw.BW_ROLE_A4)
+        del self.w_up
+        self.c4 = t.empty((M_PREFILL, HIDDEN // 2), dtype=t.uint8, device=dev)
+        self.s4 = t.empty(M_PREFILL, dtype=t.float32, device=dev)
+        self.cf = t.empty_like(self.c4)
+        self.sf = t.empty_like(self.s4)
+        self.y_11008 = t.empty((M_PREFILL, FFN), dtype=t.float32, device=dev)
+        self.y_4096 = t.empty((M_PREFILL, HIDDEN), dtype=t.float32, device=dev)
+        # ---------------- sparse path
+        g, u = synth.gate_up(S + 3, M_PREFILL, FFN)
+        self.gate, self.up = bf16(g), bf16(u)
+        del g, u
+        self.w_down = f32(synth.weight_tensor(S + 14, HIDDEN, FFN))
+        self.wp_down, self.b_down = bw.bw_pack_ternary(self.w_down, bw.BW_ROLE_A8)
+        del self.w_down
+        self.x_out = bf16(synth.heavy_tailed(S + 13, M_PREFILL, HIDDEN))
+        self.wp_o, self.b_o = bw.bw_pack_ternary(w_q, bw.BW_ROLE_A8)
+        self.c8_down = t.empty((M_PREFILL, FFN), dtype=t.int8, device=dev)
+        self.s8_down = t.empty(M_PREFILL, dtype=t.float32, device=dev)
+        self.c8_out = t.empty((M_PREFILL, HIDDEN), dtype=t.int8, device=dev)
+        self.s8_out = t.empty(M_PREFILL, dtype=t.float32, device=dev)
+        self.y_down = t.empty((M_PREFILL, HIDDEN), dtype=t.float32, device=dev)
+        self.y_o = t.empty((M_PREFILL, HIDDEN), dtype=t.float32, device=dev)
+        # ---------------- decode: 32 layers of fused qkv + gate/up weights
+        self.n_qkv = sum(synth.QKV_PARTS)
+        self.n_gu = sum(synth.GATE_UP_PARTS)
+        qkv_p = t.empty(self.n_qkv * HIDDEN // 4, dtype=t.uint8, device=dev)
+        qkv_b = t.empty(self.n_qkv, dtype=t.float32, device=dev)
+        gu_p = t.empty(self.n_gu * HIDDEN // 4, dtype=t.uint8, device=dev)
+        gu_b = t.empty(self.n_gu, dtype=t.float32, device=dev)
+        for parts, seed, P, B in ((synth.QKV_PARTS, S + 21, qkv_p, qkv_b), (synth.GATE_UP_PARTS, S + 22, gu_p, gu_b)):
+            off = 0
+            for w in synth.fused_weights(seed, parts, HIDDEN):
+                n = w.shape[0]
+                bw.bw_pack_ternary(f32(w), bw.BW_ROLE_A4, P[off * HIDDEN // 4 : (off + n) * HIDDEN // 4], B[off : off + n])
+                off += n
+        # distinct addresses per layer (copies of one layer's packed bytes)
+        self.layers = [(qkv_p.clone(), qkv_b.clone(), gu_p.clone(), gu_b.clone()) for _ in range(LAYERS)]
+        del qkv_p, gu_p
+        self.dec = {}
+        for M in DECODE_MS:
+            xa = bf16(synth.decode_activations(S + 1 + M, M, HIDDEN))
+            xf = bf16(synth.decode_activations(S + 101 + M, M, HIDDEN))
+            self.dec[M] = dict(
+                xa=xa, xf=xf,
+                ca=t.empty((M, HIDDEN // 2), dtype=t.uint8, device=dev), sa=t.empty(M, dtype=t.float32, device=dev),
+                cf=t.empty((M, HIDDEN // 2), dtype=t.uint8, device=dev), sf=t.empty(M, dtype=t.float32, device=dev),
+                ya=t.empty((M, self.n_qkv), dtype=t.float32, device=dev),
+                yf=t.empty((M, self.n_gu), dtype=t.float32, device=dev),
+            )
+        # ---------------- KV cache, one layer
+        B_, S_, H_, D_ = KV_SHAPE
+        self.kv = [bf16(synth.kv_tensor(S + 5 + i, *KV_SHAPE)) for i in range(2)]
+        slot_of, self.n_special = synth.kv_special_slots(S + 5, B_, S_)
+        self.slot_of = t.from_numpy(slot_of).to(dev)
+        self.kvp = []
+        for _ in range(2):
+            self.kvp.append((
+                t.empty((B_, S_, H_, 3 * D_ // 8), dtype=t.uint8, device=dev),
+                t.empty((B_, S_, H_), dtype=t.float32, device=dev),
+                t.zeros((self.n_special, H_, D_ // 2), dtype=t.uint8, device=dev),
+                t.zeros((self.n_special, H_), dtype=t.float32, device=dev),
+            ))
+        self.kv_out = [t.empty(KV_SHAPE, dtype=t.bfloat16, device=dev) for _ in range(2)]
+        # ---------------- weight packing (offline row): one 4096x4096 fp32 tensor
+        self.pk = t.empty(HIDDEN * HIDDEN // 4, dtype=t.uint8, device=dev)
+        self.pk_b = t.empty(HIDDEN, dtype=t.float32, device=dev)
+        self.pk_ws = t.empty(bw.bw_pack_ternary_workspace_bytes(HIDDEN, HIDDEN), dtype=t.uint8, device=dev)
+        torch.cuda.synchronize()
+        self.launches = self._launch_list()
+
+    # ------------------------------------------------------------------ launches
+    def _launch_list(self):
+        """Rows of the step: (name, unit, algorithmic amount per launch, [launch fns])."""
+        bw = self.bw
+        R = []
+
+        def gemm_ops(M, N, K):
+            return 2.0 * M * N * K
+
+        def gemv_bytes(M, N, K):
+            return N * K / 4 + 4 * N + M * K / 2 + 4 * M + 4 * M * N
+
+        M, K = M_PREFILL, HIDDEN
+        R.append(("a1_quantize_int4", "GB/s", M * K * 2 + M * K / 2 + 4 * M,
+                  [lambda: bw.bw_quantize(self.x_pre, bw.BW_ACT_INT4, self.c4, self.s4)]))
+        R.append(("a4_gemm_int4_n11008", "TOPS", gemm_ops(M, FFN, K),
+                  [lambda: bw.bw_bitlinear_a4(self.c4, self.s4, bw.BW_ACT_INT4, self.wp_11008, self.b_11008, self.y_11008)]))
+        R.append(("a4_gemm_int4_n4096", "TOPS", gemm_ops(M, HIDDEN, K),
+                  [lambda: bw.bw_bitlinear_a4(self.c4, self.s4, bw.BW_ACT_INT4, self.wp_4096, self.b_4096, self.y_4096)]))
+        R.append(("a2_quantize_fp4", "GB/s", M * K * 2 + M * K / 2 + 4 * M,
+                  [lambda: bw.bw_quantize(self.x_pre, bw.BW_ACT_FP4_E2M1, self.cf, self.sf)]))
+        R.append(("a6_gemm_fp4_n11008", "TOPS", gemm_ops(M, FFN, K),
+                  [lambda: bw.bw_bitlinear_a4(self.cf, self.sf, bw.BW_ACT_FP4_E2M1, self.wp_11008, self.b_11008, self.y_11008)]))
+        R.append(("a6_gemm_fp4_n4096", "TOPS", gemm_ops(M, HIDDEN, K),
+                  [lambda: bw.bw_bitlinear_a4(self.cf, self.sf, bw.BW_ACT_FP4_E2M1, self.wp_4096, self.b_4096, self.y_4096)]))
+        R.append(("a7_relu2_topk_int8_k11008", "GB/s", 2 * M * FFN * 2 + M * FFN + 4 * M,
+                  [lambda: bw.bw_quantize_sparse_a8(self.gate, self.up, FFN // 2, self.c8_down, self.s8_down)]))
+        R.append(("a9_gemm_a8_down", "TOPS", gemm_ops(M, HIDDEN, FFN),
+                  [lambda: bw.bw_bitlinear_sparse_a8(self.c8_down, self.s8_down, self.wp_down, self.b_down, self.y_down)]))
+        R.append(("a8_topk_int8_k4096", "GB/s", M * K * 2 + M * K + 4 * M,
+                  [lambda: bw.bw_quantize_sparse_a8(self.x_out, None, HIDDEN // 2, self.c8_out, self.s8_out)]))
+        R.append(("a9_gemm_a8_outproj", "TOPS", gemm_ops(M, HIDDEN, HIDDEN),
+                  [lambda: bw.bw_bitlinear_sparse_a8(self.c8_out, self.s8_out, self.wp_o, self.b_o, self.y_o)]))
+        for Md in DECODE_MS:
+            d = self.dec[Md]
+            R.append((f"a1_quantize_int4_decode_m{Md}", "GB/s", Md * K * 2 + Md * K / 2 + 4 * Md,
+                      [lambda d=d: bw.bw_quantize(d["xa"], bw.BW_ACT_INT4, d["ca"], d["sa"]),
+                       lambda d=d: bw.bw_quantize(d["xf"], bw.BW_ACT_INT4, d["cf"], d["sf"])] * LAYERS))
+            R.append((f"a5_gemv_qkv_m{Md}", "GB/s", gemv_bytes(Md, self.n_qkv, K),
+                      [lambda d=d, qp=qp, qb=qb: bw.bw_bitlinear_a4(d["ca"], d["sa"], bw.BW_ACT_INT4, qp, qb, d["ya"])
+                       for qp, qb, _, _ in self.layers]))
+            R.append((f"a5_gemv_gateup_m{Md}", "GB/s", gemv_bytes(Md, self.n_gu, K),
+                      [lambda d=d, gp=gp, gb=gb: bw.bw_bitlinear_a4(d["cf"], d["sf"], bw.BW_ACT_INT4, gp, gb, d["yf"])
+                       for _, _, gp, gb in self.layers]))
+        B_, S_, H_, D_ = KV_SHAPE
+        nvec = B_ * S_ * H_
+        pack_bytes = nvec * D_ * 2 + nvec * (3 * D_ // 8) + 4 * nvec + 4 * B_ * S_ + self.n_special * H_ * (D_ // 2 + 4)
+        R.append(("a10_kv_pack3", "GB/s", pack_bytes,
+                  [lambda i=i: bw.bw_kv_pack3(self.kv[i], self.slot_of, self.n_special, *self.kvp[i]) for i in range(2)]))
+        R.append(("a10_kv_unpack3", "GB/s", pack_bytes,
+                  [lambda i=i: bw.bw_kv_unpack3(*self.kvp[i], self.slot_of, self.n_special,
+                                                out_dtype=self.torch.bfloat16, out=self.kv_out[i]) for i in range(2)]))
+        R.append(("a3_pack_ternary_4096x4096", "GB/s", HIDDEN * HIDDEN * 4 + HIDDEN * HIDDEN / 4 + 4 * HIDDEN,
+                  [lambda: bw.bw_pack_ternary(self.w_q, bw.BW_ROLE_A4, self.pk, self.pk_b, self.pk_ws)]))
+        return R
+
+    def capture(self):
+        """Record each multi-launch row (the decode loops) once into a HIP graph (no
+        allocation, no memset inside), so a replay costs the host one call for the
+        row; single-launch rows are launched directly."""
+        torch = self.torch
+        self.graphs = []
+        for name, _, _, fns in self.launches:
+            if len(fns) == 1:
+                self.graphs.append(fns[0])
+                continue
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=torch.cuda.current_stream()):
+                for fn in fns:
+                    fn()
+            self.graphs.append(g.replay)
+
+    def step_eager(self):
+        for _, _, _, fns in self.launches:
+            for fn in fns:
+                fn()
+
+    def step(self, ev=None):
+        stream = self.torch.cuda.current_stream()
+        for i, run in enumerate(self.graphs):
+            if ev is not None:
+                ev[2 * i].record(stream)
+            run()
+            if ev is not None:
+                ev[2 * i + 1].record(stream)
+
+
+def cpu_baseline(target_s: float):
+    """The oracle, as it stands, on a bounded sample of the W1.58A4 prefill work:
+    INT4 quantizer + exact contraction + epilogue for a sample of token rows
+    against the N=11008 and N=4096 weights (already ternarized, as on the GPU side)."""
+    import synth
+    from oracle import act4, bitlinear, ternary
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    S = synth.SEED_BASE
+    x = synth.prefill_activations(S + 2, M_PREFILL, HIDDEN).f32
+    weights = []
+    for seed, n in ((S + 12, FFN), (S + 11, HIDDEN)):
+        t, b = ternary.quantize_weights(synth.weight_tensor(seed, n, HIDDEN))
+        weights.append((t, np.full(n, b, np.float32)))
+
+    def run(rows):
+        t0 = time.perf_counter()
+        for tq, beta in weights:
+            bitlinear.bitlinear_a4_int4(x[:rows], tq, beta)
+        return time.perf_counter() - t0
+
+    rows = 32
+    dt = run(rows)
+    while dt < target_s / 4 and rows < M_PREFILL:
+        rows = min(M_PREFILL, rows * 4)
+        dt = run(rows)
+    ops = 2.0 * rows * HIDDEN * (FFN + HIDDEN)
+    return {
+        "value": ops / dt / 1e12,
+        "unit": "TOPS",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"W1.58A4 prefill (INT4 quantize + exact contraction + epilogue) on {rows} of 2048 token rows, "
+                  f"K=4096, N=11008 and N=4096; {dt:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the hot path is data-parallel and would shard by tokens or output channels)", file=sys.stderr)
+        return 2
+    import torch
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        t0 = time.perf_counter()
+        b = Bench()
+        print(f"bench: inputs resident ({time.perf_counter() - t0:.1f} s)", file=sys.stderr, flush=True)
+        n_rows = len(b.launches)
+        b.step_eager()  # eager pass before capture
+        torch.cuda.synchronize()
+        b.capture()
+        print("bench: row graphs captured", file=sys.stderr, flush=True)
+        for _ in range(args.warmup):
+            b.step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * n_rows)] for _ in range(args.steps)]
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        # one untimed step in flight ahead of the timed region, so the GPU is busy
+        # (and the host ahead of it) from the first timed event on
+        b.step()
+        wall0 = time.perf_counter()
+        t_start.record(stream)
+        for s_ in range(args.steps):
+            b.step(evs[s_])
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_per_step = ms_total / args.steps
+
+    # per-row statistics: average launch duration = row time / launches in the row
+    table = {}
+    for i, (name, unit, amount, fns) in enumerate(b.launches):
+        row_ms = [evs[s_][2 * i].elapsed_time(evs[s_][2 * i + 1]) for s_ in range(args.steps)]
+        avg_ms = float(np.mean(row_ms)) / len(fns)
+        rate = amount / (avg_ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
+        peak = HBM_PEAK_GBS if unit == "GB/s" else (FP4_PEAK_TOPS if "fp4" in name else INT8_PEAK_TOPS)
+        table[name] = {"avg_us": round(avg_ms * 1e3, 3), "launches_per_step": len(fns), "rate": round(rate, 2),
+                       "unit": unit, "frac_of_peak": round(rate / peak, 4), "amount_per_launch": amount}
+
+    def row_ms(names):
+        return sum(table[n]["avg_us"] * table[n]["launches_per_step"] for n in names) / 1e3
+
+    prefill_ops = 2.0 * M_PREFILL * HIDDEN * (FFN + HIDDEN)
+    prefill_ms = row_ms(("a1_quantize_int4", "a4_gemm_int4_n11008", "a4_gemm_int4_n4096"))
+    value = prefill_ops / (prefill_ms * 1e-3) / 1e12
+    gemv = [n for n in table if n.startswith("a5_gemv")]
+    dec_bytes = sum(table[n]["amount_per_launch"] * table[n]["launches_per_step"] for n in gemv)
+    dec_ms = row_ms(gemv)
+    decode_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
+    dom = table["a4_gemm_int4_n11008"]
+    roof = {
+        "bound": "mfma", "kernel": "k_bitlinear<INT4> (W1.58A4 GEMM, M=2048 K=4096 N=11008)",
+        "achieved": dom["rate"], "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+        "frac": round(dom["rate"] / INT8_PEAK_TOPS, 4), "traffic": None,
+        "note": "int8 MFMA int-ops (2*M*N*K per launch) / average launch duration from HIP events",
+    }
+    out = {
+        "metric": "BitLinear W1.58A4 prefill TOPS + decode GEMV HBM GB/s at 7B shapes, 1 GPU",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4xternary->int32 (prefill); e2m1 fp4, int8 on the other rows",
+        "data": "synthetic (seeded N(0,1)/Student-t activations, N(0,0.02) weights; 7B Llama-like shapes)",
+        "config": {"workload": "a4.8 BitLinear hot path at 7B shapes: prefill M=2048 K=4096 N=11008/4096 "
+                               "(INT4+FP4), sparse A8 down/out_proj M=2048, decode GEMV M=1,2,4,8 over 32 layers "
+                               "of qkv (N=12288) + gate/up (N=22016), KV 3-bit pack/unpack 8x4096x32x128, "
+                               "ternary pack 4096x4096", "global_batch": M_PREFILL, "seq_len": KV_SHAPE[1],
+                   "parallelism": "none (1 GPU)"},
+        "value_basis": "2*2048*4096*(11008+4096) int ops / time of the INT4 quantizer + both W1.58A4 GEMMs",
+        "decode_gbs": round(decode_gbs, 1),
+        "decode_frac_hbm": round(decode_gbs / HBM_PEAK_GBS, 4),
+        "roofline": roof,
+        "rows": table,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(f"bench: timed {args.steps} steps, {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    if args.rows:
+        for n, r in table.items():
+            print(f"{n:34s} {r['avg_us']:10.2f} us x{r['launches_per_step']:4d}  {r['rate']:9.1f} {r['unit']:5s} "
+                  f"{100 * r['frac_of_peak']:6.1f}%", file=sys.stderr)
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
