@@ -16,7 +16,16 @@ hipError_t launch_quantize_act4(const void* x, bool bf16, int64_t M, int64_t K, 
 hipError_t launch_pack_ternary(const void* W, bool bf16, int64_t N, int64_t K, int role,
                                uint8_t* packed, float* beta, void* ws, hipStream_t s);
 
+// Largest token count served by the weight-streaming GEMV.
+constexpr int64_t kGemvMaxM = 16;
+
 // mode: 0 = INT4 codes, 1 = e2m1 codes, 2 = INT8 codes
+hipError_t launch_gemv(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
+                       const uint8_t* w_packed, const float* beta, int64_t N, float* y, void* acc_dbg,
+                       hipStream_t s);
+hipError_t launch_gemm(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
+                       const uint8_t* w_packed, const float* beta, int64_t N, float* y, void* acc_dbg,
+                       hipStream_t s);
 hipError_t launch_bitlinear(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
                             const uint8_t* w_packed, const float* beta, int64_t N, float* y,
                             void* acc_dbg, hipStream_t s);

@@ -5,10 +5,11 @@
 // model supports a 3-bit KV cache.
 //
 // Each lane owns 8 consecutive elements of one (b, s, h) vector, so a vector
-// of D elements spans D/8 lanes and a wave holds 512/D vectors.  The absmax
-// is reduced across the vector's lanes with shuffles; four lanes make one
-// group of 32 codes, whose three bit planes are assembled with two shuffle
-// steps and written as three 32-bit words.
+// of D elements spans D/8 lanes and a wave holds 512/D vectors per step; a
+// wave runs kSteps steps at once with every load issued before the first use.
+// The absmax is reduced across the vector's lanes with shuffles; four lanes
+// make one group of 32 codes, whose three bit planes are assembled with two
+// shuffle steps and written as three 32-bit words.
 #include "bw_device.h"
 #include "bw_internal.h"
 
@@ -16,6 +17,8 @@ namespace bw {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kSteps = 4;         // vectors per lane in flight
+constexpr int64_t kMaxBlocks = 4096;
 
 template <int LPV>  // lanes per vector = D / 8
 __device__ __forceinline__ float vec_max(float v) {
@@ -36,62 +39,70 @@ __global__ __launch_bounds__(kThreads) void k_kv_pack3(const void* __restrict__ 
   const int sub = lane % LPV;       // lane within its vector
   const int64_t waves_total = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
   const int64_t wave_id = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + (threadIdx.x >> 6);
-  for (int64_t base = wave_id * VPW; base < nvec; base += waves_total * VPW) {
-    const int64_t v = base + lane / LPV;
-    const bool active = v < nvec;
-    float x[8];
-    float amax = 0.0f;
-    if (active) {
-      load8<BF16>(kv, v * D + sub * 8, x);
+  for (int64_t base = wave_id * VPW * kSteps; base < nvec; base += waves_total * VPW * kSteps) {
+    // every load of the group (values and the token's slot) is issued before
+    // the first use; vectors past the end re-read the last vector
+    float xs[kSteps][8];
+    int32_t sl[kSteps];
+#pragma unroll
+    for (int u = 0; u < kSteps; ++u) {
+      const int64_t v = base + u * VPW + lane / LPV;
+      const int64_t vc = v < nvec ? v : nvec - 1;
+      load8<BF16>(kv, vc * D + sub * 8, xs[u]);
+      sl[u] = slot_of[vc / H];
+    }
+#pragma unroll
+    for (int u = 0; u < kSteps; ++u) {
+      const int64_t v = base + u * VPW + lane / LPV;
+      const bool active = v < nvec;
+      const float (&x)[8] = xs[u];
+      float amax = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-    } else {
+      amax = vec_max<LPV>(amax);
+      const float a = fmaxf(amax, 1e-5f);
+      const float inv3 = div_rn(3.0f, a);
+      // bit planes of this lane's 8 codes: byte j holds bit j of each code
+      uint32_t pl0 = 0, pl1 = 0, pl2 = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = 0.0f;
-    }
-    amax = vec_max<LPV>(amax);
-    const float a = fmaxf(amax, 1e-5f);
-    const float inv3 = div_rn(3.0f, a);
-    // bit planes of this lane's 8 codes: byte j holds bit j of each code
-    uint32_t pl0 = 0, pl1 = 0, pl2 = 0;
+      for (int i = 0; i < 8; ++i) {
+        const float q = fminf(fmaxf(__builtin_rintf(mul_rn(x[i], inv3)), -4.0f), 3.0f);
+        const uint32_t c = static_cast<uint32_t>(static_cast<int>(q)) & 7u;
+        pl0 |= (c & 1u) << i;
+        pl1 |= ((c >> 1) & 1u) << i;
+        pl2 |= ((c >> 2) & 1u) << i;
+      }
+      // group of 32 codes = 4 lanes; lane q of the group contributes byte q of each plane word
+      const int q4 = sub & 3;
+      pl0 <<= 8 * q4;
+      pl1 <<= 8 * q4;
+      pl2 <<= 8 * q4;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float q = fminf(fmaxf(__builtin_rintf(mul_rn(x[i], inv3)), -4.0f), 3.0f);
-      const uint32_t c = static_cast<uint32_t>(static_cast<int>(q)) & 7u;
-      pl0 |= (c & 1u) << i;
-      pl1 |= ((c >> 1) & 1u) << i;
-      pl2 |= ((c >> 2) & 1u) << i;
-    }
-    // group of 32 codes = 4 lanes; lane q of the group contributes byte q of each plane word
-    const int q4 = sub & 3;
-    pl0 <<= 8 * q4;
-    pl1 <<= 8 * q4;
-    pl2 <<= 8 * q4;
+      for (int off = 1; off <= 2; off <<= 1) {
+        pl0 |= __shfl_xor(pl0, off, kWave);
+        pl1 |= __shfl_xor(pl1, off, kWave);
+        pl2 |= __shfl_xor(pl2, off, kWave);
+      }
+      if (active) {
+        const int grp = sub >> 2;
+        uint32_t* out = reinterpret_cast<uint32_t*>(p3 + v * (3 * D / 8)) + 3 * grp;
+        if (q4 < 3) out[q4] = (q4 == 0) ? pl0 : (q4 == 1 ? pl1 : pl2);
+        if (sub == 0) s3[v] = div_rn(a, 3.0f);
+        const int64_t bs = v / H;
+        const int32_t slot = sl[u];
+        if (slot >= 0 && slot < n_special) {
+          const int64_t hh = v - bs * H;
+          const float inv4 = div_rn(7.0f, a);
+          uint32_t w = 0;
 #pragma unroll
-    for (int off = 1; off <= 2; off <<= 1) {
-      pl0 |= __shfl_xor(pl0, off, kWave);
-      pl1 |= __shfl_xor(pl1, off, kWave);
-      pl2 |= __shfl_xor(pl2, off, kWave);
-    }
-    if (active) {
-      const int grp = sub >> 2;
-      uint32_t* out = reinterpret_cast<uint32_t*>(p3 + v * (3 * D / 8)) + 3 * grp;
-      if (q4 < 3) out[q4] = (q4 == 0) ? pl0 : (q4 == 1 ? pl1 : pl2);
-      if (sub == 0) s3[v] = div_rn(a, 3.0f);
-      const int64_t bs = v / H;
-      const int32_t slot = slot_of[bs];
-      if (slot >= 0 && slot < n_special) {
-        const int64_t hh = v - bs * H;
-        const float inv4 = div_rn(7.0f, a);
-        uint32_t w = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float q = fminf(fmaxf(__builtin_rintf(mul_rn(x[i], inv4)), -8.0f), 7.0f);
-          w |= (static_cast<uint32_t>(static_cast<int>(q)) & 0xFu) << (4 * i);
+          for (int i = 0; i < 8; ++i) {
+            const float q = fminf(fmaxf(__builtin_rintf(mul_rn(x[i], inv4)), -8.0f), 7.0f);
+            w |= (static_cast<uint32_t>(static_cast<int>(q)) & 0xFu) << (4 * i);
+          }
+          const int64_t sv = static_cast<int64_t>(slot) * H + hh;
+          reinterpret_cast<uint32_t*>(p4 + sv * (D / 2))[sub] = w;
+          if (sub == 0) s4[sv] = div_rn(a, 7.0f);
         }
-        const int64_t sv = static_cast<int64_t>(slot) * H + hh;
-        reinterpret_cast<uint32_t*>(p4 + sv * (D / 2))[sub] = w;
-        if (sub == 0) s4[sv] = div_rn(a, 7.0f);
       }
     }
   }
@@ -130,36 +141,54 @@ __global__ __launch_bounds__(kThreads) void k_kv_unpack3(const uint8_t* __restri
   const int sub = lane % LPV;
   const int64_t lanes_total = static_cast<int64_t>(gridDim.x) * kThreads;
   const int64_t gl = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  // every lane owns one (vector, 8-element chunk); chunk index = gl
-  for (int64_t ch = gl; ch < nvec * LPV; ch += lanes_total) {
-    const int64_t v = ch / LPV;
-    float x[8];
-    const int64_t bs = v / H;
-    const int32_t slot = slot_of[bs];
-    if (slot >= 0 && slot < n_special) {
-      const int64_t sv = static_cast<int64_t>(slot) * H + (v - bs * H);
-      const uint32_t w = reinterpret_cast<const uint32_t*>(p4 + sv * (D / 2))[sub];
-      const float sc = s4[sv];
+  const int64_t nch = nvec * LPV;
+  // every lane owns kSteps (vector, 8-element chunk) pairs: chunk = base + u * lanes_total
+  for (int64_t base = gl; base < nch; base += lanes_total * kSteps) {
+    uint32_t pw[kSteps][3];
+    float sc[kSteps];
+    int32_t sl[kSteps];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int q = static_cast<int>(w << (28 - 4 * i)) >> 28;
-        x[i] = mul_rn(static_cast<float>(q), sc);
-      }
-    } else {
-      const uint32_t* g = reinterpret_cast<const uint32_t*>(p3 + v * (3 * D / 8)) + 3 * (sub >> 2);
-      const int sh = 8 * (sub & 3);
-      const uint32_t b0 = (g[0] >> sh) & 0xFFu;
-      const uint32_t b1 = (g[1] >> sh) & 0xFFu;
-      const uint32_t b2 = (g[2] >> sh) & 0xFFu;
-      const float sc = s3[v];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t c = ((b0 >> i) & 1u) | (((b1 >> i) & 1u) << 1) | (((b2 >> i) & 1u) << 2);
-        const int q = static_cast<int>(c << 29) >> 29;
-        x[i] = mul_rn(static_cast<float>(q), sc);
-      }
+    for (int u = 0; u < kSteps; ++u) {
+      const int64_t ch = base + u * lanes_total;
+      const int64_t v = (ch < nch ? ch : nch - 1) / LPV;
+      const uint32_t* gp = reinterpret_cast<const uint32_t*>(p3 + v * (3 * D / 8)) + 3 * (sub >> 2);
+      pw[u][0] = gp[0];
+      pw[u][1] = gp[1];
+      pw[u][2] = gp[2];
+      sc[u] = s3[v];
+      sl[u] = slot_of[v / H];
     }
-    store8<BF16>(out, v * D + sub * 8, x);
+#pragma unroll
+    for (int u = 0; u < kSteps; ++u) {
+      const int64_t ch = base + u * lanes_total;
+      if (ch >= nch) continue;
+      const int64_t v = ch / LPV;
+      float x[8];
+      const int32_t slot = sl[u];
+      if (slot >= 0 && slot < n_special) {
+        const int64_t bs = v / H;
+        const int64_t sv = static_cast<int64_t>(slot) * H + (v - bs * H);
+        const uint32_t w = reinterpret_cast<const uint32_t*>(p4 + sv * (D / 2))[sub];
+        const float s4v = s4[sv];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int q = static_cast<int>(w << (28 - 4 * i)) >> 28;
+          x[i] = mul_rn(static_cast<float>(q), s4v);
+        }
+      } else {
+        const int sh = 8 * (sub & 3);
+        const uint32_t b0 = (pw[u][0] >> sh) & 0xFFu;
+        const uint32_t b1 = (pw[u][1] >> sh) & 0xFFu;
+        const uint32_t b2 = (pw[u][2] >> sh) & 0xFFu;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t c = ((b0 >> i) & 1u) | (((b1 >> i) & 1u) << 1) | (((b2 >> i) & 1u) << 2);
+          const int q = static_cast<int>(c << 29) >> 29;
+          x[i] = mul_rn(static_cast<float>(q), sc[u]);
+        }
+      }
+      store8<BF16>(out, v * D + sub * 8, x);
+    }
   }
 }
 
@@ -167,9 +196,9 @@ template <bool BF16>
 hipError_t pack_t(const void* kv, int64_t nvec, int64_t H, int64_t D, const int32_t* slot_of,
                   int64_t ns, uint8_t* p3, float* s3, uint8_t* p4, float* s4, hipStream_t s) {
   const int64_t lpv = D / 8;
-  const int64_t vpb = (kThreads / lpv);  // vectors per block per iteration
+  const int64_t vpb = (kThreads / lpv) * kSteps;  // vectors per block per iteration
   int64_t blocks = (nvec + vpb - 1) / vpb;
-  if (blocks > 65536) blocks = 65536;
+  if (blocks > kMaxBlocks) blocks = kMaxBlocks;
   const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
   switch (lpv) {
     case 4: hipLaunchKernelGGL((k_kv_pack3<BF16, 4>), grid, block, 0, s, kv, nvec, H, slot_of, ns, p3, s3, p4, s4); break;
@@ -186,8 +215,8 @@ hipError_t unpack_t(const uint8_t* p3, const float* s3, const uint8_t* p4, const
                     const int32_t* slot_of, int64_t nvec, int64_t H, int64_t D, int64_t ns, void* out,
                     hipStream_t s) {
   const int64_t lpv = D / 8;
-  int64_t blocks = (nvec * lpv + kThreads - 1) / kThreads;
-  if (blocks > 65536) blocks = 65536;
+  int64_t blocks = (nvec * lpv + kThreads * kSteps - 1) / (kThreads * kSteps);
+  if (blocks > kMaxBlocks) blocks = kMaxBlocks;
   const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
   switch (lpv) {
     case 4: hipLaunchKernelGGL((k_kv_unpack3<BF16, 4>), grid, block, 0, s, p3, s3, p4, s4, slot_of, nvec, H, ns, out); break;

@@ -4,9 +4,12 @@
 // (INT4/FP4 kernels).  toshoseti review «Метод»: the q/k/v/gate/up inputs are
 // the 4-bit group; FP4 is the wider-range alternative to INT4.
 //
-// One workgroup (256 threads) per token row.  The row is read once into
-// registers when it fits (K <= 256*8*kMaxChunks) and otherwise streamed twice
-// (the second read hits L2).  The per-row absmax is exact and order-free.
+// One wave per token row, four rows per workgroup: the row maximum is a
+// wave-level reduction (no workgroup barrier).  Each lane owns 8-element
+// chunks c = lane + 64*i; rows of up to 64*8*kMaxChunks elements stay in
+// registers, loaded with unconditional (clamped-address) loads so all of them
+// are in flight before the first use; longer rows are streamed twice (the
+// second read hits L2).  The absmax is exact and order-free.
 #include "bw_device.h"
 #include "bw_internal.h"
 
@@ -14,7 +17,8 @@ namespace bw {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxChunks = 4;  // 8-element chunks per thread held in registers
+constexpr int kRowsPerBlock = kThreads / kWave;
+constexpr int kMaxChunks = 8;  // 8-element chunks per lane held in registers (K <= 4096)
 
 // INT4 code of t = fl(x * inv): clamp(rne(t), -8, 7) as a 4-bit field.
 __device__ __forceinline__ uint32_t int4_code(float t) {
@@ -44,12 +48,12 @@ __device__ __forceinline__ uint32_t encode8(const float (&v)[8], float inv) {
 }
 
 template <bool BF16, int FMT, bool RESIDENT>
-__global__ __launch_bounds__(kThreads) void k_quantize_act4(const void* __restrict__ x, int64_t K,
+__global__ __launch_bounds__(kThreads) void k_quantize_act4(const void* __restrict__ x, int64_t M, int64_t K,
                                                             uint8_t* __restrict__ codes,
                                                             float* __restrict__ scales) {
-  __shared__ float red[4];
-  const int64_t m = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int64_t m = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
+  if (m >= M) return;  // whole wave leaves together
   const int64_t nchunk = K >> 3;
   const int64_t row = m * K;
   uint32_t* __restrict__ out = reinterpret_cast<uint32_t*>(codes + m * (K >> 1));
@@ -57,24 +61,29 @@ __global__ __launch_bounds__(kThreads) void k_quantize_act4(const void* __restri
   float amax = 0.0f;
   float v[kMaxChunks][8];
   if constexpr (RESIDENT) {
+    // unconditional loads (chunks past the row re-read chunk 0), so every load
+    // is in flight before the first use
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) {
-      const int64_t ch = tid + c * kThreads;
-      if (ch < nchunk) {
-        load8<BF16>(x, row + ch * 8, v[c]);
+      const int64_t ch = lane + c * kWave;
+      load8<BF16>(x, row + (ch < nchunk ? ch : 0) * 8, v[c]);
+    }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
-      }
+    for (int c = 0; c < kMaxChunks; ++c) {
+      const int64_t ch = lane + c * kWave;
+      const bool in_row = ch < nchunk;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, in_row ? fabsf(v[c][i]) : 0.0f);
     }
   } else {
-    for (int64_t ch = tid; ch < nchunk; ch += kThreads) {
+    for (int64_t ch = lane; ch < nchunk; ch += kWave) {
       float t[8];
       load8<BF16>(x, row + ch * 8, t);
 #pragma unroll
       for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(t[i]));
     }
   }
-  amax = block_max256(amax, red);
+  amax = wave_max(amax);
   const float a = fmaxf(amax, 1e-5f);
   const float qmax = (FMT == 0) ? 7.0f : 6.0f;
   const float inv = div_rn(qmax, a);
@@ -82,27 +91,26 @@ __global__ __launch_bounds__(kThreads) void k_quantize_act4(const void* __restri
   if constexpr (RESIDENT) {
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) {
-      const int64_t ch = tid + c * kThreads;
+      const int64_t ch = lane + c * kWave;
       if (ch < nchunk) out[ch] = encode8<FMT>(v[c], inv);
     }
   } else {
-    for (int64_t ch = tid; ch < nchunk; ch += kThreads) {
+    for (int64_t ch = lane; ch < nchunk; ch += kWave) {
       float t[8];
       load8<BF16>(x, row + ch * 8, t);
       out[ch] = encode8<FMT>(t, inv);
     }
   }
-  if (tid == 0) scales[m] = div_rn(a, qmax);
+  if (lane == 0) scales[m] = div_rn(a, qmax);
 }
 
 template <bool BF16, int FMT>
-hipError_t launch_t(const void* x, int64_t M, int64_t K, uint8_t* codes, float* scales,
-                    hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(M)), block(kThreads);
-  if (K <= static_cast<int64_t>(kThreads) * 8 * kMaxChunks) {
-    hipLaunchKernelGGL((k_quantize_act4<BF16, FMT, true>), grid, block, 0, s, x, K, codes, scales);
+hipError_t launch_t(const void* x, int64_t M, int64_t K, uint8_t* codes, float* scales, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((M + kRowsPerBlock - 1) / kRowsPerBlock)), block(kThreads);
+  if (K <= static_cast<int64_t>(kWave) * 8 * kMaxChunks) {
+    hipLaunchKernelGGL((k_quantize_act4<BF16, FMT, true>), grid, block, 0, s, x, M, K, codes, scales);
   } else {
-    hipLaunchKernelGGL((k_quantize_act4<BF16, FMT, false>), grid, block, 0, s, x, K, codes, scales);
+    hipLaunchKernelGGL((k_quantize_act4<BF16, FMT, false>), grid, block, 0, s, x, M, K, codes, scales);
   }
   return hipGetLastError();
 }

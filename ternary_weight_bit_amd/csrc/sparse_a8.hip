@@ -6,12 +6,17 @@
 // down projection input.  9pt.com article, methodology: the low-magnitude
 // entries are the ones dropped.
 //
-// One workgroup (256 threads) per token row; thread t owns entries
-// t + 256*r, kept in registers.  The k-th largest magnitude tau is found by
-// bisection over the 31 magnitude bits (count of keys >= candidate, reduced
-// across the block); entries equal to tau are taken lowest index first, the
-// cut found from per-64-entry ballot masks.  Everything runs on the row held
-// in registers: the row is read from HBM once and its codes written once.
+// One workgroup (256 threads) per token row.  The row is read with 16-byte
+// loads (8 consecutive entries per thread, all issued before the first use),
+// h is formed and written to LDS, and read back so that thread t owns entries
+// t + 256*r in registers.  The k-th largest magnitude tau is found by
+// bisection over the magnitude bits below the row maximum's top bit; each
+// step counts keys >= candidate with one ballot + popcount per register (a
+// scalar-unit count, no cross-lane shuffles) and one workgroup barrier.  When
+// a row has fewer than k nonzero magnitudes (common after ReLU^2), tau = 0 and
+// no search runs.  Entries equal to tau are taken lowest index first, the
+// cut found from per-64-entry ballot masks.  The row is read from HBM once
+// and its codes written once.
 #include "bw_device.h"
 #include "bw_internal.h"
 
@@ -19,6 +24,16 @@ namespace bw {
 namespace {
 
 constexpr int kThreads = 256;
+
+// Number of this wave's keys >= cand, as a wave-uniform value: one ballot and
+// one popcount per register (scalar unit), no cross-lane shuffles.
+template <int R>
+__device__ __forceinline__ int wave_count_ge(const uint32_t (&key)[R], uint32_t cand) {
+  int cnt = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) cnt += __popcll(__ballot(key[r] >= cand));
+  return cnt;
+}
 
 template <bool BF16, bool GATED, int R>
 __global__ __launch_bounds__(kThreads) void k_sparse_a8(const void* __restrict__ g,
@@ -28,6 +43,7 @@ __global__ __launch_bounds__(kThreads) void k_sparse_a8(const void* __restrict__
                                                         uint32_t* __restrict__ mask) {
   __shared__ int part[2][4];
   __shared__ float red[4];
+  __shared__ __attribute__((aligned(16))) float hs[R * kThreads];
   __shared__ unsigned long long segmask[R * 4];
   __shared__ int segcnt[R * 4];
   __shared__ int cut_sh;
@@ -38,55 +54,83 @@ __global__ __launch_bounds__(kThreads) void k_sparse_a8(const void* __restrict__
   const int64_t row = static_cast<int64_t>(blockIdx.x) * K;
   const int nr = (K + kThreads - 1) / kThreads;  // rounds actually used (K % 64 == 0)
 
+  // Block-wide total of a wave-uniform count (one barrier; parity-buffered).
+  int par = 0;
+  auto block_total = [&](int wave_cnt) {
+    if (lane == 0) part[par][wave] = wave_cnt;
+    __syncthreads();
+    const int t = part[par][0] + part[par][1] + part[par][2] + part[par][3];
+    par ^= 1;
+    return t;
+  };
+
+  // load: thread t takes 8-entry chunks t + 256*c (clamped in-bounds, masked later)
+  constexpr int CPT = R / 8;  // chunks per thread
+  const int nch = K >> 3;
+  {
+    float gv[CPT][8];
+    float uv[CPT][8];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * kThreads;
+      const int64_t e0 = row + static_cast<int64_t>(ch < nch ? ch : 0) * 8;
+      load8<BF16>(g, e0, gv[c]);
+      if constexpr (GATED) load8<BF16>(u, e0, uv[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * kThreads;
+      if (ch < nch) {
+        float hv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float v = gv[c][i];
+          if constexpr (GATED) {
+            const float rr = v > 0.0f ? v : 0.0f;
+            v = mul_rn(mul_rn(rr, rr), uv[c][i]);
+          }
+          hv[i] = v;
+        }
+        *reinterpret_cast<float4*>(&hs[ch * 8]) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+        *reinterpret_cast<float4*>(&hs[ch * 8 + 4]) = make_float4(hv[4], hv[5], hv[6], hv[7]);
+      }
+    }
+  }
+  __syncthreads();
+
   float h[R];
+  uint32_t key[R];  // |h| as ordered integer bits; entries past K hold 0
   float amax = 0.0f;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    h[r] = 0.0f;
     const int idx = tid + r * kThreads;
-    if (r < nr && idx < K) {
-      float v = load1<BF16>(g, row + idx);
-      if constexpr (GATED) {
-        const float rr = v > 0.0f ? v : 0.0f;
-        v = mul_rn(mul_rn(rr, rr), load1<BF16>(u, row + idx));
-      }
-      h[r] = v;
-      amax = fmaxf(amax, fabsf(v));
-    }
+    h[r] = (r < nr && idx < K) ? hs[idx] : 0.0f;
+    amax = fmaxf(amax, fabsf(h[r]));
+    key[r] = __float_as_uint(h[r]) & 0x7FFFFFFFu;
   }
   amax = block_max256(amax, red);
 
-  // tau = largest key value with count(key >= tau) >= k_keep (bisection over bits 30..0).
+  // tau = the k-th largest key = largest value with count(key >= tau) >= k_keep.
   uint32_t tau = 0;
-  int it = 0;
-  for (int b = 30; b >= 0; --b, ++it) {
-    const uint32_t cand = tau | (1u << b);
-    int cnt = 0;
-#pragma unroll
-    for (int r = 0; r < R; ++r) cnt += ((__float_as_uint(h[r]) & 0x7FFFFFFFu) >= cand) ? 1 : 0;
-    // entries beyond K hold +0.0 and never reach cand >= 1
-    cnt = wave_sum(cnt);
-    if (lane == 0) part[it & 1][wave] = cnt;
-    __syncthreads();
-    const int total = part[it & 1][0] + part[it & 1][1] + part[it & 1][2] + part[it & 1][3];
-    if (total >= k_keep) tau = cand;
+  int n_gt;
+  const int nnz = block_total(wave_count_ge<R>(key, 1u));
+  if (nnz < k_keep) {
+    n_gt = nnz;  // fewer than k nonzeros: tau = 0, every nonzero survives, zeros fill the rest
+  } else {
+    const uint32_t top = __float_as_uint(amax) & 0x7FFFFFFFu;  // >= 1 here
+    for (int b = 31 - __builtin_clz(top); b >= 0; --b) {
+      const uint32_t cand = tau | (1u << b);
+      if (block_total(wave_count_ge<R>(key, cand)) >= k_keep) tau = cand;
+    }
+    n_gt = block_total(wave_count_ge<R>(key, tau + 1u));
   }
-  // count of keys strictly above tau
-  int gt = 0;
-#pragma unroll
-  for (int r = 0; r < R; ++r) gt += ((__float_as_uint(h[r]) & 0x7FFFFFFFu) > tau) ? 1 : 0;
-  gt = wave_sum(gt);
-  if (lane == 0) part[it & 1][wave] = gt;
-  __syncthreads();
-  const int n_gt = part[it & 1][0] + part[it & 1][1] + part[it & 1][2] + part[it & 1][3];
   const int need = k_keep - n_gt;  // >= 1 entries equal to tau, lowest index first
 
   // per-segment (64 consecutive entries) masks of key == tau
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     if (r < nr && tid + r * kThreads < K) {
-      const bool eq = (__float_as_uint(h[r]) & 0x7FFFFFFFu) == tau;
-      const unsigned long long bal = __ballot(eq);
+      const unsigned long long bal = __ballot(key[r] == tau);
       if (lane == 0) {
         segmask[r * 4 + wave] = bal;
         segcnt[r * 4 + wave] = __popcll(bal);

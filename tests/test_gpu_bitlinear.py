@@ -51,7 +51,8 @@ def test_small_bitlinear_m16_k256_n256(fmt):
 
 
 @pytest.mark.parametrize("fmt", [bw.BW_ACT_INT4, bw.BW_ACT_FP4_E2M1])
-@pytest.mark.parametrize("M,K,N", [(1, 64, 16), (37, 320, 208), (130, 1024, 144), (200, 256, 400), (8, 4096, 512)])
+@pytest.mark.parametrize("M,K,N", [(1, 64, 16), (37, 320, 208), (130, 1024, 144), (200, 256, 400), (8, 4096, 512),
+                                   (9, 320, 48), (16, 1088, 32), (17, 512, 64), (3, 11008, 64), (300, 11008, 272)])
 def test_ragged_shapes(fmt, M, K, N):
     x = synth.to_bf16(synth.normal(M + 3 * K + N, (M, K)))
     w = synth.to_bf16(synth.normal(N + 5 * K, (N, K), 0.02))
@@ -141,7 +142,8 @@ def test_prefill_full_shape_sampled():
 
 
 # ---------------------------------------------------------------- W1.58A8
-@pytest.mark.parametrize("M,K,N", [(16, 256, 256), (37, 320, 208), (64, 11008, 256), (130, 4096, 144)])
+@pytest.mark.parametrize("M,K,N", [(16, 256, 256), (37, 320, 208), (64, 11008, 256), (130, 4096, 144),
+                                   (1, 11008, 4096), (8, 11008, 512), (5, 4096, 208)])
 def test_a8_small(M, K, N):
     g, u = synth.gate_up(seed=M + K, M=M, K=K)
     w = synth.to_bf16(synth.normal(N + K, (N, K), 0.02))

@@ -59,6 +59,19 @@ def test_fp32_inputs_and_ties():
         check(f32_dev(g), f32_dev(u), g, u, k, f"ties k={k}")
 
 
+@pytest.mark.parametrize("k", [255, 256, 257])
+def test_nonzero_count_around_k(k):
+    """Rows with exactly k-1, k and k+1 nonzero entries: the k-th largest magnitude is
+    0 only when fewer than k entries are nonzero."""
+    M, K = 6, 512
+    rs = np.random.default_rng(k)
+    x = np.zeros((M, K), np.float32)
+    for m, nz in enumerate([255, 256, 257, 255, 256, 257]):
+        idx = rs.choice(K, size=nz, replace=False)
+        x[m, idx] = rs.standard_normal(nz).astype(np.float32)
+    check(f32_dev(x), None, x, None, k, f"nnz around k={k}")
+
+
 def test_full_down_proj_shape_sampled():
     """M=2048, K=11008 bf16 (the benchmark's launch), 64 sampled rows vs the oracle."""
     M, K = 2048, 11008
