@@ -37,6 +37,28 @@ INT8_PEAK_TOPS = 5000.0  # dense int8 MFMA, MI355X
 FP4_PEAK_TOPS = 10100.0  # dense fp4/fp6 MFMA, MI355X
 
 M_PREFILL, HIDDEN, FFN = 2048, 4096, 11008
+
+# HBM traffic of the dominant kernel (W1.58A4 GEMM, M=2048 K=4096 N=11008) from two
+# rocprofv3 counter passes (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, scales from a plain
+# 256 MiB copy in the same runs; summary in profiles/gemm_int4_m2048_k4096_n11008_hbm_bytes.md).
+# It is reported only while the kernel sources still hash to the digest they were taken at.
+GEMM_TRAFFIC = {
+    "bytes": 180_948_070,
+    "sources": ("gemm.hip", "bw_widen.h", "bw_device.h"),
+    "sha256": "4128de1878affe6d8ff6150af41d6e7e0c7d47a6c9a87960c000c3af7d591eca",
+}
+
+
+def gemm_traffic_bytes():
+    """The recorded counter traffic, or None once the GEMM sources have changed."""
+    import hashlib
+
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "ternary_weight_bit_amd", "csrc")
+    h = hashlib.sha256()
+    for f in GEMM_TRAFFIC["sources"]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return GEMM_TRAFFIC["bytes"] if h.hexdigest() == GEMM_TRAFFIC["sha256"] else None
 DECODE_MS = (1, 2, 4, 8)
 LAYERS = 32
 KV_SHAPE = (8, 4096, 32, 128)
@@ -50,13 +72,18 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle leg")
     p.add_argument("--rows", action="store_true", help="also print a per-row table to stderr")
+    p.add_argument("--only", default="", help="comma-separated row-name prefixes: run just those rows "
+                   "(for profiler passes; `value` is null unless the prefill rows are among them)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="add a row that copies 256 MiB device-to-device (a plain copy kernel of known size, "
+                        "to scale HBM byte counters)")
     return p.parse_args()
 
 
 class Bench:
     """Holds device inputs/outputs and the launch list of one step."""
 
-    def __init__(self):
+    def __init__(self, only=(), copy_calibration=False):
         import torch
 
         import synth
@@ -149,6 +176,13 @@ class Bench:
         self.pk_ws = t.empty(bw.bw_pack_ternary_workspace_bytes(HIDDEN, HIDDEN), dtype=t.uint8, device=dev)
         torch.cuda.synchronize()
         self.launches = self._launch_list()
+        if only:
+            self.launches = [r for r in self.launches if any(r[0].startswith(o) for o in only)]
+        if copy_calibration:
+            n = 256 << 20
+            src = t.empty(n, dtype=t.uint8, device=dev).fill_(1)
+            dst = t.empty_like(src)
+            self.launches.append(("z_copy_256MiB", "GB/s", 2.0 * n, [lambda: dst.copy_(src)]))
 
     # ------------------------------------------------------------------ launches
     def _launch_list(self):
@@ -291,7 +325,7 @@ def main():
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         t0 = time.perf_counter()
-        b = Bench()
+        b = Bench(only=tuple(o for o in args.only.split(",") if o), copy_calibration=args.copy_calibration)
         print(f"bench: inputs resident ({time.perf_counter() - t0:.1f} s)", file=sys.stderr, flush=True)
         n_rows = len(b.launches)
         b.step_eager()  # eager pass before capture
@@ -332,22 +366,28 @@ def main():
         return sum(table[n]["avg_us"] * table[n]["launches_per_step"] for n in names) / 1e3
 
     prefill_ops = 2.0 * M_PREFILL * HIDDEN * (FFN + HIDDEN)
-    prefill_ms = row_ms(("a1_quantize_int4", "a4_gemm_int4_n11008", "a4_gemm_int4_n4096"))
-    value = prefill_ops / (prefill_ms * 1e-3) / 1e12
+    prefill_rows = ("a1_quantize_int4", "a4_gemm_int4_n11008", "a4_gemm_int4_n4096")
+    value = None
+    if all(n in table for n in prefill_rows):
+        value = round(prefill_ops / (row_ms(prefill_rows) * 1e-3) / 1e12, 2)
     gemv = [n for n in table if n.startswith("a5_gemv")]
-    dec_bytes = sum(table[n]["amount_per_launch"] * table[n]["launches_per_step"] for n in gemv)
-    dec_ms = row_ms(gemv)
-    decode_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
-    dom = table["a4_gemm_int4_n11008"]
-    roof = {
-        "bound": "mfma", "kernel": "k_bitlinear<INT4> (W1.58A4 GEMM, M=2048 K=4096 N=11008)",
-        "achieved": dom["rate"], "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
-        "frac": round(dom["rate"] / INT8_PEAK_TOPS, 4), "traffic": None,
-        "note": "int8 MFMA int-ops (2*M*N*K per launch) / average launch duration from HIP events",
-    }
+    decode_gbs = None
+    if gemv:
+        dec_bytes = sum(table[n]["amount_per_launch"] * table[n]["launches_per_step"] for n in gemv)
+        decode_gbs = dec_bytes / (row_ms(gemv) * 1e-3) / 1e9
+    roof = None
+    if "a4_gemm_int4_n11008" in table:
+        dom = table["a4_gemm_int4_n11008"]
+        roof = {
+            "bound": "mfma", "kernel": "k_bitlinear<INT4> (W1.58A4 GEMM, M=2048 K=4096 N=11008)",
+            "achieved": dom["rate"], "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+            "frac": round(dom["rate"] / INT8_PEAK_TOPS, 4), "traffic": gemm_traffic_bytes(),
+            "note": "int8 MFMA int-ops (2*M*N*K per launch) / average launch duration from HIP events; "
+                    "traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE (copy-calibrated)",
+        }
     out = {
         "metric": "BitLinear W1.58A4 prefill TOPS + decode GEMV HBM GB/s at 7B shapes, 1 GPU",
-        "value": round(value, 2),
+        "value": value,
         "unit": "TOPS",
         "n_gpus": 1,
         "steps": args.steps,
@@ -364,14 +404,14 @@ def main():
                                "ternary pack 4096x4096", "global_batch": M_PREFILL, "seq_len": KV_SHAPE[1],
                    "parallelism": "none (1 GPU)"},
         "value_basis": "2*2048*4096*(11008+4096) int ops / time of the INT4 quantizer + both W1.58A4 GEMMs",
-        "decode_gbs": round(decode_gbs, 1),
-        "decode_frac_hbm": round(decode_gbs / HBM_PEAK_GBS, 4),
+        "decode_gbs": None if decode_gbs is None else round(decode_gbs, 1),
+        "decode_frac_hbm": None if decode_gbs is None else round(decode_gbs / HBM_PEAK_GBS, 4),
         "roofline": roof,
         "rows": table,
         "wall_s_timed": round(wall, 3),
     }
     print(f"bench: timed {args.steps} steps, {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.only:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     if args.rows:
         for n, r in table.items():

@@ -41,7 +41,7 @@ class BwError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(lib_path):
         raise ImportError(
-            f"{lib_path} is not built; run `python -m ternary_weight_bit_amd._build` (hipcc, gfx950)"
+            f"{lib_path} is not built; run `python ternary_weight_bit_amd/_build.py` (hipcc, gfx950)"
         )
     lib = ctypes.CDLL(lib_path)
     P, I64, SZ, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int

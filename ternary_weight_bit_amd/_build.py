@@ -1,6 +1,6 @@
 """Build libbw.so in-tree with hipcc for gfx950.
 
-    python -m ternary_weight_bit_amd._build
+    python ternary_weight_bit_amd/_build.py
 
 Every .hip file under csrc/ is compiled to an object file in _build/ and the
 objects are linked into ternary_weight_bit_amd/libbw.so.
