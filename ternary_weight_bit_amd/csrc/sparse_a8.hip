@@ -6,17 +6,22 @@
 // down projection input.  9pt.com article, methodology: the low-magnitude
 // entries are the ones dropped.
 //
-// One workgroup (256 threads) per token row.  The row is read with 16-byte
-// loads (8 consecutive entries per thread, all issued before the first use),
-// h is formed and written to LDS, and read back so that thread t owns entries
-// t + 256*r in registers.  The k-th largest magnitude tau is found by
-// bisection over the magnitude bits below the row maximum's top bit; each
-// step counts keys >= candidate with one ballot + popcount per register (a
-// scalar-unit count, no cross-lane shuffles) and one workgroup barrier.  When
-// a row has fewer than k nonzero magnitudes (common after ReLU^2), tau = 0 and
-// no search runs.  Entries equal to tau are taken lowest index first, the
-// cut found from per-64-entry ballot masks.  The row is read from HBM once
-// and its codes written once.
+// Rows of up to 12288 entries: one wave per token row, no workgroup barrier.
+// Lane l holds entries 512c + 8l + i (i < 8) of every 512-entry chunk c in
+// registers as the fp32 bits of h, read once with 16-byte loads that are all
+// in flight before the first use.  The k-th largest magnitude tau is found by
+// a three-pass radix select over the 31 magnitude bits (11, 10, 10 bits): each
+// pass histograms the still-possible entries into a per-wave LDS array with
+// LDS atomics, and a wave scan over the bins picks the bin holding the k-th
+// largest.  Zeros (half of a ReLU^2 row) never enter a histogram: when fewer
+// than k entries are nonzero, tau = 0 and no pass runs.  Entries equal to tau
+// are taken lowest index first: their rank in index order comes from one
+// ballot per register slot, counted with mbcnt, chunk by chunk.  Codes are
+// written as 8-byte runs per lane.
+//
+// Longer rows (up to 16384) use one workgroup (256 threads) per row: entries
+// t + 256*r in registers, tau found by bisection over the magnitude bits with
+// one ballot + popcount per register and one barrier per step.
 #include "bw_device.h"
 #include "bw_internal.h"
 
@@ -199,16 +204,324 @@ __global__ __launch_bounds__(kThreads) void k_sparse_a8(const void* __restrict__
   if (tid == 0) scales[blockIdx.x] = div_rn(a, 127.0f);
 }
 
+
+// ------------------------------------------------------------ one wave per row
+constexpr int kRowsPerBlock = kThreads / kWave;  // 4 rows (waves) per workgroup
+constexpr int kBins = 2048;                      // first radix pass: bits 30..20
+constexpr int kHist = kBins + kWave;             // + one private discard bin per lane
+
+// Inclusive prefix over the 64 lanes with DPP moves (no LDS round trips):
+// Hillis-Steele within each row of 16 lanes (row_shr 1, 2, 4, 8), then the
+// row totals are carried across rows (row_bcast 15 into rows 1 and 3,
+// row_bcast 31 into rows 2 and 3).  Lanes without a source add the identity.
+__device__ __forceinline__ int wave_incl_scan(int v, int /*lane*/) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
+// Same scheme for the maximum of non-negative values (identity 0).
+__device__ __forceinline__ uint32_t wave_incl_umax(uint32_t v) {
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x111, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x112, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x114, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x118, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x142, 0xa, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x143, 0xc, 0xf, false)));
+  return v;
+}
+
+// Value of lane `l` (wave-uniform l) of v.
+__device__ __forceinline__ int lane_value(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+
+// Register budget: CH*8 keys per lane stay live through the whole kernel.
+template <int CH>
+constexpr int wave_occupancy() { return CH <= 8 ? 4 : 2; }
+
+template <bool BF16, bool GATED, int CH>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(wave_occupancy<CH>(), 8)))
+void k_sparse_a8_wave(const void* __restrict__ g,
+                                                             const void* __restrict__ u, int M, int K,
+                                                             int k_keep, int8_t* __restrict__ codes,
+                                                             float* __restrict__ scales,
+                                                             uint32_t* __restrict__ mask) {
+  __shared__ __attribute__((aligned(16))) int hist_all[kRowsPerBlock][kHist];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int m = blockIdx.x * kRowsPerBlock + wave;
+  if (m >= M) return;  // whole wave leaves together
+  int* hist = hist_all[wave];
+  const int64_t row = static_cast<int64_t>(m) * K;
+  constexpr int SW = (CH + 3) / 4;
+
+  // ---- |h| bits (key) and sign bits of every entry of this lane; entries past
+  // K hold key 0 and are never counted or written
+  uint32_t key[CH][8];
+  uint32_t sg[SW];
+#pragma unroll
+  for (int w = 0; w < SW; ++w) sg[w] = 0;
+  auto put = [&](int c, int i, float v, bool ok) {
+    const uint32_t b = __float_as_uint(v);
+    key[c][i] = ok ? (b & 0x7FFFFFFFu) : 0u;
+    sg[c >> 2] |= (b >> 31) << (8 * (c & 3) + i);
+  };
+  if constexpr (BF16) {
+    uint4 rg[CH], ru[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int e = c * 512 + 8 * lane;
+      const int64_t off = row + ((e < K) ? e : 0);
+      rg[c] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(g) + off);
+      if constexpr (GATED) ru[c] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(u) + off);
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const bool ok = c * 512 + 8 * lane < K;
+      const uint32_t wg[4] = {rg[c].x, rg[c].y, rg[c].z, rg[c].w};
+      uint32_t wu[4] = {0, 0, 0, 0};
+      if constexpr (GATED) { wu[0] = ru[c].x; wu[1] = ru[c].y; wu[2] = ru[c].z; wu[3] = ru[c].w; }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float v = (i & 1) ? bf16_hi(wg[i >> 1]) : bf16_lo(wg[i >> 1]);
+        if constexpr (GATED) {
+          const float up = (i & 1) ? bf16_hi(wu[i >> 1]) : bf16_lo(wu[i >> 1]);
+          const float r = v > 0.0f ? v : 0.0f;
+          v = mul_rn(mul_rn(r, r), up);
+        }
+        put(c, i, v, ok);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int e = c * 512 + 8 * lane;
+      const bool ok = e < K;
+      const int64_t off = row + (ok ? e : 0);
+      float gv[8], uv[8];
+      load8<false>(g, off, gv);
+      if constexpr (GATED) load8<false>(u, off, uv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float v = gv[i];
+        if constexpr (GATED) {
+          const float r = v > 0.0f ? v : 0.0f;
+          v = mul_rn(mul_rn(r, r), uv[i]);
+        }
+        put(c, i, v, ok);
+      }
+    }
+  }
+
+  // The sign words go through an empty asm statement: otherwise the compiler
+  // sees that key | sign rebuilds the loaded bits and keeps those live too,
+  // doubling the registers held through the selection.
+#pragma unroll
+  for (int w = 0; w < SW; ++w) asm volatile("" : "+v"(sg[w]));
+
+  // ---- row maximum (exact, order-free) and count of nonzero magnitudes
+  uint32_t kmax = 0;
+  int nz = 0;
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      kmax = max(kmax, key[c][i]);
+      nz += 1 - static_cast<int>((key[c][i] - 1u) >> 31);  // key < 2^31: top bit of key-1 set iff key == 0
+    }
+  const float amax = __uint_as_float(static_cast<uint32_t>(lane_value(static_cast<int>(wave_incl_umax(kmax)), kWave - 1)));
+  const int nnz = lane_value(wave_incl_scan(nz, lane), kWave - 1);
+
+  // ---- tau = the k_keep-th largest magnitude; n_gt = entries above it
+  uint32_t tau = 0;
+  int n_gt = nnz;
+  if (nnz >= k_keep) {
+    // Radix passes over the nonzero magnitudes: bits 30..20, then 19..10 and
+    // 9..0.  After the first pass the entries left in the chosen bin (usually
+    // a few dozen) are gathered into an LDS list and the last two passes run
+    // over that list alone.
+    int need = k_keep;  // rank of tau among the entries that share the prefix
+    int above = 0;      // entries known to lie above the current prefix range
+    // Bin of the current histogram (per bins a lane) holding the need-th
+    // largest; returns it with the count above it and its own count.
+    auto find_bin = [&](int per, int& bin, int& cum, int& cnt_bin) {
+      int sum = 0;
+      for (int b = 0; b < per; b += 4) {
+        const int4 q = *reinterpret_cast<const int4*>(&hist[lane * per + b]);
+        sum += q.x + q.y + q.z + q.w;
+      }
+      const int incl = wave_incl_scan(sum, lane);
+      const int total = lane_value(incl, kWave - 1);
+      const int over_l = total - incl;  // candidates in higher lanes' bins
+      const int L = __ffsll(static_cast<long long>(__ballot(over_l < need && need <= over_l + sum))) - 1;
+      const int over = lane_value(over_l, L);
+      // within lane L's bins, lane j takes bin L*per + per-1-j (top first)
+      const int cnt = (lane < per) ? hist[L * per + per - 1 - lane] : 0;
+      const int run = wave_incl_scan(cnt, lane);
+      const int J = __ffsll(static_cast<long long>(__ballot(lane < per && over + run >= need))) - 1;
+      bin = L * per + per - 1 - J;
+      cum = over + lane_value(run - cnt, J);
+      cnt_bin = lane_value(cnt, J);
+    };
+    const uint32_t discard = static_cast<uint32_t>(kBins + lane);  // this lane's own bin: no conflicts
+
+    // pass 1: bits 30..20 of every nonzero magnitude.  The candidate test is
+    // plain arithmetic on purpose (the top bit of (k - 1) is set iff k == 0):
+    // lane masks per entry would be kept live and exhaust the scalar registers.
+    for (int b = 0; b < kBins / kWave; b += 4)
+      *reinterpret_cast<int4*>(&hist[lane * (kBins / kWave) + b]) = make_int4(0, 0, 0, 0);
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t k = key[c][i];
+        const uint32_t nzf = 1u - ((k - 1u) >> 31);
+        atomicAdd(&hist[discard + nzf * ((k >> 20) - discard)], 1);
+      }
+    int bin1, cum1, c1;
+    find_bin(kBins / kWave, bin1, cum1, c1);
+    need -= cum1;
+    above += cum1;
+    uint32_t prefix = static_cast<uint32_t>(bin1) << 20;
+
+    // gather the c1 entries of that bin into list[0, c1) (LDS words 1024..2047,
+    // unused by the 1024-bin passes), one ballot + mbcnt per register slot
+    constexpr int kList = 1024;
+    int* list = hist + 1024;
+    const bool gathered = c1 <= kList;
+    if (gathered) {
+      int base = 0;
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t k = key[c][i];
+          const bool f = k != 0u && (k >> 20) == static_cast<uint32_t>(bin1);
+          const uint64_t bm = __ballot(f);
+          const int pos = base + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                     static_cast<uint32_t>(bm >> 32),
+                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bm), 0u)));
+          hist[f ? 1024 + pos : static_cast<int>(discard)] = static_cast<int>(k);
+          base += __popcll(bm);
+        }
+    }
+    // passes 2 and 3: bits 19..10, then 9..0, over the list (or every entry)
+#pragma unroll 1
+    for (int pass = 1; pass < 3; ++pass) {
+      const int shift = (pass == 1) ? 10 : 0;
+      const uint32_t want = prefix >> (shift + 10);
+      for (int b = 0; b < 1024 / kWave; b += 4)
+        *reinterpret_cast<int4*>(&hist[lane * (1024 / kWave) + b]) = make_int4(0, 0, 0, 0);
+      if (gathered) {
+        for (int t = lane; t < c1; t += kWave) {
+          const uint32_t k = static_cast<uint32_t>(list[t]);
+          const bool cand = (k >> (shift + 10)) == want;
+          atomicAdd(&hist[cand ? static_cast<int>((k >> shift) & 1023u) : static_cast<int>(discard)], 1);
+        }
+      } else {
+        // (`zero` is opaque so that -k is not hoisted out of the pass loop as
+        // a second register copy of every key)
+        uint32_t zero = 0;
+        asm volatile("" : "+s"(zero));
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t k = key[c][i];
+            const uint32_t cand = ((((k >> (shift + 10)) ^ want) - 1u) & (zero - k)) >> 31;
+            const uint32_t digit = (k >> shift) & 1023u;
+            atomicAdd(&hist[discard + cand * (digit - discard)], 1);
+          }
+      }
+      int bin, cum, cnt_bin;
+      find_bin(1024 / kWave, bin, cum, cnt_bin);
+      prefix |= static_cast<uint32_t>(bin) << shift;
+      need -= cum;
+      above += cum;
+    }
+    tau = prefix;
+    n_gt = above;
+  }
+  const int need = k_keep - n_gt;  // >= 1 entries equal to tau, lowest index first
+
+  // ---- tie cut in index order, quantize, write codes (and the keep mask).
+  // Entries past K hold key 0 and come last in index order, after K - nnz >=
+  // need valid zeros, so the cut never reaches them: no per-entry bounds test.
+  const float a = fmaxf(amax, 1e-5f);
+  const float inv = div_rn(127.0f, a);
+  // When every entry equal to tau survives (no tie straddles the cut, the
+  // usual case for tau > 0) no ranking is needed.
+  int neq = 0;
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) neq += static_cast<int>(((key[c][i] ^ tau) - 1u) >> 31);  // == tau (keys < 2^31)
+  const bool all_eq = lane_value(wave_incl_scan(neq, lane), kWave - 1) == need;
+  int taken = 0;  // entries equal to tau in earlier chunks (index order)
+  // Output addresses from an opaque copy of the lane's offset: shared with the
+  // load addresses, they would be kept live (one per chunk) through the whole
+  // selection.
+  int lane_off = 8 * lane;
+  asm volatile("" : "+v"(lane_off));
+  int8_t* out = codes + row;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    // rank of this lane's first tau-equal entry in the chunk: equal entries
+    // of lower lanes (one ballot per slot i, counted with mbcnt)
+    int rank = taken;
+    if (!all_eq) {
+      int lower = 0, total = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint64_t bm = __ballot(key[c][i] == tau);
+        lower = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bm >> 32),
+                                          __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bm), lower));
+        total += __popcll(bm);
+      }
+      rank += lower;
+      taken += total;
+    }
+    uint32_t q8[2] = {0u, 0u};
+    uint32_t kbits = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t k = key[c][i];
+      const int is_eq = static_cast<int>(k == tau);
+      const uint32_t keep = static_cast<uint32_t>(k > tau) | static_cast<uint32_t>(is_eq & (all_eq || rank < need));
+      rank += is_eq;
+      const float h = __uint_as_float(k | (((sg[c >> 2] >> (8 * (c & 3) + i)) & 1u) << 31));
+      const int qv = static_cast<int>(__builtin_amdgcn_fmed3f(__builtin_rintf(mul_rn(h, inv)), -128.0f, 127.0f));
+      const uint32_t q = keep ? (static_cast<uint32_t>(qv) & 0xFFu) : 0u;
+      q8[i >> 2] |= q << (8 * (i & 3));
+      kbits |= keep << i;
+    }
+    const int e = c * 512 + lane_off;
+    if (e < K) {
+      *reinterpret_cast<uint2*>(out + e) = make_uint2(q8[0], q8[1]);
+      if (mask) reinterpret_cast<uint8_t*>(mask)[(row + e) >> 3] = static_cast<uint8_t>(kbits);
+    }
+  }
+  if (lane == 0) scales[m] = div_rn(a, 127.0f);
+}
+
 template <bool BF16, bool GATED>
 hipError_t launch_t(const void* g, const void* u, int64_t M, int64_t K, int64_t k_keep, int8_t* codes,
                     float* scales, uint32_t* mask, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(M)), block(kThreads);
-  const int k = static_cast<int>(K), kk = static_cast<int>(k_keep);
+  const int m = static_cast<int>(M), k = static_cast<int>(K), kk = static_cast<int>(k_keep);
+  const dim3 wgrid(static_cast<unsigned>((M + kRowsPerBlock - 1) / kRowsPerBlock)), block(kThreads);
   if (K <= 4096) {
-    hipLaunchKernelGGL((k_sparse_a8<BF16, GATED, 16>), grid, block, 0, s, g, u, k, kk, codes, scales, mask);
+    hipLaunchKernelGGL((k_sparse_a8_wave<BF16, GATED, 8>), wgrid, block, 0, s, g, u, m, k, kk, codes, scales, mask);
+  } else if (K <= 8192) {
+    hipLaunchKernelGGL((k_sparse_a8_wave<BF16, GATED, 16>), wgrid, block, 0, s, g, u, m, k, kk, codes, scales, mask);
+  } else if (K <= 11264) {
+    hipLaunchKernelGGL((k_sparse_a8_wave<BF16, GATED, 22>), wgrid, block, 0, s, g, u, m, k, kk, codes, scales, mask);
   } else if (K <= 12288) {
-    hipLaunchKernelGGL((k_sparse_a8<BF16, GATED, 48>), grid, block, 0, s, g, u, k, kk, codes, scales, mask);
+    hipLaunchKernelGGL((k_sparse_a8_wave<BF16, GATED, 24>), wgrid, block, 0, s, g, u, m, k, kk, codes, scales, mask);
   } else {
+    const dim3 grid(static_cast<unsigned>(M));
     hipLaunchKernelGGL((k_sparse_a8<BF16, GATED, 64>), grid, block, 0, s, g, u, k, kk, codes, scales, mask);
   }
   return hipGetLastError();
