@@ -8,7 +8,7 @@
 namespace bw {
 
 // Byte size of the scratch words bw_pack_ternary needs in its workspace.
-constexpr size_t kPackWorkspaceBytes = 4096;
+constexpr size_t kPackWorkspaceBytes = 8192;
 
 hipError_t launch_quantize_act4(const void* x, bool bf16, int64_t M, int64_t K, int fmt,
                                 uint8_t* codes, float* scales, hipStream_t s);
