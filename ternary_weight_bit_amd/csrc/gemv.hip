@@ -50,6 +50,15 @@ __global__ __launch_bounds__(kThreads) void k_gemv(const uint8_t* __restrict__ A
   acc_t acc;
   acc[0] = 0; acc[1] = 0; acc[2] = 0; acc[3] = 0;
 
+  // Epilogue scales, loaded first so their latency hides under the weight
+  // stream (16x16 accumulator layout: lane holds column lane % 16, rows
+  // 4*(lane/16) + e).
+  const int64_t n_out = nb * 16 + li;
+  const float bn = beta[n_out];
+  float sxm[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) sxm[e] = sx[(4 * g + e < M) ? 4 * g + e : 0];
+
   // Every load is issued unconditionally from an in-bounds address (rows past M
   // read row 0, tiles past t1 read tile T-1) and masked to zero afterwards, so
   // all of a lane's weight and activation loads are in flight before the first
@@ -105,12 +114,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(const uint8_t* __restrict__ A
     const acc_t p = part[w][lane];
     s[0] += p[0]; s[1] += p[1]; s[2] += p[2]; s[3] += p[3];
   }
-  // 16x16 accumulator layout: lane holds column (lane % 16), rows 4*(lane/16) + e.
-  const int64_t n = nb * 16 + li;
-  const float bn = beta[n];
-  float sxm[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) sxm[e] = sx[(4 * g + e < M) ? 4 * g + e : 0];
+  const int64_t n = n_out;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int m = 4 * g + e;
