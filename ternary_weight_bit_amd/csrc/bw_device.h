@@ -55,6 +55,34 @@ __device__ __forceinline__ int wave_sum(int v) {
   return v;
 }
 
+// Inclusive prefix over the 64 lanes with DPP moves (no LDS round trips):
+// Hillis-Steele within each row of 16 lanes (row_shr 1, 2, 4, 8), then the
+// row totals are carried across rows (row_bcast 15 into rows 1 and 3,
+// row_bcast 31 into rows 2 and 3).  Lanes without a source add the identity.
+__device__ __forceinline__ int wave_incl_scan(int v, int /*lane*/ = 0) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
+// Same scheme for the maximum of non-negative values (identity 0).
+__device__ __forceinline__ uint32_t wave_incl_umax(uint32_t v) {
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x111, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x112, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x114, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x118, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x142, 0xa, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x143, 0xc, 0xf, false)));
+  return v;
+}
+
+// Value of lane `l` (wave-uniform l) of v.
+__device__ __forceinline__ int lane_value(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+
 // Max over a 256-thread block; every thread gets the result.  `red` holds >= 4 floats.
 __device__ __forceinline__ float block_max256(float v, float* red) {
   v = wave_max(v);

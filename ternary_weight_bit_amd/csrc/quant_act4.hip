@@ -4,12 +4,12 @@
 // (INT4/FP4 kernels).  toshoseti review «Метод»: the q/k/v/gate/up inputs are
 // the 4-bit group; FP4 is the wider-range alternative to INT4.
 //
-// One wave per token row, four rows per workgroup: the row maximum is a
-// wave-level reduction (no workgroup barrier).  Each lane owns 8-element
-// chunks c = lane + 64*i; rows of up to 64*8*kMaxChunks elements stay in
-// registers, loaded with unconditional (clamped-address) loads so all of them
-// are in flight before the first use; longer rows are streamed twice (the
-// second read hits L2).  The absmax is exact and order-free.
+// Rows of up to 8192 elements: one workgroup (256 threads) per token row; each
+// thread holds CPT chunks of 8 elements (chunk t + 256*c), loaded with
+// unconditional (clamped-address) loads so all are in flight before the first
+// use; the row maximum is a DPP wave maximum plus one LDS exchange.  Longer
+// rows: one wave per row, four rows per workgroup, streamed twice (the second
+// read hits L2).  The absmax is exact and order-free.
 #include "bw_device.h"
 #include "bw_internal.h"
 
@@ -18,7 +18,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRowsPerBlock = kThreads / kWave;
-constexpr int kMaxChunks = 8;  // 8-element chunks per lane held in registers (K <= 4096)
 
 // INT4 code of t = fl(x * inv): clamp(rne(t), -8, 7) as a 4-bit field.
 __device__ __forceinline__ uint32_t int4_code(float t) {
@@ -47,7 +46,9 @@ __device__ __forceinline__ uint32_t encode8(const float (&v)[8], float inv) {
   return w;
 }
 
-template <bool BF16, int FMT, bool RESIDENT>
+// One wave per row (rows longer than 8192): the row is read twice, once for
+// the maximum and once to encode (the second read hits L2).
+template <bool BF16, int FMT>
 __global__ __launch_bounds__(kThreads) void k_quantize_act4(const void* __restrict__ x, int64_t M, int64_t K,
                                                             uint8_t* __restrict__ codes,
                                                             float* __restrict__ scales) {
@@ -57,60 +58,76 @@ __global__ __launch_bounds__(kThreads) void k_quantize_act4(const void* __restri
   const int64_t nchunk = K >> 3;
   const int64_t row = m * K;
   uint32_t* __restrict__ out = reinterpret_cast<uint32_t*>(codes + m * (K >> 1));
-
   float amax = 0.0f;
-  float v[kMaxChunks][8];
-  if constexpr (RESIDENT) {
-    // unconditional loads (chunks past the row re-read chunk 0), so every load
-    // is in flight before the first use
+  for (int64_t ch = lane; ch < nchunk; ch += kWave) {
+    float t[8];
+    load8<BF16>(x, row + ch * 8, t);
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-      const int64_t ch = lane + c * kWave;
-      load8<BF16>(x, row + (ch < nchunk ? ch : 0) * 8, v[c]);
-    }
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-      const int64_t ch = lane + c * kWave;
-      const bool in_row = ch < nchunk;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, in_row ? fabsf(v[c][i]) : 0.0f);
-    }
-  } else {
-    for (int64_t ch = lane; ch < nchunk; ch += kWave) {
-      float t[8];
-      load8<BF16>(x, row + ch * 8, t);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(t[i]));
-    }
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(t[i]));
   }
   amax = wave_max(amax);
   const float a = fmaxf(amax, 1e-5f);
   const float qmax = (FMT == 0) ? 7.0f : 6.0f;
   const float inv = div_rn(qmax, a);
-
-  if constexpr (RESIDENT) {
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-      const int64_t ch = lane + c * kWave;
-      if (ch < nchunk) out[ch] = encode8<FMT>(v[c], inv);
-    }
-  } else {
-    for (int64_t ch = lane; ch < nchunk; ch += kWave) {
-      float t[8];
-      load8<BF16>(x, row + ch * 8, t);
-      out[ch] = encode8<FMT>(t, inv);
-    }
+  for (int64_t ch = lane; ch < nchunk; ch += kWave) {
+    float t[8];
+    load8<BF16>(x, row + ch * 8, t);
+    out[ch] = encode8<FMT>(t, inv);
   }
   if (lane == 0) scales[m] = div_rn(a, qmax);
+}
+
+// One workgroup per row, CPT chunks of 8 elements per thread (K <= 2048 * CPT).
+template <bool BF16, int FMT, int CPT>
+__global__ __launch_bounds__(kThreads) void k_quantize_act4_row(const void* __restrict__ x, int64_t K,
+                                                                uint8_t* __restrict__ codes,
+                                                                float* __restrict__ scales) {
+  __shared__ uint32_t wmax[kThreads / kWave];
+  const int tid = threadIdx.x;
+  const int64_t m = blockIdx.x;
+  const int64_t nchunk = K >> 3;
+  const int64_t row = m * K;
+  float v[CPT][8];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int64_t ch = tid + c * kThreads;
+    load8<BF16>(x, row + (ch < nchunk ? ch : 0) * 8, v[c]);
+  }
+  uint32_t amax = 0;  // |x| bits: non-negative floats order as integers
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const bool in_row = tid + c * kThreads < nchunk;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = max(amax, in_row ? (__float_as_uint(v[c][i]) & 0x7FFFFFFFu) : 0u);
+  }
+  amax = static_cast<uint32_t>(lane_value(static_cast<int>(wave_incl_umax(amax)), kWave - 1));
+  if ((tid & (kWave - 1)) == 0) wmax[tid / kWave] = amax;
+  __syncthreads();
+  amax = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  const float a = fmaxf(__uint_as_float(amax), 1e-5f);
+  const float qmax = (FMT == 0) ? 7.0f : 6.0f;
+  const float inv = div_rn(qmax, a);
+  uint32_t* __restrict__ out = reinterpret_cast<uint32_t*>(codes + m * (K >> 1));
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int64_t ch = tid + c * kThreads;
+    if (ch < nchunk) out[ch] = encode8<FMT>(v[c], inv);
+  }
+  if (tid == 0) scales[m] = div_rn(a, qmax);
 }
 
 template <bool BF16, int FMT>
 hipError_t launch_t(const void* x, int64_t M, int64_t K, uint8_t* codes, float* scales, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((M + kRowsPerBlock - 1) / kRowsPerBlock)), block(kThreads);
-  if (K <= static_cast<int64_t>(kWave) * 8 * kMaxChunks) {
-    hipLaunchKernelGGL((k_quantize_act4<BF16, FMT, true>), grid, block, 0, s, x, M, K, codes, scales);
+  const dim3 rgrid(static_cast<unsigned>(M));
+  if (K <= 2048) {
+    hipLaunchKernelGGL((k_quantize_act4_row<BF16, FMT, 1>), rgrid, block, 0, s, x, K, codes, scales);
+  } else if (K <= 4096) {
+    hipLaunchKernelGGL((k_quantize_act4_row<BF16, FMT, 2>), rgrid, block, 0, s, x, K, codes, scales);
+  } else if (K <= 8192) {
+    hipLaunchKernelGGL((k_quantize_act4_row<BF16, FMT, 4>), rgrid, block, 0, s, x, K, codes, scales);
   } else {
-    hipLaunchKernelGGL((k_quantize_act4<BF16, FMT, false>), grid, block, 0, s, x, M, K, codes, scales);
+    hipLaunchKernelGGL((k_quantize_act4<BF16, FMT>), grid, block, 0, s, x, M, K, codes, scales);
   }
   return hipGetLastError();
 }
