@@ -74,6 +74,8 @@ def parse():
     p.add_argument("--rows", action="store_true", help="also print a per-row table to stderr")
     p.add_argument("--only", default="", help="comma-separated row-name prefixes: run just those rows "
                    "(for profiler passes; `value` is null unless the prefill rows are among them)")
+    p.add_argument("--no-vendor-gemm", action="store_true",
+                   help="skip timing the vendor library's int8/fp8 GEMMs on the prefill shapes")
     p.add_argument("--copy-calibration", action="store_true",
                    help="add a row that copies 256 MiB device-to-device (a plain copy kernel of known size, "
                         "to scale HBM byte counters)")
@@ -271,6 +273,43 @@ class Bench:
                 ev[2 * i + 1].record(stream)
 
 
+def vendor_gemm_reference(reps: int = 20):
+    """The vendor library's dense GEMMs on the prefill shapes, for context: int8 x int8 -> int32
+    (torch._int_mm) and fp8 e4m3 (torch._scaled_mm), both with plain 8-bit operands (no 4-bit or
+    2-bit unpacking).  Not part of `value`."""
+    import torch
+
+    dev = "cuda:0"
+    out = {}
+    for N in (FFN, HIDDEN):
+        a = torch.randint(-7, 8, (M_PREFILL, HIDDEN), dtype=torch.int8, device=dev)
+        b = torch.randint(-1, 2, (N, HIDDEN), dtype=torch.int8, device=dev).t()
+        one = torch.ones((), device=dev)
+        cases = {"int8_int_mm": lambda: torch._int_mm(a, b)}
+        try:
+            a8, b8 = a.to(torch.float8_e4m3fn), b.to(torch.float8_e4m3fn)
+            cases["fp8_scaled_mm"] = lambda: torch._scaled_mm(a8, b8, one, one, out_dtype=torch.bfloat16)
+        except Exception:  # pragma: no cover - dtype missing in this build
+            pass
+        for name, fn in cases.items():
+            try:
+                for _ in range(3):
+                    fn()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    fn()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / reps
+                out[f"{name}_m{M_PREFILL}_k{HIDDEN}_n{N}"] = {
+                    "avg_us": round(us, 2), "TOPS": round(2.0 * M_PREFILL * N * HIDDEN / us / 1e6, 1)}
+            except Exception as e:  # pragma: no cover - library call unavailable
+                out[f"{name}_m{M_PREFILL}_k{HIDDEN}_n{N}"] = {"error": str(e)[:120]}
+    return out
+
+
 def cpu_baseline(target_s: float):
     """The oracle, as it stands, on a bounded sample of the W1.58A4 prefill work:
     INT4 quantizer + exact contraction + epilogue for a sample of token rows
@@ -411,6 +450,8 @@ def main():
         "wall_s_timed": round(wall, 3),
     }
     print(f"bench: timed {args.steps} steps, {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+    if not args.no_vendor_gemm and not args.only:
+        out["vendor_gemm_reference"] = vendor_gemm_reference()
     if not args.no_cpu_baseline and not args.only:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     if args.rows:
