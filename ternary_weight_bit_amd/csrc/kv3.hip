@@ -8,8 +8,8 @@
 // of D elements spans D/8 lanes and a wave holds 512/D vectors per step; a
 // wave runs kSteps steps at once with every load issued before the first use.
 // The absmax is reduced across the vector's lanes with shuffles; four lanes
-// make one group of 32 codes, whose three bit planes are assembled with two
-// shuffle steps and written as three 32-bit words.
+// make one group of 32 codes, and each lane writes its byte of the group's
+// three bit-plane words.
 #include "bw_device.h"
 #include "bw_internal.h"
 
@@ -19,6 +19,11 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kSteps = 4;         // vectors per lane in flight
 constexpr int64_t kMaxBlocks = 4096;
+// 1.5 * 2^23: adding it to |t| < 2^22 rounds t to an integer (ties to even) that
+// sits, two's complement, in the low mantissa bits; OR-ing a small integer n
+// into its bits gives the float 1.5 * 2^23 + n.
+constexpr float kRoundMagic = 12582912.0f;
+constexpr uint32_t kRoundMagicBits = 0x4B400000u;
 
 template <int LPV>  // lanes per vector = D / 8
 __device__ __forceinline__ float vec_max(float v) {
@@ -62,43 +67,36 @@ __global__ __launch_bounds__(kThreads) void k_kv_pack3(const void* __restrict__ 
       amax = vec_max<LPV>(amax);
       const float a = fmaxf(amax, 1e-5f);
       const float inv3 = div_rn(3.0f, a);
-      // bit planes of this lane's 8 codes: byte j holds bit j of each code
+      // bit planes of this lane's 8 codes: byte j holds bit j of each code.
+      // |x| <= a' makes |x * fl(3/a')| < 3.5, so rne() lands in [-3, 3] and the
+      // clamp to [-4, 3] never acts; adding 1.5 * 2^23 rounds to an integer (ties
+      // to even) and leaves it, two's complement, in the low mantissa bits.
       uint32_t pl0 = 0, pl1 = 0, pl2 = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float q = fminf(fmaxf(__builtin_rintf(mul_rn(x[i], inv3)), -4.0f), 3.0f);
-        const uint32_t c = static_cast<uint32_t>(static_cast<int>(q)) & 7u;
+        const uint32_t c = __float_as_uint(mul_rn(x[i], inv3) + kRoundMagic);
         pl0 |= (c & 1u) << i;
         pl1 |= ((c >> 1) & 1u) << i;
         pl2 |= ((c >> 2) & 1u) << i;
       }
-      // group of 32 codes = 4 lanes; lane q of the group contributes byte q of each plane word
-      const int q4 = sub & 3;
-      pl0 <<= 8 * q4;
-      pl1 <<= 8 * q4;
-      pl2 <<= 8 * q4;
-#pragma unroll
-      for (int off = 1; off <= 2; off <<= 1) {
-        pl0 |= __shfl_xor(pl0, off, kWave);
-        pl1 |= __shfl_xor(pl1, off, kWave);
-        pl2 |= __shfl_xor(pl2, off, kWave);
-      }
+      // group of 32 codes = 4 lanes; lane q of the group writes byte q of each
+      // of the group's three plane words (bytes, not shuffles: cheaper here)
       if (active) {
         const int grp = sub >> 2;
-        uint32_t* out = reinterpret_cast<uint32_t*>(p3 + v * (3 * D / 8)) + 3 * grp;
-        if (q4 < 3) out[q4] = (q4 == 0) ? pl0 : (q4 == 1 ? pl1 : pl2);
+        uint8_t* out = p3 + v * (3 * D / 8) + 12 * grp + (sub & 3);
+        out[0] = static_cast<uint8_t>(pl0);
+        out[4] = static_cast<uint8_t>(pl1);
+        out[8] = static_cast<uint8_t>(pl2);
         if (sub == 0) s3[v] = div_rn(a, 3.0f);
         const int64_t bs = v / H;
         const int32_t slot = sl[u];
         if (slot >= 0 && slot < n_special) {
           const int64_t hh = v - bs * H;
           const float inv4 = div_rn(7.0f, a);
-          uint32_t w = 0;
+          uint32_t w = 0;  // |x * fl(7/a')| < 7.5: codes in [-7, 7], no clamp needed
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float q = fminf(fmaxf(__builtin_rintf(mul_rn(x[i], inv4)), -8.0f), 7.0f);
-            w |= (static_cast<uint32_t>(static_cast<int>(q)) & 0xFu) << (4 * i);
-          }
+          for (int i = 0; i < 8; ++i)
+            w |= (__float_as_uint(mul_rn(x[i], inv4) + kRoundMagic) & 0xFu) << (4 * i);
           const int64_t sv = static_cast<int64_t>(slot) * H + hh;
           reinterpret_cast<uint32_t*>(p4 + sv * (D / 2))[sub] = w;
           if (sub == 0) s4[sv] = div_rn(a, 7.0f);
@@ -108,17 +106,18 @@ __global__ __launch_bounds__(kThreads) void k_kv_pack3(const void* __restrict__ 
   }
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 template <bool BF16>
 __device__ __forceinline__ void store8(void* __restrict__ out, int64_t e, const float (&v)[8]) {
   if constexpr (BF16) {
+    // v_cvt_pk_bf16_f32: two fp32 -> bf16 with round-to-nearest-even
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint32_t lo = __float_as_uint(v[2 * i]);
-      uint32_t hi = __float_as_uint(v[2 * i + 1]);
-      lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;
-      hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
-      w[i] = lo | (hi << 16);
+      const f32x2 p = {v[2 * i], v[2 * i + 1]};
+      w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
     }
     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + e) = make_uint4(w[0], w[1], w[2], w[3]);
   } else {
@@ -170,21 +169,22 @@ __global__ __launch_bounds__(kThreads) void k_kv_unpack3(const uint8_t* __restri
         const int64_t sv = static_cast<int64_t>(slot) * H + (v - bs * H);
         const uint32_t w = reinterpret_cast<const uint32_t*>(p4 + sv * (D / 2))[sub];
         const float s4v = s4[sv];
+        // (nibble ^ 8) = q + 8 in [0, 15]: q exactly as 2^23*1.5 + q + 8 - (2^23*1.5 + 8)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const int q = static_cast<int>(w << (28 - 4 * i)) >> 28;
-          x[i] = mul_rn(static_cast<float>(q), s4v);
+          const uint32_t c = (w >> (4 * i)) & 0xFu;
+          x[i] = mul_rn(__uint_as_float(kRoundMagicBits | (c ^ 8u)) - (kRoundMagic + 8.0f), s4v);
         }
       } else {
         const int sh = 8 * (sub & 3);
         const uint32_t b0 = (pw[u][0] >> sh) & 0xFFu;
         const uint32_t b1 = (pw[u][1] >> sh) & 0xFFu;
         const uint32_t b2 = (pw[u][2] >> sh) & 0xFFu;
+        // (code ^ 4) = q + 4 in [0, 7], turned into the float q exactly as above
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const uint32_t c = ((b0 >> i) & 1u) | (((b1 >> i) & 1u) << 1) | (((b2 >> i) & 1u) << 2);
-          const int q = static_cast<int>(c << 29) >> 29;
-          x[i] = mul_rn(static_cast<float>(q), sc[u]);
+          x[i] = mul_rn(__uint_as_float(kRoundMagicBits | (c ^ 4u)) - (kRoundMagic + 4.0f), sc[u]);
         }
       }
       store8<BF16>(out, v * D + sub * 8, x);
