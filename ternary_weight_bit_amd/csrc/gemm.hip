@@ -10,7 +10,7 @@
 // keeps a wave under 128 VGPRs, so four waves share each SIMD and hide each
 // other's LDS and barrier waits; the operand widening it costs (about six
 // VALU ops per MFMA) co-issues with the matrix instructions.  A stage brings
-// 128 k (64 for INT8 codes) of packed activations and weights into LDS
+// 128 k of packed activations and weights into LDS
 // through registers, double-buffered with one barrier per stage; operands are
 // widened in registers right before v_mfma_i32_32x32x32_i8 (INT4/INT8 codes)
 // or v_mfma_scale_f32_32x32x64_f8f6f4 (e2m1 codes, block scales 2^0).
@@ -31,7 +31,7 @@ constexpr int BN = WN * 64;              // 256 channels
 
 template <int MODE>
 struct Cfg {
-  static constexpr int SLABS = (MODE == MODE_INT8) ? 1 : 2;       // 64-k slabs per stage
+  static constexpr int SLABS = 2;                                 // 64-k slabs per stage
   static constexpr int AB = (MODE == MODE_INT8) ? 64 : 32;        // A bytes per row per slab
   static constexpr int AROW = AB * SLABS;                         // A bytes per row per stage
   static constexpr int ASTR = AROW + 16;                          // padded LDS row stride
@@ -165,8 +165,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
           const int row = wm * 64 + r * 32 + li;
-          const uint4 x0 = *reinterpret_cast<const uint4*>(&As[cur][row * C::ASTR + 32 * lh]);
-          const uint4 x1 = *reinterpret_cast<const uint4*>(&As[cur][row * C::ASTR + 32 * lh + 16]);
+          const uint4 x0 = *reinterpret_cast<const uint4*>(&As[cur][row * C::ASTR + s * 64 + 32 * lh]);
+          const uint4 x1 = *reinterpret_cast<const uint4*>(&As[cur][row * C::ASTR + s * 64 + 32 * lh + 16]);
           const v4i a0 = as_v4i(x0);
           const v4i a1 = as_v4i(x1);
           acc[r][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b00, acc[r][0], 0, 0, 0);
