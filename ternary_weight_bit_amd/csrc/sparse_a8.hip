@@ -464,10 +464,13 @@ void k_sparse_a8_wave(const void* __restrict__ g,
       const int is_eq = static_cast<int>(k == tau);
       const uint32_t keep = static_cast<uint32_t>(k > tau) | static_cast<uint32_t>(is_eq & (all_eq || rank < need));
       rank += is_eq;
+      // |h| <= a' keeps |h * fl(127/a')| below 127.5, so rne() lands in
+      // [-127, 127] and the clamp to [-128, 127] never acts; adding 1.5 * 2^23
+      // rounds to an integer (ties to even) left, two's complement, in the low
+      // mantissa byte.
       const float h = __uint_as_float(k | (((sg[c >> 2] >> (8 * (c & 3) + i)) & 1u) << 31));
-      const int qv = static_cast<int>(__builtin_amdgcn_fmed3f(__builtin_rintf(mul_rn(h, inv)), -128.0f, 127.0f));
-      const uint32_t q = keep ? (static_cast<uint32_t>(qv) & 0xFFu) : 0u;
-      q8[i >> 2] |= q << (8 * (i & 3));
+      const uint32_t code = __float_as_uint(mul_rn(h, inv) + 12582912.0f);
+      q8[i >> 2] |= (keep ? (code & 0xFFu) : 0u) << (8 * (i & 3));
       kbits |= keep << i;
     }
     const int e = c * 512 + lane_off;
