@@ -302,7 +302,7 @@ void k_sparse_a8_wave(const void* __restrict__ g,
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       kmax = max(kmax, key[c][i]);
-      nz += 1 - static_cast<int>((key[c][i] - 1u) >> 31);  // key < 2^31: top bit of key-1 set iff key == 0
+      nz += static_cast<int>(min(key[c][i], 1u));
     }
   const float amax = __uint_as_float(static_cast<uint32_t>(lane_value(static_cast<int>(wave_incl_umax(kmax)), kWave - 1)));
   const int nnz = lane_value(wave_incl_scan(nz, lane), kWave - 1);
@@ -310,6 +310,7 @@ void k_sparse_a8_wave(const void* __restrict__ g,
   // ---- tau = the k_keep-th largest magnitude; n_gt = entries above it
   uint32_t tau = 0;
   int n_gt = nnz;
+  int n_eq = K - nnz;  // entries equal to tau (tau = 0: the valid zeros)
   if (nnz >= k_keep) {
     // Radix passes over the nonzero magnitudes: bits 30..20, then 19..10 and
     // 9..0.  After the first pass the entries left in the chosen bin (usually
@@ -413,6 +414,7 @@ void k_sparse_a8_wave(const void* __restrict__ g,
       prefix |= static_cast<uint32_t>(bin) << shift;
       need -= cum;
       above += cum;
+      n_eq = cnt_bin;  // after the last pass: entries whose 31 bits all equal tau
     }
     tau = prefix;
     n_gt = above;
@@ -426,12 +428,7 @@ void k_sparse_a8_wave(const void* __restrict__ g,
   const float inv = div_rn(127.0f, a);
   // When every entry equal to tau survives (no tie straddles the cut, the
   // usual case for tau > 0) no ranking is needed.
-  int neq = 0;
-#pragma unroll
-  for (int c = 0; c < CH; ++c)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) neq += static_cast<int>(((key[c][i] ^ tau) - 1u) >> 31);  // == tau (keys < 2^31)
-  const bool all_eq = lane_value(wave_incl_scan(neq, lane), kWave - 1) == need;
+  const bool all_eq = n_eq == need;
   int taken = 0;  // entries equal to tau in earlier chunks (index order)
   // Output addresses from an opaque copy of the lane's offset: shared with the
   // load addresses, they would be kept live (one per chunk) through the whole
@@ -462,7 +459,8 @@ void k_sparse_a8_wave(const void* __restrict__ g,
     for (int i = 0; i < 8; ++i) {
       const uint32_t k = key[c][i];
       const int is_eq = static_cast<int>(k == tau);
-      const uint32_t keep = static_cast<uint32_t>(k > tau) | static_cast<uint32_t>(is_eq & (all_eq || rank < need));
+      const uint32_t keep = all_eq ? static_cast<uint32_t>(k >= tau)
+                                   : (static_cast<uint32_t>(k > tau) | static_cast<uint32_t>(is_eq & (rank < need)));
       rank += is_eq;
       // |h| <= a' keeps |h * fl(127/a')| below 127.5, so rne() lands in
       // [-127, 127] and the clamp to [-128, 127] never acts; adding 1.5 * 2^23
