@@ -44,7 +44,7 @@ M_PREFILL, HIDDEN, FFN = 2048, 4096, 11008
 # It is reported only while the kernel sources still hash to the digest they were taken at.
 GEMM_TRAFFIC = {
     "bytes": 181_034_614,
-    "sources": ("gemm.hip", "bw_widen.h", "bw_device.h"),
+    "sources": ("gemm_lds.hip", "bw_widen.h", "bw_device.h"),
     "sha256": "7103657d8048d127ebdca12b1d9529859333c5d4c0140d30d11aba6cd2ef22b5",
 }
 
@@ -418,7 +418,7 @@ def main():
     if "a4_gemm_int4_n11008" in table:
         dom = table["a4_gemm_int4_n11008"]
         roof = {
-            "bound": "mfma", "kernel": "k_bitlinear<INT4> (W1.58A4 GEMM, M=2048 K=4096 N=11008)",
+            "bound": "mfma", "kernel": "k_gemm_lds<INT4> (W1.58A4 GEMM, M=2048 K=4096 N=11008)",
             "achieved": dom["rate"], "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
             "frac": round(dom["rate"] / INT8_PEAK_TOPS, 4), "traffic": gemm_traffic_bytes(),
             "note": "int8 MFMA int-ops (2*M*N*K per launch) / average launch duration from HIP events; "

@@ -26,6 +26,12 @@ hipError_t launch_gemv(int mode, const void* codes, const float* sx, int64_t M, 
 hipError_t launch_gemm(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
                        const uint8_t* w_packed, const float* beta, int64_t N, float* y, void* acc_dbg,
                        hipStream_t s);
+// Prefill GEMM with operands loaded straight into LDS; launch_gemm uses it
+// whenever gemm_lds_supported holds (K % 128 == 0, operands below 2 GiB).
+bool gemm_lds_supported(int mode, int64_t M, int64_t K, int64_t N);
+hipError_t launch_gemm_lds(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
+                           const uint8_t* w_packed, const float* beta, int64_t N, float* y, void* acc_dbg,
+                           hipStream_t s);
 hipError_t launch_bitlinear(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
                             const uint8_t* w_packed, const float* beta, int64_t N, float* y,
                             void* acc_dbg, hipStream_t s);

@@ -1,4 +1,7 @@
 // Prefill-shape BitLinear (M > 16 tokens) for gfx950: MFMA-bound contraction.
+// This register-staged kernel serves the shapes the LDS-streaming kernel
+// (gemm_lds.hip) does not take: K not a multiple of 128, or operands of 2 GiB
+// and more.
 //
 // BitNet a4.8 abstract: ternary layers consume 4-bit activations (INT4/FP4
 // kernels) and sparsified 8-bit states.
@@ -231,6 +234,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
 hipError_t launch_gemm(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
                        const uint8_t* w_packed, const float* beta, int64_t N, float* y, void* acc_dbg,
                        hipStream_t s) {
+  if (gemm_lds_supported(mode, M, K, N)) return launch_gemm_lds(mode, codes, sx, M, K, w_packed, beta, N, y, acc_dbg, s);
   const int MT = static_cast<int>((M + BM - 1) / BM);
   const int NT = static_cast<int>((N + BN - 1) / BN);
   const dim3 grid(static_cast<unsigned>(MT * NT)), block(kThreads);
