@@ -137,8 +137,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
       const_cast<uint8_t*>(Wp + g_first * kblocks * 256), 0, static_cast<int>((ng - g_first) * kblocks * 256),
       kRsrcWord3);
 
+  // Rows of tiles start their k walk at one of four stage offsets (the sums are
+  // exact in any order), so the workgroups in flight do not all read the same
+  // k range of cold operands at once; tiles that share activation rows stay in
+  // step and share them through L2.
+  const int64_t rot = ((t % MT) % 4) * (nst / 4);
   auto issue = [&](int64_t st_req, uint8_t* As, uint8_t* Bs) {
-    const int st = static_cast<int>(st_req < nst ? st_req : nst - 1);  // past the end: reload the last stage
+    int64_t sp = (st_req < nst ? st_req : nst - 1) + rot;  // past the end: reload the last stage
+    if (sp >= nst) sp -= nst;
+    const int st = static_cast<int>(sp);
     // the builtin's operands are plain local values: an array element or a
     // static member in them silently drops the kernel's host-side launch stub
     const int sa = st * C::AROW;
