@@ -427,21 +427,54 @@ void k_sparse_a8_wave(const void* __restrict__ g,
   const float a = fmaxf(amax, 1e-5f);
   const float inv = div_rn(127.0f, a);
   // When every entry equal to tau survives (no tie straddles the cut, the
-  // usual case for tau > 0) no ranking is needed.
+  // usual case for tau > 0) no ranking is needed.  Nor is it when tau = 0 and
+  // no keep mask is asked for: the entries equal to tau are then zeros, whose
+  // code is 0 whether they are kept or not.
   const bool all_eq = n_eq == need;
-  int taken = 0;  // entries equal to tau in earlier chunks (index order)
+  const bool no_rank = all_eq || (tau == 0u && mask == nullptr);
   // Output addresses from an opaque copy of the lane's offset: shared with the
   // load addresses, they would be kept live (one per chunk) through the whole
   // selection.
   int lane_off = 8 * lane;
   asm volatile("" : "+v"(lane_off));
   int8_t* out = codes + row;
+  // |h| <= a' keeps |h * fl(127/a')| below 127.5, so rne() lands in [-127, 127]
+  // and the clamp to [-128, 127] never acts; adding 1.5 * 2^23 rounds to an
+  // integer (ties to even) left, two's complement, in the low mantissa byte.
+  // A dropped entry is quantized as 0.
+  auto code_of = [&](int c, int i, uint32_t keep) {
+    const uint32_t k = key[c][i];
+    const float h = __uint_as_float(k | (((sg[c >> 2] >> (8 * (c & 3) + i)) & 1u) << 31));
+    return __float_as_uint(mul_rn(keep ? h : 0.0f, inv) + 12582912.0f);
+  };
+  // low bytes of four codes -> one word (byte i = code i)
+  auto pack4 = [](uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3) {
+    return __builtin_amdgcn_perm(c1, c0, 0x0c0c0400u) | __builtin_amdgcn_perm(c3, c2, 0x04000c0cu);
+  };
+  if (no_rank) {
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    // rank of this lane's first tau-equal entry in the chunk: equal entries
-    // of lower lanes (one ballot per slot i, counted with mbcnt)
-    int rank = taken;
-    if (!all_eq) {
+    for (int c = 0; c < CH; ++c) {
+      uint32_t q[8];
+      uint32_t kbits = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t keep = static_cast<uint32_t>(key[c][i] >= tau);
+        q[i] = code_of(c, i, keep);
+        kbits |= keep << i;
+      }
+      const int e = c * 512 + lane_off;
+      if (e < K) {
+        *reinterpret_cast<uint2*>(out + e) = make_uint2(pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]));
+        if (mask) reinterpret_cast<uint8_t*>(mask)[(row + e) >> 3] = static_cast<uint8_t>(kbits);
+      }
+    }
+  } else {
+    int taken = 0;  // entries equal to tau in earlier chunks (index order)
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      // rank of this lane's first tau-equal entry in the chunk: equal entries
+      // of lower lanes (one ballot per slot i, counted with mbcnt)
+      int rank = taken;
       int lower = 0, total = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -452,29 +485,22 @@ void k_sparse_a8_wave(const void* __restrict__ g,
       }
       rank += lower;
       taken += total;
-    }
-    uint32_t q8[2] = {0u, 0u};
-    uint32_t kbits = 0;
+      uint32_t q[8];
+      uint32_t kbits = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t k = key[c][i];
-      const int is_eq = static_cast<int>(k == tau);
-      const uint32_t keep = all_eq ? static_cast<uint32_t>(k >= tau)
-                                   : (static_cast<uint32_t>(k > tau) | static_cast<uint32_t>(is_eq & (rank < need)));
-      rank += is_eq;
-      // |h| <= a' keeps |h * fl(127/a')| below 127.5, so rne() lands in
-      // [-127, 127] and the clamp to [-128, 127] never acts; adding 1.5 * 2^23
-      // rounds to an integer (ties to even) left, two's complement, in the low
-      // mantissa byte.
-      const float h = __uint_as_float(k | (((sg[c >> 2] >> (8 * (c & 3) + i)) & 1u) << 31));
-      const uint32_t code = __float_as_uint(mul_rn(h, inv) + 12582912.0f);
-      q8[i >> 2] |= (keep ? (code & 0xFFu) : 0u) << (8 * (i & 3));
-      kbits |= keep << i;
-    }
-    const int e = c * 512 + lane_off;
-    if (e < K) {
-      *reinterpret_cast<uint2*>(out + e) = make_uint2(q8[0], q8[1]);
-      if (mask) reinterpret_cast<uint8_t*>(mask)[(row + e) >> 3] = static_cast<uint8_t>(kbits);
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t k = key[c][i];
+        const int is_eq = static_cast<int>(k == tau);
+        const uint32_t keep = static_cast<uint32_t>(k > tau) | static_cast<uint32_t>(is_eq & (rank < need));
+        rank += is_eq;
+        q[i] = code_of(c, i, keep);
+        kbits |= keep << i;
+      }
+      const int e = c * 512 + lane_off;
+      if (e < K) {
+        *reinterpret_cast<uint2*>(out + e) = make_uint2(pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]));
+        if (mask) reinterpret_cast<uint8_t*>(mask)[(row + e) >> 3] = static_cast<uint8_t>(kbits);
+      }
     }
   }
   if (lane == 0) scales[m] = div_rn(a, 127.0f);
