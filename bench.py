@@ -28,8 +28,10 @@ two GEMMs over the time of the INT4 quantizer and both GEMMs launched back to
 back (row a0, one event pair around the three launches);
 `value_from_separate_rows` divides the same ops by the sum of the individually
 bracketed rows a1 + a4 (each of which also pays its own launch latency).
-`decode_gbs` is the decode GEMV rate in algorithmic bytes; `roofline` covers
-the N=11008 prefill GEMM.
+`b158_baseline` runs the same two projections on BitNet b1.58's activation
+path (INT8 absmax of every entry, no top-k, W1.58A8 GEMMs; row b0) and gives
+the ratio of the two.  `decode_gbs` is the decode GEMV rate in algorithmic
+bytes; `roofline` covers the N=11008 prefill GEMM.
 """
 from __future__ import annotations
 
@@ -118,9 +120,11 @@ class Bench:
         self.x_pre = bf16(synth.prefill_activations(S + 2, M_PREFILL, HIDDEN))
         self.w_up = f32(synth.weight_tensor(S + 12, FFN, HIDDEN))
         self.wp_11008, self.b_11008 = bw.bw_pack_ternary(self.w_up, bw.BW_ROLE_A4)
+        self.wp8_11008, self.b8_11008 = bw.bw_pack_ternary(self.w_up, bw.BW_ROLE_A8)  # b1.58 baseline
         w_q = f32(synth.weight_tensor(S + 11, HIDDEN, HIDDEN))
         self.w_q = w_q
         self.wp_4096, self.b_4096 = bw.bw_pack_ternary(w_q, bw.BW_ROLE_A4)
+        self.wp8_4096, self.b8_4096 = bw.bw_pack_ternary(w_q, bw.BW_ROLE_A8)
         del self.w_up
         self.c4 = t.empty((M_PREFILL, HIDDEN // 2), dtype=t.uint8, device=dev)
         self.s4 = t.empty(M_PREFILL, dtype=t.float32, device=dev)
@@ -129,6 +133,8 @@ class Bench:
         self.y_11008 = t.empty((M_PREFILL, FFN), dtype=t.float32, device=dev)
         self.y_4096 = t.empty((M_PREFILL, HIDDEN), dtype=t.float32, device=dev)
         self.evict = t.empty(384 * 1024 * 1024 // 4, dtype=t.float32, device=dev)
+        self.c8_pre = t.empty((M_PREFILL, HIDDEN), dtype=t.int8, device=dev)
+        self.s8_pre = t.empty(M_PREFILL, dtype=t.float32, device=dev)
         # ---------------- sparse path
         g, u = synth.gate_up(S + 3, M_PREFILL, FFN)
         self.gate, self.up = bf16(g), bf16(u)
@@ -224,6 +230,16 @@ class Bench:
         # untimed: overwrite more than the 256 MB Infinity Cache, so the rows below
         # see the prefill weights cold again, as a0 did
         R.append(("_evict_cache", None, 0, [lambda: self.evict.fill_(1.0)]))
+
+        def prefill_b158():
+            bw.bw_quantize_sparse_a8(self.x_pre, None, K, self.c8_pre, self.s8_pre)
+            bw.bw_bitlinear_sparse_a8(self.c8_pre, self.s8_pre, self.wp8_11008, self.b8_11008, self.y_11008)
+            bw.bw_bitlinear_sparse_a8(self.c8_pre, self.s8_pre, self.wp8_4096, self.b8_4096, self.y_4096)
+
+        # the same two projections on BitNet b1.58's activation path (INT8 absmax of
+        # every entry, no top-k, W1.58A8 GEMMs): the baseline the pages compare against
+        R.append(("b0_prefill_b158_int8_sequence", "TOPS", gemm_ops(M, FFN, K) + gemm_ops(M, HIDDEN, K), [prefill_b158]))
+        R.append(("_evict_cache_2", None, 0, [lambda: self.evict.fill_(2.0)]))
         R.append(("a1_quantize_int4", "GB/s", M * K * 2 + M * K / 2 + 4 * M,
                   [lambda: bw.bw_quantize(self.x_pre, bw.BW_ACT_INT4, self.c4, self.s4)]))
         R.append(("a4_gemm_int4_n11008", "TOPS", gemm_ops(M, FFN, K),
@@ -444,6 +460,9 @@ def main():
         value = round(prefill_ops / (row_ms(("a0_prefill_int4_sequence",)) * 1e-3) / 1e12, 2)
     if all(n in table for n in prefill_rows):
         value_rows = round(prefill_ops / (row_ms(prefill_rows) * 1e-3) / 1e12, 2)
+    b158 = None
+    if "b0_prefill_b158_int8_sequence" in table:
+        b158 = round(prefill_ops / (row_ms(("b0_prefill_b158_int8_sequence",)) * 1e-3) / 1e12, 2)
     gemv = [n for n in table if n.startswith("a5_gemv")]
     decode_gbs = None
     if gemv:
@@ -481,6 +500,10 @@ def main():
         "value_basis": "2*2048*4096*(11008+4096) int ops / time of the INT4 quantizer + both W1.58A4 GEMMs, "
                        "launched back to back as one stream sequence (row a0)",
         "value_from_separate_rows": value_rows,
+        "b158_baseline": None if b158 is None else {
+            "value": b158, "unit": "TOPS",
+            "basis": "same ops / time of INT8 absmax (all entries, no top-k) + both W1.58A8 GEMMs, back to back (row b0)",
+            "a48_over_b158": None if value is None else round(value / b158, 3)},
         "decode_gbs": None if decode_gbs is None else round(decode_gbs, 1),
         "decode_frac_hbm": None if decode_gbs is None else round(decode_gbs / HBM_PEAK_GBS, 4),
         "roofline": roof,

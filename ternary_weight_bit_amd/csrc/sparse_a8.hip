@@ -119,8 +119,8 @@ __global__ __launch_bounds__(kThreads) void k_sparse_a8(const void* __restrict__
   uint32_t tau = 0;
   int n_gt;
   const int nnz = block_total(wave_count_ge<R>(key, 1u));
-  if (nnz < k_keep) {
-    n_gt = nnz;  // fewer than k nonzeros: tau = 0, every nonzero survives, zeros fill the rest
+  if (nnz < k_keep || k_keep >= K) {
+    n_gt = nnz;  // fewer than k nonzeros (or keep-all): tau = 0, every nonzero survives, zeros fill the rest
   } else {
     const uint32_t top = __float_as_uint(amax) & 0x7FFFFFFFu;  // >= 1 here
     for (int b = 31 - __builtin_clz(top); b >= 0; --b) {
@@ -311,7 +311,7 @@ void k_sparse_a8_wave(const void* __restrict__ g,
   uint32_t tau = 0;
   int n_gt = nnz;
   int n_eq = K - nnz;  // entries equal to tau (tau = 0: the valid zeros)
-  if (nnz >= k_keep) {
+  if (nnz >= k_keep && k_keep < K) {  // keep-all (the b1.58 INT8 absmax): no selection
     // Radix passes over the nonzero magnitudes: bits 30..20, then 19..10 and
     // 9..0.  After the first pass the entries left in the chosen bin (usually
     // a few dozen) are gathered into an LDS list and the last two passes run

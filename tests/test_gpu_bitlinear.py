@@ -170,3 +170,25 @@ def test_a8_extreme_codes():
     _, _, q, _ = sparse8.sparse_a8(h, None, K)
     t, _ = ternary.quantize_weights(w)
     assert_same(host(acc), bitlinear.contract(q, t).astype(np.int32), "a8 extreme acc")
+
+
+# ---------------------------------------------------------------- b1.58 baseline path
+@pytest.mark.parametrize("M,K,N", [(37, 4096, 208), (5, 16384, 144), (130, 4096, 272)])
+def test_b158_int8_keep_all(M, K, N):
+    """BitNet b1.58's activation path, which a4.8 is compared against: INT8 absmax of every
+    entry (the sparse front end with k = K, no top-k), then the W1.58A8 contraction.  K=16384
+    takes the one-workgroup-per-row front end, K=4096 the one-wave-per-row one."""
+    x = synth.prefill_activations(seed=M + K + N, M=M, K=K)
+    w = synth.to_bf16(synth.normal(N + 3 * K, (N, K), 0.02))
+    codes, scales = bw.bw_quantize_sparse_a8(bf16_dev(x), None, K)
+    packed, beta = bw.bw_pack_ternary(bf16_dev(w), bw.BW_ROLE_A8)
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda:0")
+    y = bw.bw_bitlinear_sparse_a8(codes, scales, packed, beta, acc_dbg=acc)
+    _, keep, q, s = sparse8.sparse_a8(x.f32, None, K)
+    assert keep.all()
+    assert_same(host(codes), q, f"b1.58 int8 codes {M}x{K}")
+    assert_same(host(scales).view(np.uint32), s.view(np.uint32), f"b1.58 int8 scales {M}x{K}")
+    t, b = ternary.quantize_weights(w.f32)
+    ra = bitlinear.contract(q, t)
+    assert_same(host(acc), ra.astype(np.int32), f"b1.58 acc {M}x{K}x{N}")
+    assert_rel(host(y), bitlinear.epilogue(ra, s, np.full(N, b, np.float32)))
