@@ -16,7 +16,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import act4
+from . import act4, ternary
 
 
 def _exact_int_matmul(a: np.ndarray, b_t: np.ndarray) -> np.ndarray:
@@ -65,3 +65,19 @@ def bitlinear_a4_fp4(x: np.ndarray, t: np.ndarray, beta: np.ndarray):
     c, s = act4.quantize_fp4(x)
     acc = contract_e2m1_doubled(c, t).astype(np.float64) / 2.0
     return c, s, acc, epilogue(acc, s, beta)
+
+
+def contract_gather_kmajor(codes: np.ndarray, packed_kmajor: np.ndarray, N: int) -> np.ndarray:
+    """acc[m][n] = sum over the inputs k with codes[m][k] != 0 of codes[m][k] * t[n][k],
+    reading from the K-major packed weights only the rows of those inputs (the
+    single-token decode product on sparsified 8-bit codes; BitNet a4.8 abstract,
+    55 % of the parameters active).  Dropped inputs add nothing, so this equals
+    contract(codes, t).  Returns int64 [M][N]."""
+    codes = np.asarray(codes)
+    M = codes.shape[0]
+    acc = np.zeros((M, N), dtype=np.int64)
+    for m in range(M):
+        ks = np.flatnonzero(codes[m])
+        rows = ternary.kmajor_rows(packed_kmajor, N, ks)  # [len][N]
+        acc[m] = _exact_int_matmul(codes[m, ks][None, :], rows.T)[0]
+    return acc

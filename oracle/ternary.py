@@ -36,6 +36,7 @@ EPS = np.float32(1e-5)
 
 ROLE_A4 = 0
 ROLE_A8 = 1
+ROLE_A8_KMAJOR = 2
 
 TILE_N = 16
 TILE_K = 64
@@ -75,12 +76,37 @@ def code_offsets(role: int) -> np.ndarray:
     raise ValueError(f"unknown role {role}")
 
 
+def _pack_kmajor(t: np.ndarray) -> np.ndarray:
+    N, K = t.shape
+    code = (t.T.astype(np.int64) + 1).astype(np.uint64)  # [K][N], t + 1
+    grp = code.reshape(K, N // 16, 16)  # [k][g][i], output n = 16g + i
+    shifts = (2 * np.arange(16)).astype(np.uint64)
+    words = (grp << shifts).sum(axis=-1).astype(np.uint32)  # [k][g]
+    return np.ascontiguousarray(words).astype("<u4").view(np.uint8).reshape(-1)
+
+
+def kmajor_rows(packed: np.ndarray, N: int, ks) -> np.ndarray:
+    """Rows t[:, k] for the inputs ks of a K-major packed tensor: int8 [len(ks)][N].
+    Only the N/4 bytes of each listed input are read."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    ks = np.asarray(ks, dtype=np.int64)
+    row_bytes = N // 4
+    rows = np.stack([packed[k * row_bytes : (k + 1) * row_bytes] for k in ks]) if ks.size else (
+        np.zeros((0, row_bytes), np.uint8))
+    words = rows.view("<u4").astype(np.uint64)  # [len][N/16]
+    shifts = (2 * np.arange(16)).astype(np.uint64)
+    code = ((words[..., None] >> shifts) & 3).astype(np.int8)  # [len][g][i]
+    return (code - 1).reshape(len(ks), N)  # code 11 would decode as 2, never written
+
+
 def pack(t: np.ndarray, role: int) -> np.ndarray:
-    """Pack ternary int8 [N][K] into the version-1 layout; returns uint8 [N*K/4]."""
+    """Pack ternary int8 [N][K] into the layout of `role`; returns uint8 [N*K/4]."""
     t = np.asarray(t)
     N, K = t.shape
     if N % TILE_N or K % TILE_K:
         raise ValueError("N must be a multiple of 16 and K of 64")
+    if role == ROLE_A8_KMAJOR:
+        return _pack_kmajor(t)
     code = np.where(t == 1, 1, np.where(t == -1, 3, 0)).astype(np.uint64)
     # [nb][c][kb][j][off]
     c5 = code.reshape(N // TILE_N, TILE_N, K // TILE_K, 4, 16)
@@ -92,7 +118,10 @@ def pack(t: np.ndarray, role: int) -> np.ndarray:
 
 
 def unpack(packed: np.ndarray, N: int, K: int, role: int) -> np.ndarray:
-    """Inverse of pack: uint8 [N*K/4] -> int8 [N][K] (code 10 decodes as -2, never written)."""
+    """Inverse of pack: uint8 [N*K/4] -> int8 [N][K] (code 10 decodes as -2, never written;
+    in the K-major layout code 11 decodes as 2, never written)."""
+    if role == ROLE_A8_KMAJOR:
+        return np.ascontiguousarray(kmajor_rows(packed, N, np.arange(K)).T)
     words = np.ascontiguousarray(packed, dtype=np.uint8).view("<u4").astype(np.uint64)
     words = words.reshape(N // TILE_N, K // TILE_K, TILE_N, 4).transpose(0, 2, 1, 3)
     shifts = (2 * np.arange(16)).astype(np.uint64)

@@ -76,3 +76,22 @@ def test_end_to_end_small_matches_float_reference():
     assert np.all(acc4 * 2 == np.rint(acc4 * 2))
     q, _ = act4.quantize_int4(x)
     assert np.array_equal(bitlinear.contract(q, t), acc)
+
+
+def test_gather_kmajor_matches_dense_and_brute_force():
+    """The row-gather product over K-major weights equals the dense contraction
+    (tiny case also by explicit loops), for sparse, empty and full code rows."""
+    rs = np.random.default_rng(21)
+    N, K = 32, 128
+    t = rs.integers(-1, 2, size=(N, K)).astype(np.int8)
+    q = rs.integers(-128, 128, size=(4, K)).astype(np.int64)
+    q[0, rs.permutation(K)[: K // 2]] = 0  # half dropped
+    q[1] = 0  # every input dropped
+    q[2, ::3] = 0
+    p = ternary.pack(t, ternary.ROLE_A8_KMAJOR)
+    acc = bitlinear.contract_gather_kmajor(q, p, N)
+    assert np.array_equal(acc, bitlinear.contract(q, t))
+    assert not acc[1].any()
+    for m in (0, 3):
+        for n in (0, 7, 31):
+            assert acc[m, n] == sum(int(q[m, k]) * int(t[n, k]) for k in range(K))

@@ -109,3 +109,31 @@ def test_pack_roundtrip(role):
     b = p
     for sh in (0, 2, 4, 6):
         assert not np.any(((b >> sh) & 3) == 2)
+
+
+def test_pack_kmajor_single_weight_positions():
+    """K-major layout written out by hand: input k owns N/4 bytes, output n sits in
+    word n // 16 at bits 2 * (n % 16), code t + 1 (so a zero weight is 01)."""
+    N, K = 48, 128
+    for (n, k, v) in [(0, 0, 1), (0, 1, -1), (5, 17, 1), (16, 64, -1), (47, 127, 1), (31, 8, -1), (20, 100, 0)]:
+        t = np.zeros((N, K), dtype=np.int8)
+        t[n, k] = v
+        p = ternary.pack(t, ternary.ROLE_A8_KMAJOR)
+        assert p.size == N * K // 4
+        expect = np.full(N * K // 4, 0x55, dtype=np.uint8)  # every code 01 (t = 0)
+        byte = k * (N // 4) + 4 * (n // 16) + (2 * (n % 16)) // 8
+        bit = (2 * (n % 16)) % 8
+        expect[byte] = (0x55 & ~(3 << bit)) | ((v + 1) << bit)
+        assert np.array_equal(p, expect), (n, k, v)
+
+
+def test_pack_kmajor_roundtrip_and_rows():
+    rs = np.random.default_rng(18)
+    t = rs.integers(-1, 2, size=(80, 192)).astype(np.int8)
+    p = ternary.pack(t, ternary.ROLE_A8_KMAJOR)
+    assert np.array_equal(ternary.unpack(p, 80, 192, ternary.ROLE_A8_KMAJOR), t)
+    ks = [191, 0, 77, 77, 3]
+    assert np.array_equal(ternary.kmajor_rows(p, 80, ks), t[:, ks].T)
+    # code 11 is never written
+    for sh in (0, 2, 4, 6):
+        assert not np.any(((p >> sh) & 3) == 3)
