@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define BW_ABI_VERSION 1
+#define BW_ABI_VERSION 2
 #define BW_PACK_LAYOUT_VERSION 1
 
 typedef enum {
@@ -68,8 +68,9 @@ typedef enum {
 /* Which activations a packed weight meets; selects the within-word order of
  * the 2-bit codes (both orders are 2 bits per weight, same tile structure). */
 typedef enum {
-  BW_ROLE_A4 = 0, /* q/k/v/gate/up: meets 4-bit activations (bw_bitlinear_a4) */
-  BW_ROLE_A8 = 1  /* out_proj/down_proj: meets 8-bit codes (bw_bitlinear_sparse_a8) */
+  BW_ROLE_A4 = 0,        /* q/k/v/gate/up: meets 4-bit activations (bw_bitlinear_a4) */
+  BW_ROLE_A8 = 1,        /* out_proj/down_proj: meets 8-bit codes (bw_bitlinear_sparse_a8) */
+  BW_ROLE_A8_KMAJOR = 2  /* out_proj/down_proj, K-major rows for bw_bitlinear_sparse_a8_gather */
 } bw_weight_role;
 
 /* host */ int bw_abi_version(void);
@@ -94,6 +95,10 @@ const char* bw_last_error(void);
  *   code slot i (bits 2i..2i+1) holds input offset
  *     BW_ROLE_A4: (i odd ? 8 : 0) + i/2
  *     BW_ROLE_A8: 4*(i%4) + i/4
+ * BW_ROLE_A8_KMAJOR instead stores one contiguous run per input: input k
+ *   owns bytes [k*N/4, (k+1)*N/4); little-endian uint32 word g of the run
+ *   holds outputs 16g + i (i = 0..15) at bits 2i..2i+1 with code t + 1
+ *   (00 = -1, 01 = 0, 10 = +1; 11 is never written).
  * beta[N] (fp32) receives beta' in every entry, so the packed bytes and beta
  * arrays of separately-scaled tensors (fused q/k/v, gate/up) concatenate
  * along N.
@@ -180,6 +185,32 @@ bw_status bw_quantize_sparse_a8(const void* gate_or_x, const void* up, bw_dtype 
 bw_status bw_bitlinear_sparse_a8(const int8_t* codes, const float* x_scales, int64_t M, int64_t K,
                                  const uint8_t* w_packed, const float* beta, int64_t N, float* y,
                                  int32_t* acc_dbg, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * W1.58A8 product that reads only the weight rows of nonzero codes.
+ * Source: BitNet a4.8 abstract (only 55 % of the parameters are active, the
+ * sparsified inputs of out_proj/down_proj being mostly zeros); toshoseti
+ * review, «Метод» (the top-k pattern is random, so a tiled weight layout
+ * cannot skip it).  Computes exactly what bw_bitlinear_sparse_a8 computes,
+ *   acc[m][n] = sum_k codes[m][k] * t[n][k]  (int32, exact)
+ *   y[m][n]   = fl( fl(acc * x_scales[m]) * beta[n] )
+ * but each token reads from the BW_ROLE_A8_KMAJOR weights only the rows k
+ * with codes[m][k] != 0: at 50 % sparsity half of the weight bytes.  Tokens
+ * are independent, so it saves bytes only at M = 1 (single-token decode);
+ * larger M re-reads the weights once per token.
+ * w_kmajor: BW_ROLE_A8_KMAJOR layout.  acc_dbg: NULL or int32 [M][N].
+ * workspace: device, >= bw_bitlinear_sparse_a8_gather_workspace_bytes(M, N)
+ *   bytes (int32 accumulators and counters).  It must be all zero before its
+ *   first use (e.g. allocated zeroed); every call that completes leaves it
+ *   zero again.  Calls sharing one workspace must be stream-ordered.
+ * Shapes: K % 64 == 0, K <= 131072, N % 16 == 0, 1 <= M <= 65535,
+ *   N*K/4 <= 2^31.
+ * ------------------------------------------------------------------------ */
+/* host */ size_t bw_bitlinear_sparse_a8_gather_workspace_bytes(int64_t M, int64_t N);
+bw_status bw_bitlinear_sparse_a8_gather(const int8_t* codes, const float* x_scales, int64_t M,
+                                        int64_t K, const uint8_t* w_kmajor, const float* beta,
+                                        int64_t N, float* y, int32_t* acc_dbg, void* workspace,
+                                        size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ *
  * 3-bit KV cache with 4-bit special tokens.

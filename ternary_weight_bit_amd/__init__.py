@@ -15,6 +15,7 @@ import torch
 
 __all__ = [
     "BW_OK", "BW_F32", "BW_BF16", "BW_ACT_INT4", "BW_ACT_FP4_E2M1", "BW_ROLE_A4", "BW_ROLE_A8",
+    "BW_ROLE_A8_KMAJOR", "bw_bitlinear_sparse_a8_gather_workspace_bytes", "bw_bitlinear_sparse_a8_gather",
     "BwError", "lib_path", "bw_abi_version", "bw_pack_layout_version", "bw_last_error",
     "bw_ternary_packed_bytes", "bw_pack_ternary_workspace_bytes", "bw_pack_ternary", "bw_quantize",
     "bw_bitlinear_a4", "bw_quantize_sparse_a8", "bw_bitlinear_sparse_a8", "bw_kv_pack3", "bw_kv_unpack3",
@@ -27,7 +28,7 @@ STATUS_NAMES = {
 }
 BW_F32, BW_BF16 = 0, 1
 BW_ACT_INT4, BW_ACT_FP4_E2M1 = 0, 1
-BW_ROLE_A4, BW_ROLE_A8 = 0, 1
+BW_ROLE_A4, BW_ROLE_A8, BW_ROLE_A8_KMAJOR = 0, 1, 2
 
 lib_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbw.so")
 
@@ -56,6 +57,8 @@ def _load() -> ctypes.CDLL:
         "bw_bitlinear_a4": ([P, P, I64, I64, I, P, P, I64, P, P, P], I),
         "bw_quantize_sparse_a8": ([P, P, I, I64, I64, I64, P, P, P, P], I),
         "bw_bitlinear_sparse_a8": ([P, P, I64, I64, P, P, I64, P, P, P], I),
+        "bw_bitlinear_sparse_a8_gather_workspace_bytes": ([I64, I64], SZ),
+        "bw_bitlinear_sparse_a8_gather": ([P, P, I64, I64, P, P, I64, P, P, P, SZ, P], I),
         "bw_kv_pack3": ([P, I, I64, I64, I64, I64, P, I64, P, P, P, P, P], I),
         "bw_kv_unpack3": ([P, P, P, P, P, I64, I64, I64, I64, I64, I, P, P], I),
     }
@@ -209,6 +212,27 @@ def bw_bitlinear_sparse_a8(codes: torch.Tensor, x_scales: torch.Tensor, w_packed
         _dev(beta, "beta", (torch.float32,), (N,)), N,
         _dev(y, "y", (torch.float32,), (M, N)), _opt(acc_dbg, "acc_dbg", (torch.int32,), (M, N)),
         _stream(codes)))
+    return y
+
+
+def bw_bitlinear_sparse_a8_gather_workspace_bytes(M: int, N: int) -> int:
+    return _lib.bw_bitlinear_sparse_a8_gather_workspace_bytes(M, N)
+
+
+def bw_bitlinear_sparse_a8_gather(codes: torch.Tensor, x_scales: torch.Tensor, w_kmajor: torch.Tensor,
+                                  beta: torch.Tensor, workspace: torch.Tensor, y=None, acc_dbg=None):
+    """y [M][N] fp32 from INT8 codes and K-major ternary weights, reading only the rows of
+    nonzero codes.  workspace: uint8, zero before its first use (torch.zeros), left zero."""
+    M, K = codes.shape
+    N = beta.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=codes.device)
+    _check(_lib.bw_bitlinear_sparse_a8_gather(
+        _dev(codes, "codes", (torch.int8,)), _dev(x_scales, "x_scales", (torch.float32,), (M,)), M, K,
+        _dev(w_kmajor, "w_kmajor", (torch.uint8,), (N * K // 4,)),
+        _dev(beta, "beta", (torch.float32,), (N,)), N,
+        _dev(y, "y", (torch.float32,), (M, N)), _opt(acc_dbg, "acc_dbg", (torch.int32,), (M, N)),
+        _dev(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(codes)))
     return y
 
 

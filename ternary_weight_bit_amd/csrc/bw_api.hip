@@ -63,7 +63,8 @@ bw_status bw_pack_ternary(const void* W, bw_dtype w_dtype, int64_t N, int64_t K,
                           void* stream) {
   BW_REQUIRE(W && w_packed && beta && workspace, BW_ERR_NULL, "bw_pack_ternary: NULL pointer");
   BW_REQUIRE(w_dtype == BW_F32 || w_dtype == BW_BF16, BW_ERR_DTYPE, "bw_pack_ternary: bad dtype %d", (int)w_dtype);
-  BW_REQUIRE(role == BW_ROLE_A4 || role == BW_ROLE_A8, BW_ERR_DTYPE, "bw_pack_ternary: bad role %d", (int)role);
+  BW_REQUIRE(role == BW_ROLE_A4 || role == BW_ROLE_A8 || role == BW_ROLE_A8_KMAJOR, BW_ERR_DTYPE,
+             "bw_pack_ternary: bad role %d", (int)role);
   BW_REQUIRE(N >= 1 && K >= 1 && N % 16 == 0 && K % 64 == 0, BW_ERR_SHAPE,
              "bw_pack_ternary: need N %% 16 == 0 and K %% 64 == 0 (N=%lld K=%lld)", (long long)N, (long long)K);
   BW_REQUIRE(N <= (int64_t(1) << 40) / K, BW_ERR_SHAPE, "bw_pack_ternary: N*K must be below 2^40");
@@ -142,6 +143,30 @@ bw_status bw_bitlinear_sparse_a8(const int8_t* codes, const float* x_scales, int
   return hip_status(bw::launch_bitlinear(2, codes, x_scales, M, K, w_packed, beta, N, y, acc_dbg,
                                          static_cast<hipStream_t>(stream)),
                     "bw_bitlinear_sparse_a8");
+}
+
+size_t bw_bitlinear_sparse_a8_gather_workspace_bytes(int64_t M, int64_t N) {
+  if (M <= 0 || N <= 0) return 0;
+  return bw::gather_a8_workspace_bytes(M, N);
+}
+
+bw_status bw_bitlinear_sparse_a8_gather(const int8_t* codes, const float* x_scales, int64_t M, int64_t K,
+                                        const uint8_t* w_kmajor, const float* beta, int64_t N, float* y,
+                                        int32_t* acc_dbg, void* workspace, size_t workspace_bytes, void* stream) {
+  bw_status st = check_gemm("bw_bitlinear_sparse_a8_gather", codes, x_scales, M, K, w_kmajor, beta, N, y, acc_dbg);
+  if (st != BW_OK || M == 0) return st;
+  BW_REQUIRE(M <= 65535, BW_ERR_SHAPE, "bw_bitlinear_sparse_a8_gather: need M <= 65535 (M=%lld)", (long long)M);
+  BW_REQUIRE(N <= (int64_t(1) << 33) / K, BW_ERR_SHAPE,
+             "bw_bitlinear_sparse_a8_gather: the packed weights must stay below 2^31 bytes (N=%lld K=%lld)",
+             (long long)N, (long long)K);
+  BW_REQUIRE(workspace, BW_ERR_NULL, "bw_bitlinear_sparse_a8_gather: NULL workspace");
+  BW_REQUIRE(!misaligned(workspace), BW_ERR_ALIGN, "bw_bitlinear_sparse_a8_gather: workspace must be 16-byte aligned");
+  const size_t need = bw::gather_a8_workspace_bytes(M, N);
+  BW_REQUIRE(workspace_bytes >= need, BW_ERR_ARG, "bw_bitlinear_sparse_a8_gather: workspace needs %zu bytes, got %zu",
+             need, workspace_bytes);
+  return hip_status(bw::launch_gather_a8(codes, x_scales, M, K, w_kmajor, beta, N, y, acc_dbg, workspace,
+                                         static_cast<hipStream_t>(stream)),
+                    "bw_bitlinear_sparse_a8_gather");
 }
 
 static bw_status check_kv(const char* who, int64_t B, int64_t S, int64_t H, int64_t D, int64_t n_special) {

@@ -16,7 +16,8 @@
 // thread then folds the buckets into a 608-bit integer and rounds it once to
 // fp64, which is the correctly-rounded sum; beta = fp32(sum / (N*K)).
 //
-// Launches: clear workspace -> bucket sums -> finalize beta' -> pack words.
+// Launches: clear workspace -> bucket sums -> finalize beta' -> pack words
+// (tile layouts for the GEMMs, or the K-major layout of the gather product).
 #include "bw_device.h"
 #include "bw_internal.h"
 
@@ -217,6 +218,39 @@ __global__ __launch_bounds__(kThreads) void k_pack_words(const void* __restrict_
   }
 }
 
+// K-major layout (out/down weights for the single-token gather product):
+// input k owns the N/4 bytes at k*N/4; word g of that run holds outputs
+// 16g + i at bits 2i, code t + 1.  Thread w covers word (g = w / K, k = w % K),
+// so for each of its 16 reads consecutive threads read consecutive inputs.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_pack_kmajor(const void* __restrict__ W, int64_t N,
+                                                          int64_t K, const uint64_t* __restrict__ ws,
+                                                          uint32_t* __restrict__ packed,
+                                                          float* __restrict__ beta) {
+  const float bp =
+      reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(ws) + kBetaOffset)[0];
+  const int64_t groups = N / 16;
+  const int64_t nwords = groups * K;
+  for (int64_t w = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; w < nwords;
+       w += static_cast<int64_t>(gridDim.x) * kThreads) {
+    const int64_t g = w / K;
+    const int64_t k = w - g * K;
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float v = load1<BF16>(W, (g * 16 + i) * K + k);
+      const bool keep = mul_rn(2.0f, fabsf(v)) > bp;
+      const uint32_t code = keep ? (v < 0.0f ? 0u : 2u) : 1u;  // t + 1
+      word |= code << (2 * i);
+    }
+    packed[k * groups + g] = word;
+  }
+  for (int64_t n = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; n < N;
+       n += static_cast<int64_t>(gridDim.x) * kThreads) {
+    beta[n] = bp;
+  }
+}
+
 template <bool BF16, int ROLE>
 hipError_t launch_t(const void* W, int64_t N, int64_t K, uint8_t* packed, float* beta, void* ws,
                     hipStream_t s) {
@@ -232,8 +266,13 @@ hipError_t launch_t(const void* W, int64_t N, int64_t K, uint8_t* packed, float*
   hipLaunchKernelGGL(k_beta_finalize, dim3(1), dim3(kBuckets), 0, s, w64, static_cast<double>(total));
   int64_t pblocks = (total / 16 + kThreads - 1) / kThreads;
   if (pblocks > 16384) pblocks = 16384;
-  hipLaunchKernelGGL((k_pack_words<BF16, ROLE>), dim3(static_cast<unsigned>(pblocks)),
-                     dim3(kThreads), 0, s, W, N, K, w64, reinterpret_cast<uint32_t*>(packed), beta);
+  if constexpr (ROLE == 2) {
+    hipLaunchKernelGGL((k_pack_kmajor<BF16>), dim3(static_cast<unsigned>(pblocks)), dim3(kThreads), 0,
+                       s, W, N, K, w64, reinterpret_cast<uint32_t*>(packed), beta);
+  } else {
+    hipLaunchKernelGGL((k_pack_words<BF16, ROLE>), dim3(static_cast<unsigned>(pblocks)),
+                       dim3(kThreads), 0, s, W, N, K, w64, reinterpret_cast<uint32_t*>(packed), beta);
+  }
   return hipGetLastError();
 }
 
@@ -242,9 +281,11 @@ hipError_t launch_t(const void* W, int64_t N, int64_t K, uint8_t* packed, float*
 hipError_t launch_pack_ternary(const void* W, bool bf16, int64_t N, int64_t K, int role,
                                uint8_t* packed, float* beta, void* ws, hipStream_t s) {
   if (bf16) {
+    if (role == 2) return launch_t<true, 2>(W, N, K, packed, beta, ws, s);
     return role == 0 ? launch_t<true, 0>(W, N, K, packed, beta, ws, s)
                      : launch_t<true, 1>(W, N, K, packed, beta, ws, s);
   }
+  if (role == 2) return launch_t<false, 2>(W, N, K, packed, beta, ws, s);
   return role == 0 ? launch_t<false, 0>(W, N, K, packed, beta, ws, s)
                    : launch_t<false, 1>(W, N, K, packed, beta, ws, s);
 }

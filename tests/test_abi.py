@@ -24,13 +24,13 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_versions():
-    assert bw.bw_abi_version() == 1
+    assert bw.bw_abi_version() == 2
     assert bw.bw_pack_layout_version() == 1
     assert bw.bw_ternary_packed_bytes(4096, 4096) == 4096 * 4096 // 4
     assert bw.bw_ternary_packed_bytes(0, 64) == 0
@@ -68,6 +68,22 @@ def test_bitlinear_validation():
     g = lib.bw_bitlinear_sparse_a8
     assert g(A, A, 8, 11008, A, A, 4095, A, None, None) == 2
     assert g(A, None, 8, 11008, A, A, 4096, A, None, None) == 1
+
+
+def test_gather_validation():
+    ws = bw.bw_bitlinear_sparse_a8_gather_workspace_bytes(1, 4096)
+    assert ws >= 4 * 4096 + 4 * 8 and ws % 256 == 0
+    assert bw.bw_bitlinear_sparse_a8_gather_workspace_bytes(0, 4096) == 0
+    g = lib.bw_bitlinear_sparse_a8_gather
+    assert g(A, A, 1, 11008, A, A, 4095, A, None, A, ws, None) == 2  # N % 16
+    assert g(A, A, 1, 11000, A, A, 4096, A, None, A, ws, None) == 2  # K % 64
+    assert g(A, A, 70000, 4096, A, A, 4096, A, None, A, 1 << 40, None) == 2  # M
+    assert g(A, A, 1, 131072, A, A, 1 << 17, A, None, A, 1 << 40, None) == 2  # weights above 2^31 bytes
+    assert g(A, A, 1, 11008, A, A, 4096, A, None, None, ws, None) == 1  # workspace
+    assert g(A, A, 1, 11008, A, A, 4096, A, None, MIS, ws, None) == 3
+    assert g(A, A, 1, 11008, A, A, 4096, A, None, A, ws - 1, None) == 5
+    assert "workspace" in bw.bw_last_error()
+    assert g(None, None, 0, 11008, None, None, 4096, None, None, None, 0, None) == 0
 
 
 def test_sparse_validation():

@@ -10,7 +10,8 @@ from tests.gpu_helpers import assert_same, bf16_dev, f32_dev, host
 
 pytestmark = pytest.mark.gpu
 
-ROLES = [(bw.BW_ROLE_A4, ternary.ROLE_A4, "A4"), (bw.BW_ROLE_A8, ternary.ROLE_A8, "A8")]
+ROLES = [(bw.BW_ROLE_A4, ternary.ROLE_A4, "A4"), (bw.BW_ROLE_A8, ternary.ROLE_A8, "A8"),
+         (bw.BW_ROLE_A8_KMAJOR, ternary.ROLE_A8_KMAJOR, "A8K")]
 
 
 def check(w_dev, w32, role_bw, role_or, label):
@@ -37,7 +38,7 @@ def test_ragged_bf16(rb, ro, name, N, K):
 
 
 def test_full_7b_tensors():
-    """One 4096x4096 (q) and one 11008x4096 (gate) tensor, fp32, both roles."""
+    """One 4096x4096 (q) and one 11008x4096 (gate) tensor, fp32, every role."""
     for (N, K), seed in [((4096, 4096), 11), ((11008, 4096), 12)]:
         w = synth.weight_tensor(synth.SEED_BASE + seed, N, K)
         wd = f32_dev(w)
