@@ -199,14 +199,13 @@ bw_status bw_bitlinear_sparse_a8(const int8_t* codes, const float* x_scales, int
  * are independent, so it saves bytes only at M = 1 (single-token decode);
  * larger M re-reads the weights once per token.
  * w_kmajor: BW_ROLE_A8_KMAJOR layout.  acc_dbg: NULL or int32 [M][N].
- * workspace: device, >= bw_bitlinear_sparse_a8_gather_workspace_bytes(M, N)
- *   bytes (int32 accumulators and counters).  It must be all zero before its
- *   first use (e.g. allocated zeroed); every call that completes leaves it
- *   zero again.  Calls sharing one workspace must be stream-ordered.
- * Shapes: K % 64 == 0, K <= 131072, N % 16 == 0, 1 <= M <= 65535,
- *   N*K/4 <= 2^31.
+ * workspace: device, >= bw_bitlinear_sparse_a8_gather_workspace_bytes(M, K, N)
+ *   bytes (int32 partial sums, a few hundred KB at decode shapes); contents
+ *   on entry are ignored.  Calls sharing one workspace must be stream-ordered.
+ * Shapes: K % 64 == 0, K <= 131072, N % 16 == 0, 1 <= M <= 16,
+ *   N*K/4 <= 2^31.  workspace_bytes() returns 0 for shapes outside these.
  * ------------------------------------------------------------------------ */
-/* host */ size_t bw_bitlinear_sparse_a8_gather_workspace_bytes(int64_t M, int64_t N);
+/* host */ size_t bw_bitlinear_sparse_a8_gather_workspace_bytes(int64_t M, int64_t K, int64_t N);
 bw_status bw_bitlinear_sparse_a8_gather(const int8_t* codes, const float* x_scales, int64_t M,
                                         int64_t K, const uint8_t* w_kmajor, const float* beta,
                                         int64_t N, float* y, int32_t* acc_dbg, void* workspace,

@@ -57,7 +57,7 @@ def _load() -> ctypes.CDLL:
         "bw_bitlinear_a4": ([P, P, I64, I64, I, P, P, I64, P, P, P], I),
         "bw_quantize_sparse_a8": ([P, P, I, I64, I64, I64, P, P, P, P], I),
         "bw_bitlinear_sparse_a8": ([P, P, I64, I64, P, P, I64, P, P, P], I),
-        "bw_bitlinear_sparse_a8_gather_workspace_bytes": ([I64, I64], SZ),
+        "bw_bitlinear_sparse_a8_gather_workspace_bytes": ([I64, I64, I64], SZ),
         "bw_bitlinear_sparse_a8_gather": ([P, P, I64, I64, P, P, I64, P, P, P, SZ, P], I),
         "bw_kv_pack3": ([P, I, I64, I64, I64, I64, P, I64, P, P, P, P, P], I),
         "bw_kv_unpack3": ([P, P, P, P, P, I64, I64, I64, I64, I64, I, P, P], I),
@@ -215,14 +215,14 @@ def bw_bitlinear_sparse_a8(codes: torch.Tensor, x_scales: torch.Tensor, w_packed
     return y
 
 
-def bw_bitlinear_sparse_a8_gather_workspace_bytes(M: int, N: int) -> int:
-    return _lib.bw_bitlinear_sparse_a8_gather_workspace_bytes(M, N)
+def bw_bitlinear_sparse_a8_gather_workspace_bytes(M: int, K: int, N: int) -> int:
+    return _lib.bw_bitlinear_sparse_a8_gather_workspace_bytes(M, K, N)
 
 
 def bw_bitlinear_sparse_a8_gather(codes: torch.Tensor, x_scales: torch.Tensor, w_kmajor: torch.Tensor,
                                   beta: torch.Tensor, workspace: torch.Tensor, y=None, acc_dbg=None):
     """y [M][N] fp32 from INT8 codes and K-major ternary weights, reading only the rows of
-    nonzero codes.  workspace: uint8, zero before its first use (torch.zeros), left zero."""
+    nonzero codes.  workspace: uint8, >= bw_bitlinear_sparse_a8_gather_workspace_bytes(M, K, N)."""
     M, K = codes.shape
     N = beta.shape[0]
     if y is None:

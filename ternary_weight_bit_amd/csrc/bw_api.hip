@@ -145,9 +145,9 @@ bw_status bw_bitlinear_sparse_a8(const int8_t* codes, const float* x_scales, int
                     "bw_bitlinear_sparse_a8");
 }
 
-size_t bw_bitlinear_sparse_a8_gather_workspace_bytes(int64_t M, int64_t N) {
-  if (M <= 0 || N <= 0) return 0;
-  return bw::gather_a8_workspace_bytes(M, N);
+size_t bw_bitlinear_sparse_a8_gather_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+  if (M <= 0 || K < 64 || K % 64 != 0 || N <= 0 || M > bw::kGatherMaxM) return 0;
+  return bw::gather_a8_workspace_bytes(M, K, N);
 }
 
 bw_status bw_bitlinear_sparse_a8_gather(const int8_t* codes, const float* x_scales, int64_t M, int64_t K,
@@ -155,13 +155,14 @@ bw_status bw_bitlinear_sparse_a8_gather(const int8_t* codes, const float* x_scal
                                         int32_t* acc_dbg, void* workspace, size_t workspace_bytes, void* stream) {
   bw_status st = check_gemm("bw_bitlinear_sparse_a8_gather", codes, x_scales, M, K, w_kmajor, beta, N, y, acc_dbg);
   if (st != BW_OK || M == 0) return st;
-  BW_REQUIRE(M <= 65535, BW_ERR_SHAPE, "bw_bitlinear_sparse_a8_gather: need M <= 65535 (M=%lld)", (long long)M);
+  BW_REQUIRE(M <= bw::kGatherMaxM, BW_ERR_SHAPE, "bw_bitlinear_sparse_a8_gather: need M <= %lld (M=%lld)",
+             (long long)bw::kGatherMaxM, (long long)M);
   BW_REQUIRE(N <= (int64_t(1) << 33) / K, BW_ERR_SHAPE,
              "bw_bitlinear_sparse_a8_gather: the packed weights must stay below 2^31 bytes (N=%lld K=%lld)",
              (long long)N, (long long)K);
   BW_REQUIRE(workspace, BW_ERR_NULL, "bw_bitlinear_sparse_a8_gather: NULL workspace");
   BW_REQUIRE(!misaligned(workspace), BW_ERR_ALIGN, "bw_bitlinear_sparse_a8_gather: workspace must be 16-byte aligned");
-  const size_t need = bw::gather_a8_workspace_bytes(M, N);
+  const size_t need = bw::gather_a8_workspace_bytes(M, K, N);
   BW_REQUIRE(workspace_bytes >= need, BW_ERR_ARG, "bw_bitlinear_sparse_a8_gather: workspace needs %zu bytes, got %zu",
              need, workspace_bytes);
   return hip_status(bw::launch_gather_a8(codes, x_scales, M, K, w_kmajor, beta, N, y, acc_dbg, workspace,

@@ -36,9 +36,10 @@ hipError_t launch_bitlinear(int mode, const void* codes, const float* sx, int64_
                             const uint8_t* w_packed, const float* beta, int64_t N, float* y,
                             void* acc_dbg, hipStream_t s);
 
-// Single-token gather product over K-major weights; the workspace holds int32
-// accumulators [M][N] and one counter per (token, 512-output chunk).
-size_t gather_a8_workspace_bytes(int64_t M, int64_t N);
+// Single-token gather product over K-major weights; the workspace holds the
+// int32 partial sums [segments][M][N] of its first launch.
+constexpr int64_t kGatherMaxM = 16;
+size_t gather_a8_workspace_bytes(int64_t M, int64_t K, int64_t N);
 hipError_t launch_gather_a8(const int8_t* codes, const float* sx, int64_t M, int64_t K,
                             const uint8_t* w_kmajor, const float* beta, int64_t N, float* y,
                             int32_t* acc_dbg, void* ws, hipStream_t s);

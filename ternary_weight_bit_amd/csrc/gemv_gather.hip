@@ -9,84 +9,96 @@
 // token's product touches only the runs of its nonzero codes, which halves
 // the weight bytes at 50 % sparsity.
 //
-// One launch, grid (segments x column chunks, tokens):
-//   * a workgroup takes a segment of up to kMaxSeg inputs of one token and a
-//     chunk of kCols = 512 outputs (128 bytes of every row);
-//   * it lists the nonzero codes of its segment in LDS (wave ballots, order
-//     free: the sum is exact integer arithmetic);
-//   * each half-wave (row group) walks every eighth listed row; lane c of the
-//     group loads the 4-byte word of outputs 16c..16c+15 of that row, 16 rows
-//     in flight, and accumulates q * (t + 1) two outputs per 32-bit register
-//     (16-bit fields, exact while a group sees at most 127 rows, which the
-//     segment bound guarantees), subtracting sum(q) at the end;
-//   * the eight row groups are summed in LDS and added into an int32
-//     accumulator in the workspace with device-scope atomics;
-//   * the last workgroup of a (token, chunk) -- counted with a wrapping atomic
-//     counter -- reads and clears the accumulators and writes
-//     y = fl(fl(acc * s_x) * beta).
-// The workspace must be zero before the first call; every completed call
-// leaves it zero again.
+// Two launches:
+//   1. grid (segments x column chunks, tokens): a workgroup takes a segment of
+//      up to kMaxSeg inputs of one token and a chunk of kCols = 512 outputs
+//      (128 bytes of every row).  It lists the nonzero codes of its segment in
+//      LDS (order free: the sum is exact integer arithmetic); each half-wave
+//      (row group) walks every sixteenth listed row, lane c of the group
+//      loading the 4-byte word of outputs 16c..16c+15 of that row, and
+//      accumulates q * (t + 1) two outputs per 32-bit register (16-bit fields,
+//      exact while a group sees at most 127 rows, which the segment bound
+//      guarantees), subtracting sum(q) at the end.  The sixteen row groups are
+//      summed in LDS and the segment's int32 partial sums are stored to the
+//      workspace.
+//   2. grid (64-output chunks, tokens): sums the partials of every segment
+//      and writes y = fl(fl(acc * s_x) * beta).
+// Plain stores and a kernel boundary replace device-scope atomics, whose
+// round trips to the coherence point cost more than the weight reads here.
 #include "bw_internal.h"
 
 namespace bw {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kCols = 512;   // outputs per workgroup
-constexpr int kGroups = 8;   // row groups (half-waves) per workgroup
-constexpr int kBatch = 16;   // rows per lane with loads in flight together
-constexpr int kMaxSeg = 960; // inputs per workgroup: multiple of 64, at most 8 * 127 nonzero
-constexpr int kTargetBlocks = 512;
+constexpr int kThreads = 512;
+constexpr int kCols = 512;    // outputs per workgroup
+constexpr int kGroups = 16;   // row groups (half-waves) per workgroup
+constexpr int kBatch = 8;     // rows per lane with loads in flight together
+constexpr int kMaxSeg = 1024; // inputs per workgroup: multiple of 64, at most 16 * 64 nonzero
+constexpr int kTargetBlocks = 256;
+constexpr int kFinishThreads = 256;
+constexpr int kFinishCols = 64;                                 // outputs per finishing workgroup
+constexpr int kFinishSlices = kFinishThreads / (kFinishCols / 2);  // segment slices per output pair
 
 static_assert(kMaxSeg % 64 == 0 && kMaxSeg / 4 <= kThreads, "segment scan: one dword per thread");
 static_assert((kMaxSeg + kGroups - 1) / kGroups <= 127, "16-bit accumulator fields");
+static_assert(kCols == kThreads, "one output per thread in the row-group sum");
 
-__global__ __launch_bounds__(kThreads) void k_gather_a8(
-    const int8_t* __restrict__ codes, const float* __restrict__ sx, int64_t K,
-    const uint8_t* __restrict__ Wk, const float* __restrict__ beta, int64_t N, int seg, int nseg,
-    int chunks, float* __restrict__ y, int32_t* __restrict__ acc_dbg, int32_t* __restrict__ acc_ws,
-    uint32_t* __restrict__ cnt_ws) {
+__global__ __launch_bounds__(kThreads) void k_gather_a8(const int8_t* __restrict__ codes, int64_t M, int64_t K,
+                                                         const uint8_t* __restrict__ Wk, int64_t N, int seg,
+                                                         int chunks, int32_t* __restrict__ part) {
   __shared__ int2 s_row[kMaxSeg];  // (byte offset of the row, code)
   __shared__ int32_t s_red[kGroups][kCols];
-  __shared__ uint32_t s_count;
-  __shared__ uint32_t s_last;
+  __shared__ int s_wtot[kThreads / 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int64_t m = blockIdx.y;
   const int chunk = static_cast<int>(blockIdx.x % chunks);
-  const int64_t k0 = static_cast<int64_t>(blockIdx.x / chunks) * seg;
+  const int sgi = static_cast<int>(blockIdx.x / chunks);
+  const int64_t k0 = static_cast<int64_t>(sgi) * seg;
   const int64_t k1 = (k0 + seg < K) ? k0 + seg : K;
   const uint32_t row_bytes = static_cast<uint32_t>(N >> 2);
 
-  if (tid == 0) s_count = 0;
-  __syncthreads();
-
-  // 1. list the nonzero codes of [k0, k1): four per thread
+  // 1. list the nonzero codes of [k0, k1), four per thread: wave ballots give
+  //    each code its slot inside the wave, wave totals the wave's base.
   const int nq = static_cast<int>((k1 - k0) >> 2);
   const int word = (tid < nq) ? *reinterpret_cast<const int*>(codes + m * K + k0 + 4 * tid) : 0;
+  uint64_t bal[4];
+  int wsum = 0;
+  int before[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    bal[j] = __ballot(static_cast<int8_t>(word >> (8 * j)) != 0);
+    before[j] = wsum;
+    wsum += __popcll(bal[j]);
+  }
+  if (lane == 0) s_wtot[wave] = wsum;
+  __syncthreads();
+  int base = 0, R = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) {
+    const int t = s_wtot[w];
+    base += (w < wave) ? t : 0;
+    R += t;
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int q = static_cast<int>(static_cast<int8_t>(word >> (8 * j)));
-    const bool nz = q != 0;
-    const uint64_t bal = __ballot(nz);
-    uint32_t base = 0;
-    if (lane == 0 && bal != 0) base = atomicAdd(&s_count, static_cast<uint32_t>(__popcll(bal)));
-    base = __shfl(base, 0);
-    if (nz) {
-      const uint32_t below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
-                                                       __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0u));
+    if (q != 0) {
+      const int below = static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+          static_cast<uint32_t>(bal[j] >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal[j]), 0u)));
       const uint32_t k = static_cast<uint32_t>(k0 + 4 * tid + j);
-      s_row[base + below] = make_int2(static_cast<int>(k * row_bytes), q);
+      s_row[base + before[j] + below] = make_int2(static_cast<int>(k * row_bytes), q);
     }
   }
   __syncthreads();
-  const int R = static_cast<int>(s_count);
 
-  // 2. gather: row group g = half-wave, lane c of the group owns 16 outputs
-  // Loads are unconditional so that all of a batch is in flight at once: a
-  // slot past the list end re-reads listed row 0 with q = 0, and a lane past
-  // the last output reads the chunk's first word (its sums are never stored).
+  // 2. gather: row group g = half-wave, lane c of the group owns 16 outputs.
+  // Loads are unconditional so that a whole batch is in flight at once: a slot
+  // past the list end re-reads listed row 0 with q = 0, and a lane past the
+  // last output reads the chunk's first word (its sums are never stored).
   const int g = tid >> 5;
   const int c = tid & 31;
   const bool col_ok = static_cast<int64_t>(chunk) * kCols + 16 * c < N;
@@ -127,42 +139,60 @@ __global__ __launch_bounds__(kThreads) void k_gather_a8(
 #pragma unroll
   for (int v = 0; v < 4; ++v) dst[v] = make_int4(sums[4 * v], sums[4 * v + 1], sums[4 * v + 2], sums[4 * v + 3]);
   __syncthreads();
-  const int col = 2 * tid;
-  int s0 = 0, s1 = 0;
+  int total = 0;
 #pragma unroll
-  for (int gg = 0; gg < kGroups; ++gg) {
-    const int2 v = *reinterpret_cast<const int2*>(&s_red[gg][col]);
-    s0 += v.x;
-    s1 += v.y;
-  }
-  const int64_t n = static_cast<int64_t>(chunk) * kCols + col;
-  const bool out_ok = n < N;  // N % 16 == 0: n + 1 < N too
-  int32_t* __restrict__ acc_row = acc_ws + m * N;
-  if (R > 0 && out_ok) {
-    atomicAdd(&acc_row[n], s0);
-    atomicAdd(&acc_row[n + 1], s1);
-  }
+  for (int gg = 0; gg < kGroups; ++gg) total += s_red[gg][tid];
+  const int64_t n = static_cast<int64_t>(chunk) * kCols + tid;
+  if (n < N) part[(static_cast<int64_t>(sgi) * M + m) * N + n] = total;
+}
 
-  // 4. the last workgroup of this (token, chunk) finishes the outputs
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t last = static_cast<uint32_t>(nseg - 1);
-    s_last = (atomicInc(&cnt_ws[m * chunks + chunk], last) == last) ? 1u : 0u;
+// Sum the segments' partials of 64 outputs of one token and apply the
+// epilogue.  Thread (r, p) adds output pair p of every eighth segment starting
+// at r, so each thread's loads (at most eight per pass) are all in flight at
+// once; the eight slices are then summed in LDS.
+__global__ __launch_bounds__(kFinishThreads) void k_gather_finish(const int32_t* __restrict__ part, int nseg,
+                                                                  const float* __restrict__ sx, int64_t M,
+                                                                  const float* __restrict__ beta, int64_t N,
+                                                                  float* __restrict__ y,
+                                                                  int32_t* __restrict__ acc_dbg) {
+  __shared__ int2 s_sum[kFinishSlices][kFinishCols / 2];
+  const int tid = threadIdx.x;
+  const int pi = tid & (kFinishCols / 2 - 1);
+  const int r = tid / (kFinishCols / 2);
+  const int64_t m = blockIdx.y;
+  const int64_t n = static_cast<int64_t>(blockIdx.x) * kFinishCols + 2 * pi;
+  const bool ok = n < N;  // N % 16 == 0: n + 1 < N too
+  const int32_t* __restrict__ src = part + m * N + (ok ? n : 0);
+  const int64_t stride = M * N;
+  int a0 = 0, a1 = 0;
+  for (int s0 = r; s0 < nseg; s0 += kFinishSlices * 8) {
+    int2 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int sg = s0 + u * kFinishSlices;
+      v[u] = (sg < nseg) ? *reinterpret_cast<const int2*>(src + sg * stride) : make_int2(0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      a0 += v[u].x;
+      a1 += v[u].y;
+    }
   }
+  s_sum[r][pi] = make_int2(a0, a1);
   __syncthreads();
-  if (s_last == 0) return;
-  __threadfence();
-  if (out_ok) {
-    const int a0 = atomicExch(&acc_row[n], 0);
-    const int a1 = atomicExch(&acc_row[n + 1], 0);
-    const float s = sx[m];
-    float2 out;
-    out.x = __fmul_rn(__fmul_rn(static_cast<float>(a0), s), beta[n]);
-    out.y = __fmul_rn(__fmul_rn(static_cast<float>(a1), s), beta[n + 1]);
-    *reinterpret_cast<float2*>(y + m * N + n) = out;
-    if (acc_dbg) *reinterpret_cast<int2*>(acc_dbg + m * N + n) = make_int2(a0, a1);
+  if (r != 0 || !ok) return;
+#pragma unroll
+  for (int q = 1; q < kFinishSlices; ++q) {
+    const int2 v = s_sum[q][pi];
+    a0 += v.x;
+    a1 += v.y;
   }
+  const float s = sx[m];
+  float2 out;
+  out.x = __fmul_rn(__fmul_rn(static_cast<float>(a0), s), beta[n]);
+  out.y = __fmul_rn(__fmul_rn(static_cast<float>(a1), s), beta[n + 1]);
+  *reinterpret_cast<float2*>(y + m * N + n) = out;
+  if (acc_dbg) *reinterpret_cast<int2*>(acc_dbg + m * N + n) = make_int2(a0, a1);
 }
 
 struct GatherGrid {
@@ -185,20 +215,21 @@ GatherGrid gather_grid(int64_t M, int64_t K, int64_t N) {
 
 }  // namespace
 
-size_t gather_a8_workspace_bytes(int64_t M, int64_t N) {
-  const int64_t chunks = (N + kCols - 1) / kCols;
-  const size_t bytes = static_cast<size_t>(M) * static_cast<size_t>(N) * 4 + static_cast<size_t>(M * chunks) * 4;
+size_t gather_a8_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+  const GatherGrid gg = gather_grid(M, K, N);
+  const size_t bytes = static_cast<size_t>(gg.nseg) * static_cast<size_t>(M) * static_cast<size_t>(N) * 4;
   return (bytes + 255) & ~static_cast<size_t>(255);
 }
 
 hipError_t launch_gather_a8(const int8_t* codes, const float* sx, int64_t M, int64_t K, const uint8_t* w_kmajor,
                             const float* beta, int64_t N, float* y, int32_t* acc_dbg, void* ws, hipStream_t s) {
   const GatherGrid gg = gather_grid(M, K, N);
-  int32_t* acc_ws = static_cast<int32_t*>(ws);
-  uint32_t* cnt_ws = reinterpret_cast<uint32_t*>(acc_ws + M * N);
+  int32_t* part = static_cast<int32_t*>(ws);
   hipLaunchKernelGGL(k_gather_a8, dim3(static_cast<unsigned>(gg.nseg * gg.chunks), static_cast<unsigned>(M)),
-                     dim3(kThreads), 0, s, codes, sx, K, w_kmajor, beta, N, gg.seg, gg.nseg, gg.chunks, y, acc_dbg,
-                     acc_ws, cnt_ws);
+                     dim3(kThreads), 0, s, codes, M, K, w_kmajor, N, gg.seg, gg.chunks, part);
+  const unsigned fblocks = static_cast<unsigned>((N + kFinishCols - 1) / kFinishCols);
+  hipLaunchKernelGGL(k_gather_finish, dim3(fblocks, static_cast<unsigned>(M)), dim3(kFinishThreads), 0, s, part,
+                     gg.nseg, sx, M, beta, N, y, acc_dbg);
   return hipGetLastError();
 }
 

@@ -71,13 +71,15 @@ def test_bitlinear_validation():
 
 
 def test_gather_validation():
-    ws = bw.bw_bitlinear_sparse_a8_gather_workspace_bytes(1, 4096)
-    assert ws >= 4 * 4096 + 4 * 8 and ws % 256 == 0
-    assert bw.bw_bitlinear_sparse_a8_gather_workspace_bytes(0, 4096) == 0
+    ws = bw.bw_bitlinear_sparse_a8_gather_workspace_bytes(1, 11008, 4096)
+    assert ws >= 4 * 4096 and ws % 256 == 0
+    assert bw.bw_bitlinear_sparse_a8_gather_workspace_bytes(0, 11008, 4096) == 0
+    assert bw.bw_bitlinear_sparse_a8_gather_workspace_bytes(17, 11008, 4096) == 0
+    assert bw.bw_bitlinear_sparse_a8_gather_workspace_bytes(1, 100, 4096) == 0
     g = lib.bw_bitlinear_sparse_a8_gather
     assert g(A, A, 1, 11008, A, A, 4095, A, None, A, ws, None) == 2  # N % 16
     assert g(A, A, 1, 11000, A, A, 4096, A, None, A, ws, None) == 2  # K % 64
-    assert g(A, A, 70000, 4096, A, A, 4096, A, None, A, 1 << 40, None) == 2  # M
+    assert g(A, A, 17, 4096, A, A, 4096, A, None, A, 1 << 40, None) == 2  # M
     assert g(A, A, 1, 131072, A, A, 1 << 17, A, None, A, 1 << 40, None) == 2  # weights above 2^31 bytes
     assert g(A, A, 1, 11008, A, A, 4096, A, None, None, ws, None) == 1  # workspace
     assert g(A, A, 1, 11008, A, A, 4096, A, None, MIS, ws, None) == 3
