@@ -11,6 +11,9 @@ that are resident in HBM before timing starts:
   decode, M = 1, 2, 4, 8 tokens:     INT4 quantizer -> W1.58A4 GEMV over 32 layers of fused q/k/v
                                      (N=12288) and gate/up (N=22016) weights (1.12 GB, > 4x the
                                      256 MB Infinity Cache, so weights stream from HBM)
+  decode down_proj / out_proj, M = 1: W1.58A8 GEMV on the tiled weights vs the gather product on
+                                     K-major weights (reads only the rows of nonzero codes),
+                                     32 layers each
   KV cache, one layer (8x4096x32x128): 3-bit pack of K and V, unpack of both to bf16
   weights:                           absmean ternary pack of one 4096x4096 fp32 tensor
 
@@ -31,7 +34,8 @@ bracketed rows a1 + a4 (each of which also pays its own launch latency).
 `b158_baseline` runs the same two projections on BitNet b1.58's activation
 path (INT8 absmax of every entry, no top-k, W1.58A8 GEMMs; row b0) and gives
 the ratio of the two.  `decode_gbs` is the decode GEMV rate in algorithmic
-bytes; `roofline` covers the N=11008 prefill GEMM.
+bytes; `gather_decode_m1` sets the single-token gather product beside the
+tiled GEMV; `roofline` covers the N=11008 prefill GEMM.
 """
 from __future__ import annotations
 
@@ -141,9 +145,11 @@ class Bench:
         del g, u
         self.w_down = f32(synth.weight_tensor(S + 14, HIDDEN, FFN))
         self.wp_down, self.b_down = bw.bw_pack_ternary(self.w_down, bw.BW_ROLE_A8)
+        wk_down, _ = bw.bw_pack_ternary(self.w_down, bw.BW_ROLE_A8_KMAJOR)  # single-token gather layout
         del self.w_down
         self.x_out = bf16(synth.heavy_tailed(S + 13, M_PREFILL, HIDDEN))
         self.wp_o, self.b_o = bw.bw_pack_ternary(w_q, bw.BW_ROLE_A8)
+        wk_o, _ = bw.bw_pack_ternary(w_q, bw.BW_ROLE_A8_KMAJOR)
         self.c8_down = t.empty((M_PREFILL, FFN), dtype=t.int8, device=dev)
         self.s8_down = t.empty(M_PREFILL, dtype=t.float32, device=dev)
         self.c8_out = t.empty((M_PREFILL, HIDDEN), dtype=t.int8, device=dev)
@@ -177,6 +183,25 @@ class Bench:
                 ya=t.empty((M, self.n_qkv), dtype=t.float32, device=dev),
                 yf=t.empty((M, self.n_gu), dtype=t.float32, device=dev),
             )
+        # ---------------- decode down_proj / out_proj, one token: sparsified INT8 codes
+        # and 32 layers of weights in both the tiled and the K-major layout
+        gd, ud = synth.gate_up(S + 31, 1, FFN)
+        x1 = bf16(synth.heavy_tailed(S + 32, 1, HIDDEN))
+        self.one = {}
+        for name, K1, N1, tiled, kmaj, beta in (("down", FFN, HIDDEN, self.wp_down, wk_down, self.b_down),
+                                                ("outproj", HIDDEN, HIDDEN, self.wp_o, wk_o, self.b_o)):
+            c = t.empty((1, K1), dtype=t.int8, device=dev)
+            sc = t.empty(1, dtype=t.float32, device=dev)
+            if name == "down":
+                bw.bw_quantize_sparse_a8(bf16(gd), bf16(ud), K1 // 2, c, sc)
+            else:
+                bw.bw_quantize_sparse_a8(x1, None, K1 // 2, c, sc)
+            self.one[name] = dict(
+                K=K1, N=N1, codes=c, scales=sc, beta=beta, nnz=int((c != 0).sum().item()),
+                layers=[(tiled.clone(), kmaj.clone()) for _ in range(LAYERS)],
+                ws=t.empty(bw.bw_bitlinear_sparse_a8_gather_workspace_bytes(1, K1, N1), dtype=t.uint8, device=dev),
+                yt=t.empty((1, N1), dtype=t.float32, device=dev), yg=t.empty((1, N1), dtype=t.float32, device=dev))
+        del gd, ud, wk_down, wk_o
         # ---------------- KV cache, one layer
         B_, S_, H_, D_ = KV_SHAPE
         self.kv = [bf16(synth.kv_tensor(S + 5 + i, *KV_SHAPE)) for i in range(2)]
@@ -271,6 +296,20 @@ class Bench:
             R.append((f"a5_gemv_gateup_m{Md}", "GB/s", gemv_bytes(Md, self.n_gu, K),
                       [lambda d=d, gp=gp, gb=gb: bw.bw_bitlinear_a4(d["cf"], d["sf"], bw.BW_ACT_INT4, gp, gb, d["yf"])
                        for _, _, gp, gb in self.layers]))
+        for name, o in self.one.items():
+            K1, N1 = o["K"], o["N"]
+            # tiled W1.58A8 GEMV: every weight byte; gather: only the rows of nonzero codes.
+            # Each row starts behind an untimed cache fill: the gather's rows of all 32 layers
+            # (~108 MB for down_proj) would otherwise stay in the 256 MB Infinity Cache.
+            R.append((f"_evict_cache_{name}_t", None, 0, [lambda: self.evict.fill_(3.0)]))
+            R.append((f"a9_gemv_a8_{name}_m1", "GB/s", N1 * K1 / 4 + 4 * N1 + K1 + 4 + 4 * N1,
+                      [lambda o=o, wt=wt: bw.bw_bitlinear_sparse_a8(o["codes"], o["scales"], wt, o["beta"], o["yt"])
+                       for wt, _ in o["layers"]]))
+            R.append((f"_evict_cache_{name}_g", None, 0, [lambda: self.evict.fill_(4.0)]))
+            R.append((f"k10_gather_a8_{name}_m1", "GB/s", o["nnz"] * N1 / 4 + 4 * N1 + K1 + 4 + 4 * N1,
+                      [lambda o=o, wk=wk: bw.bw_bitlinear_sparse_a8_gather(o["codes"], o["scales"], wk, o["beta"],
+                                                                           o["ws"], o["yg"])
+                       for _, wk in o["layers"]]))
         B_, S_, H_, D_ = KV_SHAPE
         nvec = B_ * S_ * H_
         pack_bytes = nvec * D_ * 2 + nvec * (3 * D_ // 8) + 4 * nvec + 4 * B_ * S_ + self.n_special * H_ * (D_ // 2 + 4)
@@ -468,6 +507,15 @@ def main():
     if gemv:
         dec_bytes = sum(table[n]["amount_per_launch"] * table[n]["launches_per_step"] for n in gemv)
         decode_gbs = dec_bytes / (row_ms(gemv) * 1e-3) / 1e9
+    gather = {}
+    for name, o in b.one.items():
+        rt, rg = f"a9_gemv_a8_{name}_m1", f"k10_gather_a8_{name}_m1"
+        if rt in table and rg in table:
+            gather[name] = {
+                "K": o["K"], "N": o["N"], "nonzero_codes": o["nnz"],
+                "weight_bytes_read_frac": round(o["nnz"] / o["K"], 4),
+                "tiled_us": table[rt]["avg_us"], "gather_us": table[rg]["avg_us"],
+                "tiled_over_gather_time": round(table[rt]["avg_us"] / table[rg]["avg_us"], 3)}
     roof = None
     if "a4_gemm_int4_n11008" in table:
         dom = table["a4_gemm_int4_n11008"]
@@ -504,6 +552,7 @@ def main():
             "value": b158, "unit": "TOPS",
             "basis": "same ops / time of INT8 absmax (all entries, no top-k) + both W1.58A8 GEMMs, back to back (row b0)",
             "a48_over_b158": None if value is None else round(value / b158, 3)},
+        "gather_decode_m1": gather or None,
         "decode_gbs": None if decode_gbs is None else round(decode_gbs, 1),
         "decode_frac_hbm": None if decode_gbs is None else round(decode_gbs / HBM_PEAK_GBS, 4),
         "roofline": roof,

@@ -121,3 +121,15 @@ def test_workspace_reuse_across_shapes():
         q, s = half_sparse_codes(50 + i, M, K)
         w = synth.weight_tensor(synth.SEED_BASE + 50 + i, N, K)
         check(q, s, w, f"reuse {i}", ws=ws[:need])
+
+
+def test_long_k_and_repeat():
+    """K twice the sparsifier's row limit (32768: 128 segments of 256 inputs at M = 2,
+    N = 96) and a second call on the same buffers: the two results must be identical."""
+    M, K, N = 2, 32768, 96
+    q, s = half_sparse_codes(61, M, K, keep=0.9)
+    w = synth.weight_tensor(synth.SEED_BASE + 61, N, K)
+    ws = workspace(M, K, N, 0x33)
+    y1 = check(q, s, w, "long K", ws=ws)
+    y2 = check(q, s, w, "long K repeat", ws=ws)
+    assert torch.equal(y1, y2)
