@@ -6,13 +6,15 @@
 // the whole cost, so the kernel is shaped for HBM streaming:
 //   * one workgroup per 16 output channels (one packed tile column); its
 //     K/64 tiles are one contiguous run of K*4 bytes;
-//   * the four waves split the tiles; a wave's lane group g (16 lanes) reads
-//     tile base+g, so one wave load moves 1 KB of contiguous weights, 16 B per
-//     lane, and all of a wave's loads are issued before any is consumed;
+//   * the waves split the tiles; a wave's lane group g (16 lanes) reads tile
+//     base+g, so one wave load moves 1 KB of contiguous weights, 16 B per lane,
+//     and all of a wave's loads are issued before any is consumed.  A grid of
+//     few workgroups with a long K (N = 4096, K = 11008) takes 8 waves per
+//     workgroup so that each wave's share of K is two rounds of loads;
 //   * the tokens (M <= 16, zero-padded) are the rows of 16x16 MFMAs
 //     (i8 16x16x64, or scaled f8f6f4 16x16x128 for e2m1); activations are read
 //     straight from L2-resident global memory;
-//   * the four partial int32/fp32 tiles are summed through LDS (exact) and
+//   * the waves' partial int32/fp32 tiles are summed through LDS (exact) and
 //     the epilogue writes y for the M real rows.
 #include "bw_internal.h"
 #include "bw_widen.h"
@@ -20,17 +22,16 @@
 namespace bw {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kUnroll = 4;  // tile groups in flight per lane
 
-template <int MODE>
-__global__ __launch_bounds__(kThreads) void k_gemv(const uint8_t* __restrict__ A,
+template <int MODE, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_gemv(const uint8_t* __restrict__ A,
                                                    const float* __restrict__ sx, int M, int64_t K,
                                                    const uint8_t* __restrict__ Wp,
                                                    const float* __restrict__ beta, int64_t N,
                                                    float* __restrict__ y, void* __restrict__ acc_dbg) {
   using acc_t = typename std::conditional<MODE == MODE_FP4, v4f, v4i>::type;
-  __shared__ acc_t part[4][64];
+  __shared__ acc_t part[WAVES][64];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -43,7 +44,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(const uint8_t* __restrict__ A
   const bool row_ok = li < M;
 
   // wave w handles tiles [t0, t1)
-  const int64_t per = (T + 3) >> 2;
+  const int64_t per = (T + WAVES - 1) / WAVES;
   const int64_t t0 = wave * per;
   const int64_t t1 = (t0 + per < T) ? t0 + per : T;
 
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(const uint8_t* __restrict__ A
   if (wave != 0) return;
   acc_t s = part[0][lane];
 #pragma unroll
-  for (int w = 1; w < 4; ++w) {
+  for (int w = 1; w < WAVES; ++w) {
     const acc_t p = part[w][lane];
     s[0] += p[0]; s[1] += p[1]; s[2] += p[2]; s[3] += p[3];
   }
@@ -132,23 +133,45 @@ __global__ __launch_bounds__(kThreads) void k_gemv(const uint8_t* __restrict__ A
   }
 }
 
+template <int MODE>
+void launch_waves(int waves, const uint8_t* A, const float* sx, int m, int64_t K, const uint8_t* w,
+                  const float* beta, int64_t N, float* y, void* acc_dbg, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(N / 16));
+  if (waves == 8) {
+    hipLaunchKernelGGL((k_gemv<MODE, 8>), grid, dim3(512), 0, s, A, sx, m, K, w, beta, N, y, acc_dbg);
+  } else {
+    hipLaunchKernelGGL((k_gemv<MODE, 4>), grid, dim3(256), 0, s, A, sx, m, K, w, beta, N, y, acc_dbg);
+  }
+}
+
+// Waves per workgroup.  Measured at M = 1 over 32 layers: 8 waves help only
+// where the grid is small and K long (down_proj, N = 4096, K = 11008:
+// 8.3 -> 7.3 us); at K = 4096 (q/k/v, out_proj) and at N = 22016 (gate/up)
+// 4-wave workgroups, several per CU, are faster, and 16 waves are slower
+// everywhere.
+int gemv_waves(int64_t K, int64_t N) {
+  const int64_t T = K >> 6;
+  const int64_t blocks = N / 16;
+  return (blocks <= 512 && T >= 128) ? 8 : 4;
+}
+
 }  // namespace
 
 hipError_t launch_gemv(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
                        const uint8_t* w_packed, const float* beta, int64_t N, float* y, void* acc_dbg,
                        hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(N / 16)), block(kThreads);
   const uint8_t* A = static_cast<const uint8_t*>(codes);
   const int m = static_cast<int>(M);
+  const int waves = gemv_waves(K, N);
   switch (mode) {
     case MODE_INT4:
-      hipLaunchKernelGGL(k_gemv<MODE_INT4>, grid, block, 0, s, A, sx, m, K, w_packed, beta, N, y, acc_dbg);
+      launch_waves<MODE_INT4>(waves, A, sx, m, K, w_packed, beta, N, y, acc_dbg, s);
       break;
     case MODE_FP4:
-      hipLaunchKernelGGL(k_gemv<MODE_FP4>, grid, block, 0, s, A, sx, m, K, w_packed, beta, N, y, acc_dbg);
+      launch_waves<MODE_FP4>(waves, A, sx, m, K, w_packed, beta, N, y, acc_dbg, s);
       break;
     default:
-      hipLaunchKernelGGL(k_gemv<MODE_INT8>, grid, block, 0, s, A, sx, m, K, w_packed, beta, N, y, acc_dbg);
+      launch_waves<MODE_INT8>(waves, A, sx, m, K, w_packed, beta, N, y, acc_dbg, s);
       break;
   }
   return hipGetLastError();
