@@ -241,6 +241,29 @@ bw_status bw_kv_unpack3(const uint8_t* p3, const float* s3, const uint8_t* p4, c
                         const int32_t* slot_of, int64_t B, int64_t S, int64_t H, int64_t D,
                         int64_t n_special, bw_dtype out_dtype, void* out, void* stream);
 
+/* ------------------------------------------------------------------------ *
+ * Single-token attention over the 3-bit KV cache.
+ * Source: BitNet a4.8 abstract (3-bit KV cache); toshoseti review,
+ * «Эксперименты» (bos/eos kept at 4 bits); 9pt.com article, methodology (the
+ * 3-bit cache as part of faster, leaner inference).  The pages give no
+ * attention formula; this is standard scaled dot-product attention of one
+ * query per (batch, head) over all S cached positions:
+ *   k_s, v_s = dequantized vectors as bw_kv_unpack3 defines them (code *
+ *              scale; the 4-bit side-slab codes where 0 <= slot_of[b][s] <
+ *              n_special);
+ *   z_s = (q . k_s) / sqrt(D);  p = softmax_s(z);  out = sum_s p_s v_s.
+ * fp32 arithmetic throughout (dot products, exp, sums), so results differ
+ * from an exact evaluation by rounding only.
+ * q: fp32 [B][H][D].  K and V: p3/s3/p4/s4 slabs as written by bw_kv_pack3
+ * for each tensor with the same slot_of.  out: fp32 [B][H][D].
+ * Shapes: D = 64 or 128, 1 <= S <= 16384, H >= 1.  k_p4/k_s4/v_p4/v_s4 may be
+ * NULL when n_special == 0.
+ * ------------------------------------------------------------------------ */
+bw_status bw_attn_decode_kv3(const float* q, const uint8_t* k_p3, const float* k_s3, const uint8_t* k_p4,
+                             const float* k_s4, const uint8_t* v_p3, const float* v_s3, const uint8_t* v_p4,
+                             const float* v_s4, const int32_t* slot_of, int64_t n_special, int64_t B,
+                             int64_t S, int64_t H, int64_t D, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,6 +19,7 @@ __all__ = [
     "BwError", "lib_path", "bw_abi_version", "bw_pack_layout_version", "bw_last_error",
     "bw_ternary_packed_bytes", "bw_pack_ternary_workspace_bytes", "bw_pack_ternary", "bw_quantize",
     "bw_bitlinear_a4", "bw_quantize_sparse_a8", "bw_bitlinear_sparse_a8", "bw_kv_pack3", "bw_kv_unpack3",
+    "bw_attn_decode_kv3",
 ]
 
 BW_OK = 0
@@ -61,6 +62,7 @@ def _load() -> ctypes.CDLL:
         "bw_bitlinear_sparse_a8_gather": ([P, P, I64, I64, P, P, I64, P, P, P, SZ, P], I),
         "bw_kv_pack3": ([P, I, I64, I64, I64, I64, P, I64, P, P, P, P, P], I),
         "bw_kv_unpack3": ([P, P, P, P, P, I64, I64, I64, I64, I64, I, P, P], I),
+        "bw_attn_decode_kv3": ([P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P, P], I),
     }
     for name, (argt, rest) in sig.items():
         fn = getattr(lib, name)
@@ -268,4 +270,26 @@ def bw_kv_unpack3(p3: torch.Tensor, s3: torch.Tensor, p4: torch.Tensor, s4: torc
         _dev(p4, "p4", (torch.uint8,)), _dev(s4, "s4", (torch.float32,)),
         _dev(slot_of, "slot_of", (torch.int32,), (B, S)), B, S, H, D, n_special, _fdtype(out),
         _dev(out, "out", _FLOATS, (B, S, H, D)), _stream(p3)))
+    return out
+
+
+def bw_attn_decode_kv3(q: torch.Tensor, k_pack, v_pack, slot_of: torch.Tensor, n_special: int, out=None):
+    """Single-token attention over the 3-bit KV cache.  q fp32 [B][H][D]; k_pack / v_pack =
+    (p3, s3, p4, s4) as returned by bw_kv_pack3 with this slot_of; returns out fp32 [B][H][D]."""
+    B, H, D = q.shape
+    kp3, ks3, kp4, ks4 = k_pack
+    vp3, vs3, vp4, vs4 = v_pack
+    S = kp3.shape[1]
+    if out is None:
+        out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
+    shp3, shs = (B, S, H, 3 * D // 8), (B, S, H)
+    shp4, shs4 = (n_special, H, D // 2), (n_special, H)
+    _check(_lib.bw_attn_decode_kv3(
+        _dev(q, "q", (torch.float32,)),
+        _dev(kp3, "k_p3", (torch.uint8,), shp3), _dev(ks3, "k_s3", (torch.float32,), shs),
+        _opt(kp4, "k_p4", (torch.uint8,), shp4), _opt(ks4, "k_s4", (torch.float32,), shs4),
+        _dev(vp3, "v_p3", (torch.uint8,), shp3), _dev(vs3, "v_s3", (torch.float32,), shs),
+        _opt(vp4, "v_p4", (torch.uint8,), shp4), _opt(vs4, "v_s4", (torch.float32,), shs4),
+        _dev(slot_of, "slot_of", (torch.int32,), (B, S)), n_special, B, S, H, D,
+        _dev(out, "out", (torch.float32,), (B, H, D)), _stream(q)))
     return out

@@ -214,4 +214,28 @@ bw_status bw_kv_unpack3(const uint8_t* p3, const float* s3, const uint8_t* p4, c
                     "bw_kv_unpack3");
 }
 
+bw_status bw_attn_decode_kv3(const float* q, const uint8_t* k_p3, const float* k_s3, const uint8_t* k_p4,
+                             const float* k_s4, const uint8_t* v_p3, const float* v_s3, const uint8_t* v_p4,
+                             const float* v_s4, const int32_t* slot_of, int64_t n_special, int64_t B, int64_t S,
+                             int64_t H, int64_t D, float* out, void* stream) {
+  BW_REQUIRE(B >= 0 && H >= 1 && n_special >= 0 && S >= 1 && S <= bw::kAttnMaxS, BW_ERR_SHAPE,
+             "bw_attn_decode_kv3: need B >= 0, H >= 1, 1 <= S <= %lld, n_special >= 0 (B=%lld S=%lld H=%lld)",
+             (long long)bw::kAttnMaxS, (long long)B, (long long)S, (long long)H);
+  BW_REQUIRE(D == 64 || D == 128, BW_ERR_SHAPE, "bw_attn_decode_kv3: head_dim must be 64 or 128 (D=%lld)",
+             (long long)D);
+  BW_REQUIRE(B <= (int64_t(1) << 40) / S / H / D && B * H <= (int64_t(1) << 31) - 1, BW_ERR_SHAPE,
+             "bw_attn_decode_kv3: tensor too large");
+  if (B == 0) return ok();
+  BW_REQUIRE(q && k_p3 && k_s3 && v_p3 && v_s3 && slot_of && out, BW_ERR_NULL, "bw_attn_decode_kv3: NULL pointer");
+  BW_REQUIRE(n_special == 0 || (k_p4 && k_s4 && v_p4 && v_s4), BW_ERR_NULL,
+             "bw_attn_decode_kv3: 4-bit slabs required when n_special > 0");
+  BW_REQUIRE(!misaligned(q) && !misaligned(k_p3) && !misaligned(k_s3) && !misaligned(k_p4) && !misaligned(k_s4) &&
+                 !misaligned(v_p3) && !misaligned(v_s3) && !misaligned(v_p4) && !misaligned(v_s4) &&
+                 !misaligned(slot_of) && !misaligned(out),
+             BW_ERR_ALIGN, "bw_attn_decode_kv3: device pointers must be 16-byte aligned");
+  return hip_status(bw::launch_attn_decode3(q, k_p3, k_s3, k_p4, k_s4, v_p3, v_s3, v_p4, v_s4, slot_of, n_special, B,
+                                            S, H, D, out, static_cast<hipStream_t>(stream)),
+                    "bw_attn_decode_kv3");
+}
+
 }  // extern "C"

@@ -48,6 +48,13 @@ hipError_t launch_sparse_a8(const void* g, const void* u, bool bf16, int64_t M, 
                             int64_t k_keep, int8_t* codes, float* scales, uint32_t* mask,
                             hipStream_t s);
 
+// Single-token attention over the 3-bit KV cache (one workgroup per batch x head).
+constexpr int64_t kAttnMaxS = 16384;
+hipError_t launch_attn_decode3(const float* q, const uint8_t* kp3, const float* ks3, const uint8_t* kp4,
+                               const float* ks4, const uint8_t* vp3, const float* vs3, const uint8_t* vp4,
+                               const float* vs4, const int32_t* slot_of, int64_t n_special, int64_t B, int64_t S,
+                               int64_t H, int64_t D, float* out, hipStream_t s);
+
 hipError_t launch_kv_pack3(const void* kv, bool bf16, int64_t B, int64_t S, int64_t H, int64_t D,
                            const int32_t* slot_of, int64_t n_special, uint8_t* p3, float* s3,
                            uint8_t* p4, float* s4, hipStream_t s);

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -115,3 +115,15 @@ def test_kv_validation():
     g = lib.bw_kv_unpack3
     assert g(A, A, A, A, A, 8, 16, 4, 128, 2, 5, A, None) == 4
     assert g(A, A, A, A, A, 8, 16, 0, 128, 2, 1, A, None) == 2  # H = 0
+
+
+def test_attn_validation():
+    f = lib.bw_attn_decode_kv3
+    args = lambda B, S, H, D, n=0, q=A, k4=None, out=A: (q, A, A, k4, k4, A, A, k4, k4, A, n, B, S, H, D, out, None)
+    assert f(*args(8, 4096, 32, 96)) == 2  # head_dim
+    assert f(*args(8, 0, 32, 128)) == 2  # S
+    assert f(*args(8, 16385, 32, 128)) == 2  # S above the LDS-resident limit
+    assert f(*args(8, 4096, 32, 128, n=3)) == 1  # side slabs missing
+    assert f(*args(8, 4096, 32, 128, q=None)) == 1
+    assert f(*args(8, 4096, 32, 128, out=MIS)) == 3
+    assert f(*args(0, 4096, 32, 128, q=None, out=None)) == 0  # empty batch
