@@ -14,7 +14,8 @@ that are resident in HBM before timing starts:
   decode down_proj / out_proj, M = 1: W1.58A8 GEMV on the tiled weights vs the gather product on
                                      K-major weights (reads only the rows of nonzero codes),
                                      32 layers each
-  KV cache, one layer (8x4096x32x128): 3-bit pack of K and V, unpack of both to bf16
+  KV cache, one layer (8x4096x32x128): 3-bit pack of K and V, unpack of both to bf16,
+                                     single-token attention over the packed K and V
   weights:                           absmean ternary pack of one 4096x4096 fp32 tensor
 
 Each decode row's 32-64 launches are recorded once into a HIP graph; the other
@@ -216,6 +217,9 @@ class Bench:
                 t.zeros((self.n_special, H_), dtype=t.float32, device=dev),
             ))
         self.kv_out = [t.empty(KV_SHAPE, dtype=t.bfloat16, device=dev) for _ in range(2)]
+        # single-token attention over that layer's packed K (kvp[0]) and V (kvp[1])
+        self.q_att = f32(synth.normal(S + 6, (B_, H_, D_)))
+        self.att_out = t.empty((B_, H_, D_), dtype=t.float32, device=dev)
         # ---------------- weight packing (offline row): one 4096x4096 fp32 tensor
         self.pk = t.empty(HIDDEN * HIDDEN // 4, dtype=t.uint8, device=dev)
         self.pk_b = t.empty(HIDDEN, dtype=t.float32, device=dev)
@@ -318,6 +322,14 @@ class Bench:
         R.append(("a10_kv_unpack3", "GB/s", pack_bytes,
                   [lambda i=i: bw.bw_kv_unpack3(*self.kvp[i], self.slot_of, self.n_special,
                                                 out_dtype=self.torch.bfloat16, out=self.kv_out[i]) for i in range(2)]))
+        # single-token attention over the packed cache: algorithmic bytes are the 3-bit
+        # planes and scales of K and V, slot ids, both side slabs, q and out
+        att_bytes = (2 * nvec * (3 * D_ // 8 + 4) + 4 * B_ * S_ + 2 * self.n_special * H_ * (D_ // 2 + 4)
+                     + 2 * 4 * B_ * H_ * D_)
+        R.append(("_evict_cache_attn", None, 0, [lambda: self.evict.fill_(5.0)]))
+        R.append(("k11_attn_decode_kv3", "GB/s", att_bytes,
+                  [lambda: bw.bw_attn_decode_kv3(self.q_att, self.kvp[0], self.kvp[1], self.slot_of, self.n_special,
+                                                 self.att_out)]))
         R.append(("a3_pack_ternary_4096x4096", "GB/s", HIDDEN * HIDDEN * 4 + HIDDEN * HIDDEN / 4 + 4 * HIDDEN,
                   [lambda: bw.bw_pack_ternary(self.w_q, bw.BW_ROLE_A4, self.pk, self.pk_b, self.pk_ws)]))
         return R

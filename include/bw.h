@@ -256,13 +256,18 @@ bw_status bw_kv_unpack3(const uint8_t* p3, const float* s3, const uint8_t* p4, c
  * from an exact evaluation by rounding only.
  * q: fp32 [B][H][D].  K and V: p3/s3/p4/s4 slabs as written by bw_kv_pack3
  * for each tensor with the same slot_of.  out: fp32 [B][H][D].
- * Shapes: D = 64 or 128, 1 <= S <= 16384, H >= 1.  k_p4/k_s4/v_p4/v_s4 may be
+ * workspace: device, >= bw_attn_decode_kv3_workspace_bytes(B, S, H, D) bytes
+ *   (per-chunk partial sums; about 2 MB for 8 x 4096 x 32 x 128); contents
+ *   on entry are ignored.  Calls sharing a workspace must be stream-ordered.
+ * Shapes: D = 64 or 128, S >= 1, 1 <= H <= 1024.  k_p4/k_s4/v_p4/v_s4 may be
  * NULL when n_special == 0.
  * ------------------------------------------------------------------------ */
+/* host */ size_t bw_attn_decode_kv3_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D);
 bw_status bw_attn_decode_kv3(const float* q, const uint8_t* k_p3, const float* k_s3, const uint8_t* k_p4,
                              const float* k_s4, const uint8_t* v_p3, const float* v_s3, const uint8_t* v_p4,
                              const float* v_s4, const int32_t* slot_of, int64_t n_special, int64_t B,
-                             int64_t S, int64_t H, int64_t D, float* out, void* stream);
+                             int64_t S, int64_t H, int64_t D, float* out, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -19,7 +19,7 @@ __all__ = [
     "BwError", "lib_path", "bw_abi_version", "bw_pack_layout_version", "bw_last_error",
     "bw_ternary_packed_bytes", "bw_pack_ternary_workspace_bytes", "bw_pack_ternary", "bw_quantize",
     "bw_bitlinear_a4", "bw_quantize_sparse_a8", "bw_bitlinear_sparse_a8", "bw_kv_pack3", "bw_kv_unpack3",
-    "bw_attn_decode_kv3",
+    "bw_attn_decode_kv3_workspace_bytes", "bw_attn_decode_kv3",
 ]
 
 BW_OK = 0
@@ -62,7 +62,8 @@ def _load() -> ctypes.CDLL:
         "bw_bitlinear_sparse_a8_gather": ([P, P, I64, I64, P, P, I64, P, P, P, SZ, P], I),
         "bw_kv_pack3": ([P, I, I64, I64, I64, I64, P, I64, P, P, P, P, P], I),
         "bw_kv_unpack3": ([P, P, P, P, P, I64, I64, I64, I64, I64, I, P, P], I),
-        "bw_attn_decode_kv3": ([P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P, P], I),
+        "bw_attn_decode_kv3_workspace_bytes": ([I64, I64, I64, I64], SZ),
+        "bw_attn_decode_kv3": ([P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P, P, SZ, P], I),
     }
     for name, (argt, rest) in sig.items():
         fn = getattr(lib, name)
@@ -273,7 +274,12 @@ def bw_kv_unpack3(p3: torch.Tensor, s3: torch.Tensor, p4: torch.Tensor, s4: torc
     return out
 
 
-def bw_attn_decode_kv3(q: torch.Tensor, k_pack, v_pack, slot_of: torch.Tensor, n_special: int, out=None):
+def bw_attn_decode_kv3_workspace_bytes(B: int, S: int, H: int, D: int) -> int:
+    return _lib.bw_attn_decode_kv3_workspace_bytes(B, S, H, D)
+
+
+def bw_attn_decode_kv3(q: torch.Tensor, k_pack, v_pack, slot_of: torch.Tensor, n_special: int, out=None,
+                       workspace=None):
     """Single-token attention over the 3-bit KV cache.  q fp32 [B][H][D]; k_pack / v_pack =
     (p3, s3, p4, s4) as returned by bw_kv_pack3 with this slot_of; returns out fp32 [B][H][D]."""
     B, H, D = q.shape
@@ -282,6 +288,9 @@ def bw_attn_decode_kv3(q: torch.Tensor, k_pack, v_pack, slot_of: torch.Tensor, n
     S = kp3.shape[1]
     if out is None:
         out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(bw_attn_decode_kv3_workspace_bytes(B, S, H, D), 16), dtype=torch.uint8,
+                                device=q.device)
     shp3, shs = (B, S, H, 3 * D // 8), (B, S, H)
     shp4, shs4 = (n_special, H, D // 2), (n_special, H)
     _check(_lib.bw_attn_decode_kv3(
@@ -291,5 +300,6 @@ def bw_attn_decode_kv3(q: torch.Tensor, k_pack, v_pack, slot_of: torch.Tensor, n
         _dev(vp3, "v_p3", (torch.uint8,), shp3), _dev(vs3, "v_s3", (torch.float32,), shs),
         _opt(vp4, "v_p4", (torch.uint8,), shp4), _opt(vs4, "v_s4", (torch.float32,), shs4),
         _dev(slot_of, "slot_of", (torch.int32,), (B, S)), n_special, B, S, H, D,
-        _dev(out, "out", (torch.float32,), (B, H, D)), _stream(q)))
+        _dev(out, "out", (torch.float32,), (B, H, D)),
+        _dev(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(q)))
     return out

@@ -9,50 +9,37 @@
 // 4-bit codes at special positions).  The codes are never expanded in HBM:
 // the kernel reads 3*D/8 + 4 bytes per vector, a fifth of a bf16 cache.
 //
-// One workgroup (512 threads) per (batch, head); the block index runs over
-// batches fastest, so with 8 batches each batch's heads share one XCD (the
-// dispatcher's round robin) and its L2 (scales and plane bytes of
-// neighbouring heads share cache lines).  Thread t takes 32-dim group
-// g = t % G (G = D/32) of the positions s = t / G + i * (512 / G):
-//   pass 1: the group's three plane words are unpacked four codes per 32-bit
-//     word: ((P >> k) & 0x01010101) holds bit j of codes k, k+8, k+16, k+24
-//     in its bytes, so u = b0 + 2 b1 + 4 (1 - b2) = code + 4 is built with
-//     shifts and masks and converted per byte; sum q*u, minus 4 * sum q, is
-//     reduced over the G lanes of a position (DPP) and scaled;
-//   special positions (slot_of in [0, n_special)) are rescored from their
-//     4-bit codes by one wave each, and are flagged in an LDS bitmask;
-//   softmax in LDS (max, exp, sum; fp32);
-//   pass 2: acc[d] += w_s * u_d with w_s = e_s * s3_s (0 at special
-//     positions), minus 4 * sum w; special positions are added from their
-//     4-bit codes by one wave each; lanes, waves and the special part are
-//     summed and divided by sum e.
+// Two launches (split over positions, then merged):
+//   1. grid (position chunks x batches): a workgroup takes CH positions of
+//      one batch for every head, so each position's H vectors (H * 3D/8
+//      contiguous bytes) and H scales are read whole.  Thread t owns head h,
+//      32-dim group g and position phase t % 4 (positions 4j + phase):
+//      pass 1: the group's three plane words are unpacked four codes per
+//        32-bit word: ((P >> k) & 0x01010101) holds bit j of codes k, k+8,
+//        k+16, k+24 in its bytes, so u = b0 + 2 b1 + 4 (1 - b2) = code + 4
+//        is built with shifts and masks; with q in fixed point (four
+//        base-256 digits of q * 2^30 / max|q|) sum q*u is four integer dot4
+//        per word, exact; minus 4 * sum q it is summed over the G groups and
+//        scaled.  Special positions (slot_of in [0, n_special)) are rescored
+//        from their 4-bit codes by the same threads;
+//      per head: m = max z, e = exp(z - m), l = sum e over the chunk;
+//      pass 2: acc[d] += w * u_d with w = e * s3 (0 at special positions;
+//        u_d converted two at a time as fp8 subnormals, the unit folded into w),
+//        minus 4 * sum w, plus the special positions' 4-bit terms; summed
+//        over the four phases, then (acc[D], m, l) per (chunk, head) go to
+//        the workspace.
+//   2. grid (batch x head): M = max m_c, out = sum_c acc_c e^(m_c - M) /
+//      sum_c l_c e^(m_c - M).
+// Every sum runs in a fixed order, so results are deterministic.
 #include "bw_internal.h"
 
 namespace bw {
 namespace {
 
 constexpr int kAttnThreads = 512;
+constexpr int kUnroll = 8;  // positions per thread with loads in flight together
+constexpr int kAttnMergeMax = 4096;  // chunks per (batch, head) the merge holds in LDS
 constexpr uint32_t kBytes = 0x01010101u;
-
-template <int G>
-__device__ __forceinline__ float group_sum(float v) {
-  // sum over the G consecutive lanes that share a position (G = 2 or 4)
-  v += __shfl_xor(v, 1);
-  if constexpr (G == 4) v += __shfl_xor(v, 2);
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum_f(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-__device__ __forceinline__ float wave_max_f(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
 
 // x shifted right by n (left by -n); n is a compile-time constant
 template <int n>
@@ -85,209 +72,440 @@ __device__ __forceinline__ void unpack_group(uint32_t p0, uint32_t p1, uint32_t 
   u[7] = unpack_k<7>(p0, p1, p2n);
 }
 
-// byte b of x as a float (one v_cvt_f32_ubyteN)
-__device__ __forceinline__ float byte_f(uint32_t x, int b) {
-  return static_cast<float>((x >> (8 * b)) & 0xFFu);
+// bytes 2w and 2w+1 of x (w = HI_WORD) read as fp8 values: a byte 0..7 is an fp8 subnormal,
+// so the pair is (x_b * unit) exactly, unit being the fp8 value of byte 1
+template <bool HI_WORD>
+__device__ __forceinline__ float2 byte_pair_fp8(uint32_t x) {
+  const auto v = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(x), HI_WORD);
+  return make_float2(v[0], v[1]);
 }
 
-// 4-bit two's-complement nibble n (0..15) -> value
+// 4-bit two's-complement nibble (low or high half of a byte) -> value
 __device__ __forceinline__ float nib_f(uint32_t byte, int hi) {
   const int n = static_cast<int>((byte >> (4 * hi)) & 0xFu);
   return static_cast<float>(n >= 8 ? n - 16 : n);
 }
 
+// DPP move of a float with bound control (lanes whose source is outside the
+// row read 0): row_shr:n is 0x110 + n, quad_perm(a,b,c,d) is a|b<<2|c<<4|d<<6
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+constexpr int kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E;  // quad_perm [1,0,3,2] and [2,3,0,1]
+
+// Sum over the G lanes of one (head, phase), lanes 4g + phase of a 16-lane
+// row: after the row shifts the lane with g = G - 1 holds the total (others
+// hold partial sums).
+template <int G>
+__device__ __forceinline__ float groups_sum_last(float v) {
+  v += dpp_f<kRowShr4>(v);
+  if constexpr (G == 4) v += dpp_f<kRowShr8>(v);
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
 template <int D>
-__global__ __launch_bounds__(kAttnThreads) void k_attn_decode3(
+__global__ __launch_bounds__(kAttnThreads) void k_attn_chunk(
     const float* __restrict__ q, const uint8_t* __restrict__ kp3, const float* __restrict__ ks3,
     const uint8_t* __restrict__ kp4, const float* __restrict__ ks4, const uint8_t* __restrict__ vp3,
     const float* __restrict__ vs3, const uint8_t* __restrict__ vp4, const float* __restrict__ vs4,
-    const int32_t* __restrict__ slot_of, int64_t n_special, int64_t B, int64_t S, int64_t H,
-    float* __restrict__ out) {
-  constexpr int G = D / 32;                 // 32-dim groups per vector
-  constexpr int SL = kAttnThreads / G;      // positions in flight per pass step
-  constexpr int VB = 3 * D / 8;             // plane bytes per vector
-  extern __shared__ float s_z[];            // [S] scores, then exp weights
-  __shared__ uint32_t s_spec[kAttnMaxS / 32];
-  __shared__ float s_red[kAttnThreads / 64];
-  __shared__ float s_acc[kAttnThreads / 64][D];
-  __shared__ float s_fix[kAttnThreads / 64][D];
+    const int32_t* __restrict__ slot_of, int64_t n_special, int64_t B, int64_t S, int64_t H, int CH, int nch,
+    float* __restrict__ part) {
+  constexpr int G = D / 32;                   // 32-dim groups per vector
+  constexpr int HS = kAttnThreads / (4 * G);  // heads per head block
+  constexpr int VB = 3 * D / 8;               // plane bytes per vector
+  extern __shared__ float s_dyn[];            // s_z[CH][H + 1], then s_m[H], s_l[H]
+  __shared__ uint16_t s_list[kAttnMaxChunk];  // special positions of the chunk, ascending
+  __shared__ uint32_t s_spec[kAttnMaxChunk / 32];
+  __shared__ int s_wscan[kAttnThreads / 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int g = tid % G;
-  const int slice = tid / G;
+  const int phase = tid & 3;
+  const int g = (tid >> 2) % G;
+  const int hl = tid / (4 * G);
   const int64_t b = blockIdx.x % B;
-  const int64_t h = blockIdx.x / B;
-  const float* __restrict__ qv = q + (b * H + h) * D;
-  const int32_t* __restrict__ slots = slot_of + b * S;
+  const int64_t c = blockIdx.x / B;
+  const int64_t p0 = c * CH;
+  const int np = static_cast<int>((S - p0 < CH) ? S - p0 : CH);  // positions in this chunk
+  const int HP = static_cast<int>(H) + 1;
+  float* __restrict__ s_z = s_dyn;
+  float* __restrict__ s_m = s_dyn + static_cast<int64_t>(CH) * HP;
+  float* __restrict__ s_l = s_m + H;
+  const int32_t* __restrict__ slots = slot_of + b * S + p0;
   const float inv_sqrt_d = 1.0f / sqrtf(static_cast<float>(D));
 
-  // this thread's 32 query values (group g)
-  float qg[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) qg[i] = qv[32 * g + i];
-  float qsum = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) qsum += qg[i];
-
-  // special-position bitmask
-  const int nwords = static_cast<int>((S + 31) / 32);
-  for (int w = tid; w < nwords; w += kAttnThreads) s_spec[w] = 0u;
-  __syncthreads();
-  for (int64_t s = tid; s < S; s += kAttnThreads) {
-    const int32_t sl = slots[s];
-    if (sl >= 0 && sl < n_special) atomicOr(&s_spec[s >> 5], 1u << (s & 31));
-  }
-
-  // pass 1: scores from the 3-bit codes
-  for (int64_t s = slice; s < S; s += SL) {
-    const int64_t vec = (b * S + s) * H + h;
-    const uint32_t* __restrict__ pw = reinterpret_cast<const uint32_t*>(kp3 + vec * VB) + 3 * g;
-    uint32_t u[8];
-    unpack_group(pw[0], pw[1], pw[2], u);
-    float dot = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-#pragma unroll
-      for (int by = 0; by < 4; ++by) dot = fmaf(qg[k + 8 * by], byte_f(u[k], by), dot);
-    dot = group_sum<G>(dot - 4.0f * qsum);
-    if (g == 0) s_z[s] = dot * ks3[vec] * inv_sqrt_d;
-  }
-  __syncthreads();
-
-  // special positions: rescore from the 4-bit codes, one wave per position
-  for (int w = wave; w < nwords; w += kAttnThreads / 64) {
-    uint32_t bits = s_spec[w];
-    while (bits) {
-      const int i = __builtin_ctz(bits);
-      bits &= bits - 1;
-      const int64_t s = 32 * static_cast<int64_t>(w) + i;
-      const int64_t sl = slots[s];
-      const uint8_t* __restrict__ p4 = kp4 + (sl * H + h) * (D / 2);
-      float part = 0.0f;
-      for (int d2 = lane; d2 < D / 2; d2 += 64) {
-        const uint32_t byte = p4[d2];
-        part = fmaf(qv[2 * d2], nib_f(byte, 0), part);
-        part = fmaf(qv[2 * d2 + 1], nib_f(byte, 1), part);
-      }
-      part = wave_sum_f(part);
-      if (lane == 0) s_z[s] = part * ks4[sl * H + h] * inv_sqrt_d;
+  // special positions of the chunk: bitmask by wave ballots, then an ordered list
+  const int nwords = (np + 31) / 32;
+  for (int s0 = 64 * wave; s0 < np; s0 += kAttnThreads) {
+    const int s = s0 + lane;
+    const int32_t sl = (s < np) ? slots[s] : -1;
+    const uint64_t bal = __ballot(sl >= 0 && sl < n_special);
+    if (lane == 0) {
+      s_spec[s0 >> 5] = static_cast<uint32_t>(bal);
+      if (s0 + 32 < np) s_spec[(s0 >> 5) + 1] = static_cast<uint32_t>(bal >> 32);
     }
   }
   __syncthreads();
-
-  // softmax: max, exp, sum
-  float mx = -INFINITY;
-  for (int64_t s = tid; s < S; s += kAttnThreads) mx = fmaxf(mx, s_z[s]);
-  mx = wave_max_f(mx);
-  if (lane == 0) s_red[wave] = mx;
-  __syncthreads();
-  mx = s_red[0];
+  {
+    const uint32_t word = (tid < nwords) ? s_spec[tid] : 0u;
+    const int cnt = __popc(word);
+    int incl = cnt;
 #pragma unroll
-  for (int w = 1; w < kAttnThreads / 64; ++w) mx = fmaxf(mx, s_red[w]);
-  __syncthreads();
-  float tot = 0.0f;
-  for (int64_t s = tid; s < S; s += kAttnThreads) {
-    const float e = expf(s_z[s] - mx);
-    s_z[s] = e;
-    tot += e;
-  }
-  tot = wave_sum_f(tot);
-  if (lane == 0) s_red[wave] = tot;
-  __syncthreads();
-  tot = 0.0f;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    if (lane == 63) s_wscan[wave] = incl;
+    __syncthreads();
+    int pos = incl - cnt;
 #pragma unroll
-  for (int w = 0; w < kAttnThreads / 64; ++w) tot += s_red[w];
-
-  // pass 2: weighted values from the 3-bit codes (special positions weigh 0)
-  float acc[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) acc[i] = 0.0f;
-  float wsum = 0.0f;
-  for (int64_t s = slice; s < S; s += SL) {
-    const int64_t vec = (b * S + s) * H + h;
-    const uint32_t* __restrict__ pw = reinterpret_cast<const uint32_t*>(vp3 + vec * VB) + 3 * g;
-    const bool sp = (s_spec[s >> 5] >> (s & 31)) & 1u;
-    const float w = sp ? 0.0f : s_z[s] * vs3[vec];
-    uint32_t u[8];
-    unpack_group(pw[0], pw[1], pw[2], u);
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-#pragma unroll
-      for (int by = 0; by < 4; ++by) acc[k + 8 * by] = fmaf(w, byte_f(u[k], by), acc[k + 8 * by]);
-    wsum += w;
-  }
-  // remove the +4 of the codes, then sum the lanes of each group within the wave
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    float v = acc[i] - 4.0f * wsum;
-#pragma unroll
-    for (int o = G; o < 64; o <<= 1) v += __shfl_xor(v, o);
-    acc[i] = v;
-  }
-  if (lane < G) {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) s_acc[wave][32 * g + i] = acc[i];
-  }
-
-  // special positions from their 4-bit codes, one wave per position
-  float fix[D / 64 > 0 ? D / 64 : 1][2];
-#pragma unroll
-  for (int j = 0; j < (D / 64 > 0 ? D / 64 : 1); ++j) fix[j][0] = fix[j][1] = 0.0f;
-  for (int w = wave; w < nwords; w += kAttnThreads / 64) {
-    uint32_t bits = s_spec[w];
+    for (int w = 0; w < kAttnThreads / 64; ++w) pos += (w < wave) ? s_wscan[w] : 0;
+    uint32_t bits = word;
     while (bits) {
       const int i = __builtin_ctz(bits);
       bits &= bits - 1;
-      const int64_t s = 32 * static_cast<int64_t>(w) + i;
-      const int64_t sl = slots[s];
-      const uint8_t* __restrict__ p4 = vp4 + (sl * H + h) * (D / 2);
-      const float wt = s_z[s] * vs4[sl * H + h];
+      s_list[pos++] = static_cast<uint16_t>(32 * tid + i);
+    }
+  }
+  int nspec = 0;
 #pragma unroll
-      for (int j = 0; j < (D / 64 > 0 ? D / 64 : 1); ++j) {
-        const int d2 = lane + 64 * j;
-        if (d2 < D / 2) {
-          const uint32_t byte = p4[d2];
-          fix[j][0] = fmaf(wt, nib_f(byte, 0), fix[j][0]);
-          fix[j][1] = fmaf(wt, nib_f(byte, 1), fix[j][1]);
+  for (int w = 0; w < kAttnThreads / 64; ++w) nspec += s_wscan[w];
+  __syncthreads();
+
+  // ---- pass 1: scores, one head block at a time
+  for (int hb = 0; hb < H; hb += HS) {
+    const int64_t h = hb + hl;
+    const bool hok = h < H;
+    const int64_t hc = hok ? h : H - 1;
+    const float* __restrict__ qv = q + (b * H + hc) * D + 32 * g;
+    float qg[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) qg[i] = qv[i];
+    // fixed-point query: Q_i = rne(q_i * 2^30 / max|q|) (fp64 product), four
+    // balanced base-256 digits; its deviation from q is at most 2^-31 max|q|
+    float qmax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) qmax = fmaxf(qmax, fabsf(qg[i]));
+    qmax = fmaxf(qmax, __shfl_xor(qmax, 4));
+    if constexpr (G == 4) qmax = fmaxf(qmax, __shfl_xor(qmax, 8));
+    const double qscale = qmax > 0.0f ? 1073741824.0 / static_cast<double>(qmax) : 0.0;
+    const float qunit = qmax * (1.0f / 1073741824.0f);  // exact: a power-of-two scaling
+    uint32_t qd[4][8];  // digit j of codes k, k+8, k+16, k+24 in bytes 0..3
+    int64_t qsum = 0;   // sum of the group's Q
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qd[j][k] = 0u;
+#pragma unroll
+      for (int by = 0; by < 4; ++by) {
+        int Q = static_cast<int>(rint(static_cast<double>(qg[k + 8 * by]) * qscale));
+        qsum += Q;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int dg = (j < 3) ? static_cast<int>(static_cast<int8_t>(Q & 0xFF)) : Q;
+          qd[j][k] |= (static_cast<uint32_t>(dg) & 0xFFu) << (8 * by);
+          Q = (Q - dg) >> 8;
         }
       }
     }
-  }
+    // 4 sum Q = 2^24 q4hi + q4lo with 0 <= q4lo < 2^24, so that the exact sum
+    // below splits into two int32 parts
+    const int q4lo = static_cast<int>((4 * qsum) & 0xFFFFFF);
+    const int q4hi = static_cast<int>((4 * qsum - q4lo) >> 24);
+
+    // Loads are unconditional so a batch is in flight at once: a position past
+    // the chunk or a head past H reads position p0, head hc (in bounds) and is
+    // not stored.  The next batch's loads are issued before this batch is
+    // computed (two register buffers).
+    uint32_t pl[kUnroll][3], nl[kUnroll][3];
+    float sc[kUnroll], ns[kUnroll];
+    auto load_k = [&](int j0, uint32_t (&dl)[kUnroll][3], float (&ds)[kUnroll]) {
 #pragma unroll
-  for (int j = 0; j < (D / 64 > 0 ? D / 64 : 1); ++j) {
-    const int d2 = lane + 64 * j;
-    if (d2 < D / 2) {
-      s_fix[wave][2 * d2] = fix[j][0];
-      s_fix[wave][2 * d2 + 1] = fix[j][1];
+      for (int j = 0; j < kUnroll; ++j) {
+        const int p = j0 + 4 * j;
+        const int64_t vec = (b * S + p0 + (p < np ? p : 0)) * H + hc;
+        const uint32_t* __restrict__ pw = reinterpret_cast<const uint32_t*>(kp3 + vec * VB) + 3 * g;
+        dl[j][0] = pw[0];
+        dl[j][1] = pw[1];
+        dl[j][2] = pw[2];
+        ds[j] = ks3[vec];
+      }
+    };
+    load_k(phase, pl, sc);
+    for (int j0 = phase; j0 < np; j0 += 4 * kUnroll) {
+      load_k(j0 + 4 * kUnroll < np ? j0 + 4 * kUnroll : phase, nl, ns);
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j) {
+        uint32_t u[8];
+        unpack_group(pl[j][0], pl[j][1], pl[j][2], u);
+        int dg[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+          for (int d = 0; d < 4; ++d)
+            dg[d] = __builtin_amdgcn_sdot4(static_cast<int>(u[k]), static_cast<int>(qd[d][k]), dg[d], false);
+        // sum Q u - 4 sum Q = lo + 2^24 hi, both exact in int32
+        // (|dg[d]| <= 32 * 7 * 128, so |lo| < 1.96e9); one rounding each to fp32
+        const int lo = dg[0] + (dg[1] << 8) + (dg[2] << 16) - q4lo;
+        const int hi = dg[3] - q4hi;
+        const float tf = fmaf(static_cast<float>(hi), 16777216.0f, static_cast<float>(lo));
+        const float dot = groups_sum_last<G>(tf);
+        const int p = j0 + 4 * j;
+        if (g == G - 1 && hok && p < np) s_z[p * HP + h] = dot * qunit * sc[j] * inv_sqrt_d;
+      }
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j) {
+        pl[j][0] = nl[j][0];
+        pl[j][1] = nl[j][1];
+        pl[j][2] = nl[j][2];
+        sc[j] = ns[j];
+      }
+    }
+    // special positions: rescored from their 4-bit codes by the lanes of the
+    // same phase (the g = G - 1 lane wrote the 3-bit score: program order)
+    for (int e = 0; e < nspec; ++e) {
+      const int p = s_list[e];
+      if ((p & 3) != phase) continue;
+      const int64_t sl = slots[p];
+      const uint4 nb = *reinterpret_cast<const uint4*>(kp4 + (sl * H + hc) * (D / 2) + 16 * g);
+      const uint32_t w4[4] = {nb.x, nb.y, nb.z, nb.w};
+      float dot = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t byte = (w4[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+        dot = fmaf(qg[2 * i], nib_f(byte, 0), dot);
+        dot = fmaf(qg[2 * i + 1], nib_f(byte, 1), dot);
+      }
+      dot = groups_sum_last<G>(dot);
+      if (g == G - 1 && hok) s_z[p * HP + h] = dot * ks4[sl * H + hc] * inv_sqrt_d;
     }
   }
   __syncthreads();
-  if (tid < D) {
-    // byte `by` of u[k] is code k + 8 by of its group, so acc[i] (written to
-    // s_acc[.][32 g + i]) is dimension 32 g + i
-    float a = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kAttnThreads / 64; ++w) a += s_acc[w][tid] + s_fix[w][tid];
-    out[(b * H + h) * D + tid] = a / tot;
+
+  // ---- per head over the chunk: m = max z, e = exp(z - m), l = sum e
+  for (int64_t h = wave; h < H; h += kAttnThreads / 64) {
+    float mx = -INFINITY;
+    for (int p = lane; p < np; p += 64) mx = fmaxf(mx, s_z[p * HP + h]);
+    mx = wave_max_f(mx);
+    float tot = 0.0f;
+    for (int p = lane; p < np; p += 64) {
+      const float e = expf(s_z[p * HP + h] - mx);
+      s_z[p * HP + h] = e;
+      tot += e;
+    }
+    tot = wave_sum_f(tot);
+    if (lane == 0) {
+      s_m[h] = mx;
+      s_l[h] = tot;
+    }
   }
+  __syncthreads();
+
+  // ---- pass 2: weighted values, one head block at a time
+  for (int hb = 0; hb < H; hb += HS) {
+    const int64_t h = hb + hl;
+    const bool hok = h < H;
+    const int64_t hc = hok ? h : H - 1;
+    float acc[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[i] = 0.0f;
+    float wsum = 0.0f;
+    // codes enter as fp8 subnormals (byte * unit); 1 / unit is a power of two
+    const float inv_unit = 1.0f / byte_pair_fp8<false>(1u).x;
+    uint32_t pl[kUnroll][3], nl[kUnroll][3];
+    float sc[kUnroll], ns[kUnroll];
+    auto load_v = [&](int j0, uint32_t (&dl)[kUnroll][3], float (&ds)[kUnroll]) {
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j) {
+        const int p = j0 + 4 * j;
+        const int64_t vec = (b * S + p0 + (p < np ? p : 0)) * H + hc;
+        const uint32_t* __restrict__ pw = reinterpret_cast<const uint32_t*>(vp3 + vec * VB) + 3 * g;
+        dl[j][0] = pw[0];
+        dl[j][1] = pw[1];
+        dl[j][2] = pw[2];
+        ds[j] = vs3[vec];
+      }
+    };
+    load_v(phase, pl, sc);
+    for (int j0 = phase; j0 < np; j0 += 4 * kUnroll) {
+      load_v(j0 + 4 * kUnroll < np ? j0 + 4 * kUnroll : phase, nl, ns);
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j) {
+        const int p = j0 + 4 * j;
+        const int pc = p < np ? p : 0;
+        const bool live = p < np && !((s_spec[pc >> 5] >> (pc & 31)) & 1u);
+        const float w = live ? s_z[pc * HP + hc] * sc[j] : 0.0f;
+        const float wu = w * inv_unit;  // exact: power-of-two scaling
+        uint32_t u[8];
+        unpack_group(pl[j][0], pl[j][1], pl[j][2], u);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float2 lo2 = byte_pair_fp8<false>(u[k]);  // codes k, k + 8
+          const float2 hi2 = byte_pair_fp8<true>(u[k]);   // codes k + 16, k + 24
+          acc[k] = fmaf(wu, lo2.x, acc[k]);
+          acc[k + 8] = fmaf(wu, lo2.y, acc[k + 8]);
+          acc[k + 16] = fmaf(wu, hi2.x, acc[k + 16]);
+          acc[k + 24] = fmaf(wu, hi2.y, acc[k + 24]);
+        }
+        wsum += w;
+      }
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j) {
+        pl[j][0] = nl[j][0];
+        pl[j][1] = nl[j][1];
+        pl[j][2] = nl[j][2];
+        sc[j] = ns[j];
+      }
+    }
+    // remove the +4 of the codes, add the special positions' 4-bit terms
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[i] -= 4.0f * wsum;
+    for (int e = 0; e < nspec; ++e) {
+      const int p = s_list[e];
+      if ((p & 3) != phase) continue;
+      const int64_t sl = slots[p];
+      const uint4 nb = *reinterpret_cast<const uint4*>(vp4 + (sl * H + hc) * (D / 2) + 16 * g);
+      const uint32_t w4[4] = {nb.x, nb.y, nb.z, nb.w};
+      const float w = s_z[p * HP + hc] * vs4[sl * H + hc];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t byte = (w4[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+        acc[2 * i] = fmaf(w, nib_f(byte, 0), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(w, nib_f(byte, 1), acc[2 * i + 1]);
+      }
+    }
+    // sum the four phases; phase 0 writes dims 32 g .. 32 g + 31 of head h
+    // (byte `by` of u[k] is code k + 8 by of its group, so acc[i] is dim 32 g + i)
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      float v = acc[i];
+      v += dpp_f<kQuadXor1>(v);
+      v += dpp_f<kQuadXor2>(v);
+      acc[i] = v;
+    }
+    if (phase == 0 && hok) {
+      float4* dst = reinterpret_cast<float4*>(part + ((b * nch + c) * H + h) * (D + 4) + 32 * g);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) dst[v] = make_float4(acc[4 * v], acc[4 * v + 1], acc[4 * v + 2], acc[4 * v + 3]);
+    }
+  }
+  for (int64_t h = tid; h < H; h += kAttnThreads) {
+    float* dst = part + ((b * nch + c) * H + h) * (D + 4) + D;
+    dst[0] = s_m[h];
+    dst[1] = s_l[h];
+  }
+}
+
+// Merge the chunks of one (batch, head): the chunk maxima and sums go to LDS
+// (one thread per chunk), then one thread per dimension adds the chunks'
+// rescaled sums with eight loads in flight.
+template <int D>
+__global__ __launch_bounds__(D) void k_attn_merge(const float* __restrict__ part, int64_t B, int64_t H, int nch,
+                                                  float* __restrict__ out) {
+  __shared__ float s_mc[kAttnMergeMax];
+  __shared__ float s_f[kAttnMergeMax];
+  __shared__ float s_L;
+  const int d = threadIdx.x;
+  const int64_t b = blockIdx.x % B;
+  const int64_t h = blockIdx.x / B;
+  const int64_t stride = H * (D + 4);
+  const float* __restrict__ base = part + (b * nch * H + h) * (D + 4);
+  for (int c = d; c < nch; c += D) {
+    s_mc[c] = base[c * stride + D];
+    s_f[c] = base[c * stride + D + 1];
+  }
+  __syncthreads();
+  float M = -INFINITY;
+  for (int c = 0; c < nch; ++c) M = fmaxf(M, s_mc[c]);
+  __syncthreads();
+  for (int c = d; c < nch; c += D) s_mc[c] = expf(s_mc[c] - M);  // rescale factor of chunk c
+  __syncthreads();
+  if (d == 0) {
+    float L = 0.0f;
+    for (int c = 0; c < nch; ++c) L = fmaf(s_f[c], s_mc[c], L);
+    s_L = L;
+  }
+  float O = 0.0f;
+  int c = 0;
+  for (; c + 8 <= nch; c += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = base[(c + u) * stride + d];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) O = fmaf(v[u], s_mc[c + u], O);
+  }
+  for (; c < nch; ++c) O = fmaf(base[c * stride + d], s_mc[c], O);
+  __syncthreads();
+  out[(b * H + h) * D + d] = O / s_L;
+}
+
+struct AttnGrid {
+  int ch, nch;
+};
+
+// Positions per chunk: about one workgroup per CU over the batch, a multiple of
+// 4, with the chunk's scores (CH * (H + 1) + 2H floats) within kAttnLdsFloats
+// and at most kAttnMergeMax chunks; nch = 0 marks a shape beyond those limits.
+AttnGrid attn_grid(int64_t B, int64_t S, int64_t H) {
+  int64_t ch = (S * B) / 256;
+  const int64_t min_ch = (S + kAttnMergeMax - 1) / kAttnMergeMax;
+  if (ch < min_ch) ch = min_ch;
+  int64_t cap = (kAttnLdsFloats - 2 * H) / (H + 1);
+  if (cap > kAttnMaxChunk) cap = kAttnMaxChunk;
+  const int64_t s4 = (S + 3) / 4 * 4;
+  if (cap > s4) cap = s4;
+  cap = cap / 4 * 4;
+  ch = (ch + 3) / 4 * 4;
+  if (ch > cap) ch = cap;
+  if (ch < 4) ch = 4;
+  AttnGrid g;
+  g.ch = static_cast<int>(ch);
+  const int64_t nch = (S + ch - 1) / ch;
+  g.nch = (nch <= kAttnMergeMax && cap >= 4) ? static_cast<int>(nch) : 0;
+  return g;
 }
 
 }  // namespace
 
+bool attn_decode3_supported(int64_t B, int64_t S, int64_t H) { return attn_grid(B, S, H).nch > 0; }
+
+size_t attn_decode3_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D) {
+  const AttnGrid g = attn_grid(B, S, H);
+  return static_cast<size_t>(B) * g.nch * H * (D + 4) * sizeof(float);
+}
+
 hipError_t launch_attn_decode3(const float* q, const uint8_t* kp3, const float* ks3, const uint8_t* kp4,
                                const float* ks4, const uint8_t* vp3, const float* vs3, const uint8_t* vp4,
                                const float* vs4, const int32_t* slot_of, int64_t n_special, int64_t B, int64_t S,
-                               int64_t H, int64_t D, float* out, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(B * H));
-  const size_t lds = static_cast<size_t>(S) * sizeof(float);
+                               int64_t H, int64_t D, float* out, void* ws, hipStream_t s) {
+  const AttnGrid g = attn_grid(B, S, H);
+  float* part = static_cast<float*>(ws);
+  const dim3 grid1(static_cast<unsigned>(g.nch * B));
+  const size_t lds = (static_cast<size_t>(g.ch) * (H + 1) + 2 * H) * sizeof(float);
+  const dim3 grid2(static_cast<unsigned>(B * H));
   if (D == 64) {
-    hipLaunchKernelGGL(k_attn_decode3<64>, grid, dim3(kAttnThreads), lds, s, q, kp3, ks3, kp4, ks4, vp3, vs3, vp4,
-                       vs4, slot_of, n_special, B, S, H, out);
+    hipLaunchKernelGGL(k_attn_chunk<64>, grid1, dim3(kAttnThreads), lds, s, q, kp3, ks3, kp4, ks4, vp3, vs3, vp4, vs4,
+                       slot_of, n_special, B, S, H, g.ch, g.nch, part);
+    hipLaunchKernelGGL(k_attn_merge<64>, grid2, dim3(64), 0, s, part, B, H, g.nch, out);
   } else {
-    hipLaunchKernelGGL(k_attn_decode3<128>, grid, dim3(kAttnThreads), lds, s, q, kp3, ks3, kp4, ks4, vp3, vs3, vp4,
-                       vs4, slot_of, n_special, B, S, H, out);
+    hipLaunchKernelGGL(k_attn_chunk<128>, grid1, dim3(kAttnThreads), lds, s, q, kp3, ks3, kp4, ks4, vp3, vs3, vp4,
+                       vs4, slot_of, n_special, B, S, H, g.ch, g.nch, part);
+    hipLaunchKernelGGL(k_attn_merge<128>, grid2, dim3(128), 0, s, part, B, H, g.nch, out);
   }
   return hipGetLastError();
 }

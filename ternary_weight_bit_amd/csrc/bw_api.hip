@@ -214,27 +214,40 @@ bw_status bw_kv_unpack3(const uint8_t* p3, const float* s3, const uint8_t* p4, c
                     "bw_kv_unpack3");
 }
 
+size_t bw_attn_decode_kv3_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D) {
+  if (B <= 0 || S <= 0 || H <= 0 || H > bw::kAttnMaxH || (D != 64 && D != 128)) return 0;
+  if (!bw::attn_decode3_supported(B, S, H)) return 0;
+  return bw::attn_decode3_workspace_bytes(B, S, H, D);
+}
+
 bw_status bw_attn_decode_kv3(const float* q, const uint8_t* k_p3, const float* k_s3, const uint8_t* k_p4,
                              const float* k_s4, const uint8_t* v_p3, const float* v_s3, const uint8_t* v_p4,
                              const float* v_s4, const int32_t* slot_of, int64_t n_special, int64_t B, int64_t S,
-                             int64_t H, int64_t D, float* out, void* stream) {
-  BW_REQUIRE(B >= 0 && H >= 1 && n_special >= 0 && S >= 1 && S <= bw::kAttnMaxS, BW_ERR_SHAPE,
-             "bw_attn_decode_kv3: need B >= 0, H >= 1, 1 <= S <= %lld, n_special >= 0 (B=%lld S=%lld H=%lld)",
-             (long long)bw::kAttnMaxS, (long long)B, (long long)S, (long long)H);
+                             int64_t H, int64_t D, float* out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  BW_REQUIRE(B >= 0 && H >= 1 && H <= bw::kAttnMaxH && n_special >= 0 && S >= 1, BW_ERR_SHAPE,
+             "bw_attn_decode_kv3: need B >= 0, S >= 1, 1 <= H <= %lld, n_special >= 0 (B=%lld S=%lld H=%lld)",
+             (long long)bw::kAttnMaxH, (long long)B, (long long)S, (long long)H);
   BW_REQUIRE(D == 64 || D == 128, BW_ERR_SHAPE, "bw_attn_decode_kv3: head_dim must be 64 or 128 (D=%lld)",
              (long long)D);
   BW_REQUIRE(B <= (int64_t(1) << 40) / S / H / D && B * H <= (int64_t(1) << 31) - 1, BW_ERR_SHAPE,
              "bw_attn_decode_kv3: tensor too large");
   if (B == 0) return ok();
-  BW_REQUIRE(q && k_p3 && k_s3 && v_p3 && v_s3 && slot_of && out, BW_ERR_NULL, "bw_attn_decode_kv3: NULL pointer");
+  BW_REQUIRE(bw::attn_decode3_supported(B, S, H), BW_ERR_SHAPE,
+             "bw_attn_decode_kv3: S=%lld with H=%lld exceeds the chunk limits", (long long)S, (long long)H);
+  BW_REQUIRE(q && k_p3 && k_s3 && v_p3 && v_s3 && slot_of && out && workspace, BW_ERR_NULL,
+             "bw_attn_decode_kv3: NULL pointer");
   BW_REQUIRE(n_special == 0 || (k_p4 && k_s4 && v_p4 && v_s4), BW_ERR_NULL,
              "bw_attn_decode_kv3: 4-bit slabs required when n_special > 0");
   BW_REQUIRE(!misaligned(q) && !misaligned(k_p3) && !misaligned(k_s3) && !misaligned(k_p4) && !misaligned(k_s4) &&
                  !misaligned(v_p3) && !misaligned(v_s3) && !misaligned(v_p4) && !misaligned(v_s4) &&
-                 !misaligned(slot_of) && !misaligned(out),
+                 !misaligned(slot_of) && !misaligned(out) && !misaligned(workspace),
              BW_ERR_ALIGN, "bw_attn_decode_kv3: device pointers must be 16-byte aligned");
+  const size_t need = bw::attn_decode3_workspace_bytes(B, S, H, D);
+  BW_REQUIRE(workspace_bytes >= need, BW_ERR_ARG, "bw_attn_decode_kv3: workspace needs %zu bytes, got %zu", need,
+             workspace_bytes);
   return hip_status(bw::launch_attn_decode3(q, k_p3, k_s3, k_p4, k_s4, v_p3, v_s3, v_p4, v_s4, slot_of, n_special, B,
-                                            S, H, D, out, static_cast<hipStream_t>(stream)),
+                                            S, H, D, out, workspace, static_cast<hipStream_t>(stream)),
                     "bw_attn_decode_kv3");
 }
 

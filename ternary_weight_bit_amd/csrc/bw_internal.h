@@ -48,12 +48,17 @@ hipError_t launch_sparse_a8(const void* g, const void* u, bool bf16, int64_t M, 
                             int64_t k_keep, int8_t* codes, float* scales, uint32_t* mask,
                             hipStream_t s);
 
-// Single-token attention over the 3-bit KV cache (one workgroup per batch x head).
-constexpr int64_t kAttnMaxS = 16384;
+// Single-token attention over the 3-bit KV cache: chunks of positions x batches,
+// then a merge; the workspace holds each (chunk, head)'s partial sums.
+constexpr int kAttnMaxChunk = 4096;     // positions per chunk
+constexpr int64_t kAttnLdsFloats = 16384;  // chunk scores + per-head max/sum in LDS
+constexpr int64_t kAttnMaxH = 1024;
+bool attn_decode3_supported(int64_t B, int64_t S, int64_t H);  // S within the chunk x merge limits
+size_t attn_decode3_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D);
 hipError_t launch_attn_decode3(const float* q, const uint8_t* kp3, const float* ks3, const uint8_t* kp4,
                                const float* ks4, const uint8_t* vp3, const float* vs3, const uint8_t* vp4,
                                const float* vs4, const int32_t* slot_of, int64_t n_special, int64_t B, int64_t S,
-                               int64_t H, int64_t D, float* out, hipStream_t s);
+                               int64_t H, int64_t D, float* out, void* ws, hipStream_t s);
 
 hipError_t launch_kv_pack3(const void* kv, bool bf16, int64_t B, int64_t S, int64_t H, int64_t D,
                            const int32_t* slot_of, int64_t n_special, uint8_t* p3, float* s3,

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -119,11 +119,18 @@ def test_kv_validation():
 
 def test_attn_validation():
     f = lib.bw_attn_decode_kv3
-    args = lambda B, S, H, D, n=0, q=A, k4=None, out=A: (q, A, A, k4, k4, A, A, k4, k4, A, n, B, S, H, D, out, None)
+    ws = bw.bw_attn_decode_kv3_workspace_bytes(8, 4096, 32, 128)
+    assert ws >= 8 * 32 * 128 * 4 and bw.bw_attn_decode_kv3_workspace_bytes(8, 4096, 32, 96) == 0
+
+    def args(B, S, H, D, n=0, q=A, k4=None, out=A, w=A, wb=ws):
+        return (q, A, A, k4, k4, A, A, k4, k4, A, n, B, S, H, D, out, w, wb, None)
+
     assert f(*args(8, 4096, 32, 96)) == 2  # head_dim
     assert f(*args(8, 0, 32, 128)) == 2  # S
-    assert f(*args(8, 16385, 32, 128)) == 2  # S above the LDS-resident limit
+    assert f(*args(8, 4096, 2048, 128)) == 2  # H above the LDS limit
     assert f(*args(8, 4096, 32, 128, n=3)) == 1  # side slabs missing
     assert f(*args(8, 4096, 32, 128, q=None)) == 1
+    assert f(*args(8, 4096, 32, 128, w=None)) == 1
     assert f(*args(8, 4096, 32, 128, out=MIS)) == 3
-    assert f(*args(0, 4096, 32, 128, q=None, out=None)) == 0  # empty batch
+    assert f(*args(8, 4096, 32, 128, wb=ws - 1)) == 5
+    assert f(*args(0, 4096, 32, 128, q=None, out=None, w=None)) == 0  # empty batch

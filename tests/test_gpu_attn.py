@@ -5,7 +5,12 @@ Both sides quantize the same bf16 K/V themselves (GPU: bw_kv_pack3, pinned bit-e
 to the oracle codec elsewhere; oracle: kv3.kv_pack3).  The GPU computes in fp32, so
 each output is held to a first-order rounding bound derived from the arithmetic:
 with u = 2^-24 and gamma_n = n u / (1 - n u),
-  score error  E_z   = max_s gamma_D * sum_d |q_d k_sd| / sqrt(D) + 4u |z_s|
+  score error  E_z   = max_s [gamma_D * sum_d |q_d k_sd| + 2^-31 max|q| sum_d |k_sd|
+                            + 2^-23 max|q| s_s] / sqrt(D) + 4u |z_s|
+(the second term is the kernel's fixed-point query, q rounded to multiples of
+2^-30 max|q|, for its integer dot products; the third covers the two fp32
+roundings of the exact integer sum, whose low part is below 2^31 units of
+2^-30 max|q| times the scale s_s)
   weight error E_p   = 2 E_z + gamma_S + 2u      (exp, normalization, max shift)
   |out_d - ref_d| <= (E_p + gamma_S + 2u) * sum_s p_s |v_sd|  (+ 1e-30)
 A wrong index, sign, scale or a missed special position costs O(1) of that sum."""
@@ -39,7 +44,9 @@ def check_attention(q32, k16, v16, slot_of, n_special, label, pairs=None):
     if ns == 0:
         kp = (kp[0], kp[1], None, None)
         vp = (vp[0], vp[1], None, None)
-    out = host(bw.bw_attn_decode_kv3(f32_dev(q32), kp, vp, sl, ns))
+    ws = torch.full((max(bw.bw_attn_decode_kv3_workspace_bytes(B, S, H, D), 16),), 0x7F, dtype=torch.uint8,
+                    device="cuda:0")  # contents on entry are ignored
+    out = host(bw.bw_attn_decode_kv3(f32_dev(q32), kp, vp, sl, ns, workspace=ws))
     assert np.isfinite(out).all()
     okp = kv3.kv_pack3(k16.f32, slot_of, ns)
     ovp = kv3.kv_pack3(v16.f32, slot_of, ns)
@@ -54,7 +61,9 @@ def check_attention(q32, k16, v16, slot_of, n_special, label, pairs=None):
         vd = kv3.kv_unpack3(*sub(ovp), so, D)[0, :, 0].astype(np.float64)
         qd = q32[b, h].astype(np.float64)
         z = kd @ qd / np.sqrt(D)
-        e_z = np.max(gamma(D) * (np.abs(kd) @ np.abs(qd)) / np.sqrt(D) + 4 * U * np.abs(z))
+        s_pos = np.abs(kd).max(axis=1) / 3.0 + 1e-30  # the position's scale (3-bit: max|k| = 3 s3)
+        fixed = 2.0**-31 * np.abs(qd).max() * np.abs(kd).sum(axis=1) + 2.0**-23 * np.abs(qd).max() * s_pos
+        e_z = np.max((gamma(D) * (np.abs(kd) @ np.abs(qd)) + fixed) / np.sqrt(D) + 4 * U * np.abs(z))
         e_p = 2 * e_z + gamma(S) + 2 * U
         mag = p[0, 0] @ np.abs(vd)  # [D]
         bound = (e_p + gamma(S) + 2 * U) * mag + 1e-30
@@ -73,7 +82,7 @@ def qkv(seed, B, S, H, D):
 
 
 @pytest.mark.parametrize("B,S,H,D", [(2, 100, 3, 128), (1, 130, 2, 64), (3, 257, 1, 128), (2, 1, 2, 128),
-                                     (1, 33, 4, 64)])
+                                     (1, 33, 4, 64), (2, 90, 40, 128), (1, 70, 70, 64), (4, 999, 5, 128)])
 def test_small_ragged(B, S, H, D):
     q, k, v, slot_of, ns = qkv(synth.SEED_BASE + 70 + S, B, S, H, D)
     check_attention(q, k, v, slot_of, ns, f"ragged {B}x{S}x{H}x{D}")
@@ -116,3 +125,13 @@ def test_longest_sequence():
     B, S, H, D = 1, 16384, 2, 64
     q, k, v, slot_of, ns = qkv(synth.SEED_BASE + 84, B, S, H, D)
     check_attention(q, k, v, slot_of, ns, "S=16384")
+
+
+def test_query_with_one_huge_entry():
+    """max|q| far above the rest: the fixed-point query's step (2^-30 max|q|) is the
+    largest error term, and the result must still meet the bound."""
+    B, S, H, D = 1, 200, 2, 128
+    q, k, v, slot_of, ns = qkv(synth.SEED_BASE + 85, B, S, H, D)
+    q = q.copy()
+    q[0, :, 5] = np.float32(3.0e4)
+    check_attention(q, k, v, slot_of, ns, "huge q entry")
