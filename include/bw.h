@@ -269,6 +269,44 @@ bw_status bw_attn_decode_kv3(const float* q, const uint8_t* k_p3, const float* k
                              int64_t S, int64_t H, int64_t D, float* out, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------ *
+ * One decoder layer for one new token per sequence (decode step).
+ * Source: BitNet a4.8 abstract (4-bit inputs of attention and FFN, sparsified
+ * 8-bit intermediate states, 3-bit KV cache); toshoseti review, «Метод»
+ * (INT4 for q/k/v/gate/up inputs, top-k 50 % for the out_proj input, ReLU^2
+ * gate for down_proj) and «Эксперименты» (bos/eos at 4 bits).  The pages give
+ * no layer formula; the composition, without normalization or rotary
+ * embedding (neither is described), is, with HD = H*D:
+ *   y_qkv = bitlinear_a4(quantize(x, INT4), W_qkv)            [B][3HD]
+ *   append k = y_qkv[:, HD:2HD], v = y_qkv[:, 2HD:3HD] at position pos of the
+ *          3-bit cache (the codec of bw_kv_pack3; the 4-bit slot if special)
+ *   a     = attention of q = y_qkv[:, 0:HD] over positions 0..pos (as
+ *           bw_attn_decode_kv3)
+ *   x1    = x + bitlinear_sparse_a8(quantize_sparse_a8(a, k_keep = HD/2), W_o)
+ *   g, u  = bitlinear_a4(quantize(x1, INT4), W_gate), (..., W_up)
+ *   x_out = x1 + bitlinear_sparse_a8(quantize_sparse_a8(g, up = u,
+ *           k_keep = F/2), W_down)
+ * with every intermediate in fp32 exactly as the separate calls produce it.
+ * x, x_out: fp32 [B][HD] (distinct buffers).  Weights packed by
+ * bw_pack_ternary: W_qkv [3HD][HD] and W_gate_up [2F][HD] (gate rows, then
+ * up rows) in the BW_ROLE_A4 layout; W_o [HD][HD] and W_down [HD][F] in
+ * BW_ROLE_A8; b_* the matching beta arrays.  Cache: k_/v_ p3, s3 [B][S_cap]
+ * [H][...] and p4, s4 [n_special][H][...] as bw_kv_pack3 writes them, with
+ * slot_of [B][S_cap]; position pos of every sequence is overwritten.
+ * workspace: >= bw_block_decode_workspace_bytes(B, S_cap, H, D, F) bytes;
+ * contents on entry are ignored.
+ * Shapes: 1 <= B <= 16, D = 64 or 128, HD % 64 == 0, HD <= 16384,
+ * F % 64 == 0, F <= 16384, 0 <= pos < S_cap.
+ * ------------------------------------------------------------------------ */
+/* host */ size_t bw_block_decode_workspace_bytes(int64_t B, int64_t S_cap, int64_t H, int64_t D, int64_t F);
+bw_status bw_block_decode(const float* x, float* x_out, int64_t B, int64_t H, int64_t D, int64_t F,
+                          const uint8_t* w_qkv, const float* b_qkv, const uint8_t* w_o, const float* b_o,
+                          const uint8_t* w_gate_up, const float* b_gate_up, const uint8_t* w_down,
+                          const float* b_down, uint8_t* k_p3, float* k_s3, uint8_t* k_p4, float* k_s4,
+                          uint8_t* v_p3, float* v_s3, uint8_t* v_p4, float* v_s4, const int32_t* slot_of,
+                          int64_t n_special, int64_t S_cap, int64_t pos, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

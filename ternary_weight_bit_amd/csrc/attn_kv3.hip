@@ -122,8 +122,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_chunk(
     const float* __restrict__ q, const uint8_t* __restrict__ kp3, const float* __restrict__ ks3,
     const uint8_t* __restrict__ kp4, const float* __restrict__ ks4, const uint8_t* __restrict__ vp3,
     const float* __restrict__ vs3, const uint8_t* __restrict__ vp4, const float* __restrict__ vs4,
-    const int32_t* __restrict__ slot_of, int64_t n_special, int64_t B, int64_t S, int64_t H, int CH, int nch,
-    float* __restrict__ part) {
+    const int32_t* __restrict__ slot_of, int64_t n_special, int64_t B, int64_t S, int64_t S_cap, int64_t H,
+    int64_t q_stride, int CH, int nch, float* __restrict__ part) {
   constexpr int G = D / 32;                   // 32-dim groups per vector
   constexpr int HS = kAttnThreads / (4 * G);  // heads per head block
   constexpr int VB = 3 * D / 8;               // plane bytes per vector
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_chunk(
   float* __restrict__ s_z = s_dyn;
   float* __restrict__ s_m = s_dyn + static_cast<int64_t>(CH) * HP;
   float* __restrict__ s_l = s_m + H;
-  const int32_t* __restrict__ slots = slot_of + b * S + p0;
+  const int32_t* __restrict__ slots = slot_of + b * S_cap + p0;
   const float inv_sqrt_d = 1.0f / sqrtf(static_cast<float>(D));
 
   // special positions of the chunk: bitmask by wave ballots, then an ordered list
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_chunk(
     const int64_t h = hb + hl;
     const bool hok = h < H;
     const int64_t hc = hok ? h : H - 1;
-    const float* __restrict__ qv = q + (b * H + hc) * D + 32 * g;
+    const float* __restrict__ qv = q + b * q_stride + hc * D + 32 * g;
     float qg[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) qg[i] = qv[i];
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_chunk(
 #pragma unroll
       for (int j = 0; j < kUnroll; ++j) {
         const int p = j0 + 4 * j;
-        const int64_t vec = (b * S + p0 + (p < np ? p : 0)) * H + hc;
+        const int64_t vec = (b * S_cap + p0 + (p < np ? p : 0)) * H + hc;
         const uint32_t* __restrict__ pw = reinterpret_cast<const uint32_t*>(kp3 + vec * VB) + 3 * g;
         dl[j][0] = pw[0];
         dl[j][1] = pw[1];
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_chunk(
 #pragma unroll
       for (int j = 0; j < kUnroll; ++j) {
         const int p = j0 + 4 * j;
-        const int64_t vec = (b * S + p0 + (p < np ? p : 0)) * H + hc;
+        const int64_t vec = (b * S_cap + p0 + (p < np ? p : 0)) * H + hc;
         const uint32_t* __restrict__ pw = reinterpret_cast<const uint32_t*>(vp3 + vec * VB) + 3 * g;
         dl[j][0] = pw[0];
         dl[j][1] = pw[1];
@@ -493,6 +493,15 @@ hipError_t launch_attn_decode3(const float* q, const uint8_t* kp3, const float* 
                                const float* ks4, const uint8_t* vp3, const float* vs3, const uint8_t* vp4,
                                const float* vs4, const int32_t* slot_of, int64_t n_special, int64_t B, int64_t S,
                                int64_t H, int64_t D, float* out, void* ws, hipStream_t s) {
+  return launch_attn_decode3_strided(q, H * D, kp3, ks3, kp4, ks4, vp3, vs3, vp4, vs4, slot_of, n_special, B, S, S, H,
+                                     D, out, ws, s);
+}
+
+hipError_t launch_attn_decode3_strided(const float* q, int64_t q_stride, const uint8_t* kp3, const float* ks3,
+                                       const uint8_t* kp4, const float* ks4, const uint8_t* vp3, const float* vs3,
+                                       const uint8_t* vp4, const float* vs4, const int32_t* slot_of,
+                                       int64_t n_special, int64_t B, int64_t S, int64_t S_cap, int64_t H, int64_t D,
+                                       float* out, void* ws, hipStream_t s) {
   const AttnGrid g = attn_grid(B, S, H);
   float* part = static_cast<float*>(ws);
   const dim3 grid1(static_cast<unsigned>(g.nch * B));
@@ -500,11 +509,11 @@ hipError_t launch_attn_decode3(const float* q, const uint8_t* kp3, const float* 
   const dim3 grid2(static_cast<unsigned>(B * H));
   if (D == 64) {
     hipLaunchKernelGGL(k_attn_chunk<64>, grid1, dim3(kAttnThreads), lds, s, q, kp3, ks3, kp4, ks4, vp3, vs3, vp4, vs4,
-                       slot_of, n_special, B, S, H, g.ch, g.nch, part);
+                       slot_of, n_special, B, S, S_cap, H, q_stride, g.ch, g.nch, part);
     hipLaunchKernelGGL(k_attn_merge<64>, grid2, dim3(64), 0, s, part, B, H, g.nch, out);
   } else {
     hipLaunchKernelGGL(k_attn_chunk<128>, grid1, dim3(kAttnThreads), lds, s, q, kp3, ks3, kp4, ks4, vp3, vs3, vp4,
-                       vs4, slot_of, n_special, B, S, H, g.ch, g.nch, part);
+                       vs4, slot_of, n_special, B, S, S_cap, H, q_stride, g.ch, g.nch, part);
     hipLaunchKernelGGL(k_attn_merge<128>, grid2, dim3(128), 0, s, part, B, H, g.nch, out);
   }
   return hipGetLastError();

@@ -1,0 +1,230 @@
+// One BitNet a4.8 decoder layer for a single new token per sequence, chained
+// from the library's kernels on one stream.
+//
+// BitNet a4.8 abstract: 4-bit activations (INT4/FP4) for the inputs of the
+// attention and feed-forward layers, sparsified then 8-bit intermediate
+// states, 3-bit KV cache; toshoseti review, «Метод»: 4 bits for the q/k/v and
+// gate/up inputs, top-k (50 %) for the out_proj input, ReLU^2 gate for the
+// down_proj input; «Эксперименты»: bos/eos kept at 4 bits in the KV cache.
+// The pages give no layer formula; the plainest composition is used, with no
+// normalization and no rotary embedding (neither is described):
+//   c, s   = INT4(x)                         y_qkv = W_qkv (c, s)
+//   append k = y_qkv[HD:2HD], v = y_qkv[2HD:3HD] at position pos (3-bit codes)
+//   a      = attention(q = y_qkv[0:HD], cache positions 0..pos)
+//   x1     = x + W_o SparseA8(a, top-k HD/2)
+//   c, s   = INT4(x1)                        g = W_gate (c, s), u = W_up (c, s)
+//   x_out  = x1 + W_down SparseA8(relu(g)^2 * u, top-k F/2)
+// Launches: quantizer, q/k/v GEMV, KV append, attention (2), top-k INT8,
+// out_proj GEMV, add, quantizer, gate GEMV, up GEMV, ReLU^2 top-k INT8,
+// down GEMV, add.
+#include "bw_internal.h"
+
+namespace bw {
+namespace {
+
+constexpr int kAppendThreads = 256;  // four waves, one (batch, head) vector each
+
+__device__ __forceinline__ float wave_absmax(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Write the 3-bit codes (and, at a special position, the 4-bit slot) of the
+// new token's K and V vectors at position pos, exactly as the cache packer
+// defines them: a' = max(max|v|, 1e-5); 3-bit q = clamp(rne(fl(v * fl(3/a'))),
+// -4, 3) with s3 = fl(a'/3), stored as three bit planes per 32 codes; 4-bit
+// q = clamp(rne(fl(v * fl(7/a'))), -8, 7) with s4 = fl(a'/7), even d in the
+// low nibble.  blockIdx.y selects K (0) or V (1).
+template <int D>
+__global__ __launch_bounds__(kAppendThreads) void k_kv_append3(
+    const float* __restrict__ y_qkv, int64_t row_stride, int64_t B, int64_t H, int64_t pos, int64_t S_cap,
+    const int32_t* __restrict__ slot_of, int64_t n_special, uint8_t* __restrict__ kp3, float* __restrict__ ks3,
+    uint8_t* __restrict__ kp4, float* __restrict__ ks4, uint8_t* __restrict__ vp3, float* __restrict__ vs3,
+    uint8_t* __restrict__ vp4, float* __restrict__ vs4) {
+  constexpr int NV = D / 64;  // values per lane
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * (kAppendThreads / 64) + (threadIdx.x >> 6);
+  if (wid >= B * H) return;  // whole wave leaves together
+  const bool is_v = blockIdx.y == 1;
+  const int64_t b = wid / H;
+  const int64_t h = wid - b * H;
+  const int64_t hd = H * D;
+  const float* __restrict__ src = y_qkv + b * row_stride + (is_v ? 2 * hd : hd) + h * D;
+  uint8_t* __restrict__ p3 = is_v ? vp3 : kp3;
+  float* __restrict__ s3 = is_v ? vs3 : ks3;
+  uint8_t* __restrict__ p4 = is_v ? vp4 : kp4;
+  float* __restrict__ s4 = is_v ? vs4 : ks4;
+
+  float x[NV];
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    x[i] = src[lane + 64 * i];
+    a = fmaxf(a, fabsf(x[i]));
+  }
+  const float ap = fmaxf(wave_absmax(a), 1e-5f);
+  const int64_t vec = (b * S_cap + pos) * H + h;
+
+  // 3-bit codes; plane j of the 32 codes of group g is a ballot of bit j
+  const float inv3 = 3.0f / ap;
+  uint32_t planes[2 * NV][3];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int q = static_cast<int>(fminf(fmaxf(rintf(__fmul_rn(x[i], inv3)), -4.0f), 3.0f));
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const uint64_t bal = __ballot((q >> j) & 1);
+      planes[2 * i][j] = static_cast<uint32_t>(bal);
+      planes[2 * i + 1][j] = static_cast<uint32_t>(bal >> 32);
+    }
+  }
+  if (lane < 3 * 2 * NV) {
+    const int g = lane / 3, j = lane % 3;  // dword 3g + j of the vector
+    uint32_t w = 0;
+#pragma unroll
+    for (int gg = 0; gg < 2 * NV; ++gg)
+#pragma unroll
+      for (int jj = 0; jj < 3; ++jj)
+        if (gg == g && jj == j) w = planes[gg][jj];
+    reinterpret_cast<uint32_t*>(p3 + vec * (3 * D / 8))[lane] = w;
+  }
+  if (lane == 0) s3[vec] = ap / 3.0f;
+
+  // 4-bit slot of a special position
+  const int32_t slot = slot_of[b * S_cap + pos];
+  if (slot >= 0 && slot < n_special) {
+    const float inv7 = 7.0f / ap;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int q = static_cast<int>(fminf(fmaxf(rintf(__fmul_rn(x[i], inv7)), -8.0f), 7.0f));
+      const uint32_t nib = static_cast<uint32_t>(q) & 0xFu;
+      const uint32_t hi = static_cast<uint32_t>(__shfl_down(static_cast<int>(nib), 1));
+      if ((lane & 1) == 0) p4[(static_cast<int64_t>(slot) * H + h) * (D / 2) + (lane >> 1) + 32 * i] =
+          static_cast<uint8_t>(nib | (hi << 4));
+    }
+    if (lane == 0) s4[static_cast<int64_t>(slot) * H + h] = ap / 7.0f;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_add(const float4* __restrict__ a, const float4* __restrict__ b,
+                                             float4* __restrict__ o, int64_t n4) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n4) {
+    const float4 x = a[i], y = b[i];
+    o[i] = make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
+  }
+}
+
+hipError_t launch_add(const float* a, const float* b, float* o, int64_t n, hipStream_t s) {
+  const int64_t n4 = n / 4;
+  hipLaunchKernelGGL(k_add, dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const float4*>(a), reinterpret_cast<const float4*>(b),
+                     reinterpret_cast<float4*>(o), n4);
+  return hipGetLastError();
+}
+
+// Attention workspace for any attended length in [1, S_cap]: the chunk count
+// is at most max(count at S_cap, 256 / B + 2) (chunks hold about S * B / 256
+// positions until a cap binds, which only happens at the largest lengths).
+size_t attn_ws_bound(int64_t B, int64_t S_cap, int64_t H, int64_t D) {
+  const size_t at_cap = attn_decode3_workspace_bytes(B, S_cap, H, D);
+  const size_t small = static_cast<size_t>(B) * H * (D + 4) * sizeof(float) * static_cast<size_t>(256 / B + 2);
+  return at_cap > small ? at_cap : small;
+}
+
+struct BlockWs {
+  uint8_t* c4;
+  float* sx4;
+  float* y_qkv;
+  float* att;
+  void* attn_ws;
+  int8_t* c8;
+  float* s8;
+  float* y_o;
+  float* x1;
+  float* y_g;
+  float* y_u;
+  int8_t* c8d;
+  float* s8d;
+  float* y_d;
+  size_t bytes;
+};
+
+BlockWs block_ws(void* base, int64_t B, int64_t S_cap, int64_t H, int64_t D, int64_t F) {
+  const int64_t hd = H * D;
+  uint8_t* p = static_cast<uint8_t*>(base);
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    uint8_t* r = p ? p + off : nullptr;
+    off += (n + 255) & ~static_cast<size_t>(255);
+    return r;
+  };
+  BlockWs w;
+  w.c4 = take(static_cast<size_t>(B) * hd / 2);
+  w.sx4 = reinterpret_cast<float*>(take(4 * B));
+  w.y_qkv = reinterpret_cast<float*>(take(4 * static_cast<size_t>(B) * 3 * hd));
+  w.att = reinterpret_cast<float*>(take(4 * static_cast<size_t>(B) * hd));
+  w.attn_ws = take(attn_ws_bound(B, S_cap, H, D));
+  w.c8 = reinterpret_cast<int8_t*>(take(static_cast<size_t>(B) * hd));
+  w.s8 = reinterpret_cast<float*>(take(4 * B));
+  w.y_o = reinterpret_cast<float*>(take(4 * static_cast<size_t>(B) * hd));
+  w.x1 = reinterpret_cast<float*>(take(4 * static_cast<size_t>(B) * hd));
+  w.y_g = reinterpret_cast<float*>(take(4 * static_cast<size_t>(B) * F));
+  w.y_u = reinterpret_cast<float*>(take(4 * static_cast<size_t>(B) * F));
+  w.c8d = reinterpret_cast<int8_t*>(take(static_cast<size_t>(B) * F));
+  w.s8d = reinterpret_cast<float*>(take(4 * B));
+  w.y_d = reinterpret_cast<float*>(take(4 * static_cast<size_t>(B) * hd));
+  w.bytes = off;
+  return w;
+}
+
+#define BW_TRY(expr)                  \
+  do {                                \
+    const hipError_t e_ = (expr);     \
+    if (e_ != hipSuccess) return e_;  \
+  } while (0)
+
+}  // namespace
+
+size_t block_decode_workspace_bytes(int64_t B, int64_t S_cap, int64_t H, int64_t D, int64_t F) {
+  return block_ws(nullptr, B, S_cap, H, D, F).bytes;
+}
+
+hipError_t launch_block_decode(const float* x, float* x_out, int64_t B, int64_t H, int64_t D, int64_t F,
+                               const uint8_t* w_qkv, const float* b_qkv, const uint8_t* w_o, const float* b_o,
+                               const uint8_t* w_gu, const float* b_gu, const uint8_t* w_down, const float* b_down,
+                               uint8_t* kp3, float* ks3, uint8_t* kp4, float* ks4, uint8_t* vp3, float* vs3,
+                               uint8_t* vp4, float* vs4, const int32_t* slot_of, int64_t n_special, int64_t S_cap,
+                               int64_t pos, void* ws, hipStream_t s) {
+  const int64_t hd = H * D;
+  const BlockWs w = block_ws(ws, B, S_cap, H, D, F);
+  // attention input side: q/k/v projection and KV append
+  BW_TRY(launch_quantize_act4(x, false, B, hd, 0, w.c4, w.sx4, s));
+  BW_TRY(launch_bitlinear(0, w.c4, w.sx4, B, hd, w_qkv, b_qkv, 3 * hd, w.y_qkv, nullptr, s));
+  const dim3 agrid(static_cast<unsigned>((B * H + kAppendThreads / 64 - 1) / (kAppendThreads / 64)), 2);
+  if (D == 64) {
+    hipLaunchKernelGGL(k_kv_append3<64>, agrid, dim3(kAppendThreads), 0, s, w.y_qkv, 3 * hd, B, H, pos, S_cap,
+                       slot_of, n_special, kp3, ks3, kp4, ks4, vp3, vs3, vp4, vs4);
+  } else {
+    hipLaunchKernelGGL(k_kv_append3<128>, agrid, dim3(kAppendThreads), 0, s, w.y_qkv, 3 * hd, B, H, pos, S_cap,
+                       slot_of, n_special, kp3, ks3, kp4, ks4, vp3, vs3, vp4, vs4);
+  }
+  BW_TRY(hipGetLastError());
+  BW_TRY(launch_attn_decode3_strided(w.y_qkv, 3 * hd, kp3, ks3, kp4, ks4, vp3, vs3, vp4, vs4, slot_of, n_special,
+                                     B, pos + 1, S_cap, H, D, w.att, w.attn_ws, s));
+  // out_proj on the top-k 50 % INT8 codes, residual
+  BW_TRY(launch_sparse_a8(w.att, nullptr, false, B, hd, hd / 2, w.c8, w.s8, nullptr, s));
+  BW_TRY(launch_bitlinear(2, w.c8, w.s8, B, hd, w_o, b_o, hd, w.y_o, nullptr, s));
+  BW_TRY(launch_add(x, w.y_o, w.x1, B * hd, s));
+  // feed-forward: gate and up on INT4 codes, ReLU^2 * up top-k 50 % INT8, down_proj, residual
+  BW_TRY(launch_quantize_act4(w.x1, false, B, hd, 0, w.c4, w.sx4, s));
+  BW_TRY(launch_bitlinear(0, w.c4, w.sx4, B, hd, w_gu, b_gu, F, w.y_g, nullptr, s));
+  BW_TRY(launch_bitlinear(0, w.c4, w.sx4, B, hd, w_gu + F * hd / 4, b_gu + F, F, w.y_u, nullptr, s));
+  BW_TRY(launch_sparse_a8(w.y_g, w.y_u, false, B, F, F / 2, w.c8d, w.s8d, nullptr, s));
+  BW_TRY(launch_bitlinear(2, w.c8d, w.s8d, B, F, w_down, b_down, hd, w.y_d, nullptr, s));
+  BW_TRY(launch_add(w.x1, w.y_d, x_out, B * hd, s));
+  return hipSuccess;
+}
+
+}  // namespace bw

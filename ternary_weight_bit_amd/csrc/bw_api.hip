@@ -251,4 +251,47 @@ bw_status bw_attn_decode_kv3(const float* q, const uint8_t* k_p3, const float* k
                     "bw_attn_decode_kv3");
 }
 
+static bool block_shape_ok(int64_t B, int64_t S_cap, int64_t H, int64_t D, int64_t F) {
+  const int64_t hd = H * D;
+  return B >= 1 && B <= bw::kGemvMaxM && H >= 1 && H <= bw::kAttnMaxH && (D == 64 || D == 128) && hd % 64 == 0 &&
+         hd <= kMaxKSparse && F >= 64 && F % 64 == 0 && F <= kMaxKSparse && S_cap >= 1 &&
+         B <= (int64_t(1) << 40) / S_cap / hd && bw::attn_decode3_supported(B, S_cap, H);
+}
+
+size_t bw_block_decode_workspace_bytes(int64_t B, int64_t S_cap, int64_t H, int64_t D, int64_t F) {
+  if (!block_shape_ok(B, S_cap, H, D, F)) return 0;
+  return bw::block_decode_workspace_bytes(B, S_cap, H, D, F);
+}
+
+bw_status bw_block_decode(const float* x, float* x_out, int64_t B, int64_t H, int64_t D, int64_t F,
+                          const uint8_t* w_qkv, const float* b_qkv, const uint8_t* w_o, const float* b_o,
+                          const uint8_t* w_gate_up, const float* b_gate_up, const uint8_t* w_down,
+                          const float* b_down, uint8_t* k_p3, float* k_s3, uint8_t* k_p4, float* k_s4,
+                          uint8_t* v_p3, float* v_s3, uint8_t* v_p4, float* v_s4, const int32_t* slot_of,
+                          int64_t n_special, int64_t S_cap, int64_t pos, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  BW_REQUIRE(block_shape_ok(B, S_cap, H, D, F), BW_ERR_SHAPE,
+             "bw_block_decode: need 1 <= B <= %lld, D = 64 or 128, H*D %% 64 == 0 and <= %lld, F %% 64 == 0 and "
+             "<= %lld, S_cap within the attention limits (B=%lld H=%lld D=%lld F=%lld S_cap=%lld)",
+             (long long)bw::kGemvMaxM, (long long)kMaxKSparse, (long long)kMaxKSparse, (long long)B, (long long)H,
+             (long long)D, (long long)F, (long long)S_cap);
+  BW_REQUIRE(pos >= 0 && pos < S_cap && n_special >= 0, BW_ERR_ARG,
+             "bw_block_decode: need 0 <= pos < S_cap and n_special >= 0 (pos=%lld)", (long long)pos);
+  BW_REQUIRE(x && x_out && w_qkv && b_qkv && w_o && b_o && w_gate_up && b_gate_up && w_down && b_down && k_p3 &&
+                 k_s3 && v_p3 && v_s3 && slot_of && workspace,
+             BW_ERR_NULL, "bw_block_decode: NULL pointer");
+  BW_REQUIRE(n_special == 0 || (k_p4 && k_s4 && v_p4 && v_s4), BW_ERR_NULL,
+             "bw_block_decode: 4-bit slabs required when n_special > 0");
+  const void* ptrs[] = {x, x_out, w_qkv, b_qkv, w_o, b_o, w_gate_up, b_gate_up, w_down, b_down, k_p3, k_s3, k_p4,
+                        k_s4, v_p3, v_s3, v_p4, v_s4, slot_of, workspace};
+  for (const void* p : ptrs) BW_REQUIRE(!misaligned(p), BW_ERR_ALIGN, "bw_block_decode: device pointers must be 16-byte aligned");
+  const size_t need = bw::block_decode_workspace_bytes(B, S_cap, H, D, F);
+  BW_REQUIRE(workspace_bytes >= need, BW_ERR_ARG, "bw_block_decode: workspace needs %zu bytes, got %zu", need,
+             workspace_bytes);
+  return hip_status(bw::launch_block_decode(x, x_out, B, H, D, F, w_qkv, b_qkv, w_o, b_o, w_gate_up, b_gate_up, w_down,
+                                            b_down, k_p3, k_s3, k_p4, k_s4, v_p3, v_s3, v_p4, v_s4, slot_of,
+                                            n_special, S_cap, pos, workspace, static_cast<hipStream_t>(stream)),
+                    "bw_block_decode");
+}
+
 }  // extern "C"

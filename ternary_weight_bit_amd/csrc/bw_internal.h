@@ -59,6 +59,22 @@ hipError_t launch_attn_decode3(const float* q, const uint8_t* kp3, const float* 
                                const float* ks4, const uint8_t* vp3, const float* vs3, const uint8_t* vp4,
                                const float* vs4, const int32_t* slot_of, int64_t n_special, int64_t B, int64_t S,
                                int64_t H, int64_t D, float* out, void* ws, hipStream_t s);
+// Same, attending over positions [0, S) of a cache allocated with S_cap
+// positions per sequence, q rows q_stride floats apart.
+hipError_t launch_attn_decode3_strided(const float* q, int64_t q_stride, const uint8_t* kp3, const float* ks3,
+                                       const uint8_t* kp4, const float* ks4, const uint8_t* vp3, const float* vs3,
+                                       const uint8_t* vp4, const float* vs4, const int32_t* slot_of,
+                                       int64_t n_special, int64_t B, int64_t S, int64_t S_cap, int64_t H, int64_t D,
+                                       float* out, void* ws, hipStream_t s);
+
+// One decoder layer for one new token per sequence (block.hip).
+size_t block_decode_workspace_bytes(int64_t B, int64_t S_cap, int64_t H, int64_t D, int64_t F);
+hipError_t launch_block_decode(const float* x, float* x_out, int64_t B, int64_t H, int64_t D, int64_t F,
+                               const uint8_t* w_qkv, const float* b_qkv, const uint8_t* w_o, const float* b_o,
+                               const uint8_t* w_gu, const float* b_gu, const uint8_t* w_down, const float* b_down,
+                               uint8_t* kp3, float* ks3, uint8_t* kp4, float* ks4, uint8_t* vp3, float* vs3,
+                               uint8_t* vp4, float* vs4, const int32_t* slot_of, int64_t n_special, int64_t S_cap,
+                               int64_t pos, void* ws, hipStream_t s);
 
 hipError_t launch_kv_pack3(const void* kv, bool bf16, int64_t B, int64_t S, int64_t H, int64_t D,
                            const int32_t* slot_of, int64_t n_special, uint8_t* p3, float* s3,

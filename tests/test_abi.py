@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -134,3 +134,20 @@ def test_attn_validation():
     assert f(*args(8, 4096, 32, 128, out=MIS)) == 3
     assert f(*args(8, 4096, 32, 128, wb=ws - 1)) == 5
     assert f(*args(0, 4096, 32, 128, q=None, out=None, w=None)) == 0  # empty batch
+
+
+def test_block_validation():
+    ws = bw.bw_block_decode_workspace_bytes(8, 4096, 32, 128, 11008)
+    assert ws > 0 and bw.bw_block_decode_workspace_bytes(17, 4096, 32, 128, 11008) == 0
+    f = lib.bw_block_decode
+
+    def args(B=8, H=32, D=128, F=11008, S_cap=4096, pos=100, x=A, w=A, nsp=0, k4=None):
+        return (x, A, B, H, D, F) + (A,) * 8 + (A, A, k4, k4, A, A, k4, k4) + (A, nsp, S_cap, pos, w, ws, None)
+
+    assert f(*args(B=17)) == 2
+    assert f(*args(D=96)) == 2
+    assert f(*args(F=11000)) == 2
+    assert f(*args(pos=4096)) == 5
+    assert f(*args(x=None)) == 1
+    assert f(*args(nsp=3)) == 1  # side slabs missing
+    assert f(*args(w=MIS)) == 3
