@@ -16,6 +16,8 @@ that are resident in HBM before timing starts:
                                      32 layers each
   KV cache, one layer (8x4096x32x128): 3-bit pack of K and V, unpack of both to bf16,
                                      single-token attention over the packed K and V
+  decoder layer, one new token for each of 8 sequences over that cache: the whole
+                                     chain (bw_block_decode) over 32 layers of weights
   weights:                           absmean ternary pack of one 4096x4096 fp32 tensor
 
 Each decode row's 32-64 launches are recorded once into a HIP graph; the other
@@ -220,6 +222,32 @@ class Bench:
         # single-token attention over that layer's packed K (kvp[0]) and V (kvp[1])
         self.q_att = f32(synth.normal(S + 6, (B_, H_, D_)))
         self.att_out = t.empty((B_, H_, D_), dtype=t.float32, device=dev)
+        # ---------------- one decoder layer per new token (8 sequences, 4096 cached positions):
+        # 32 layers of weights (copies of one layer's packed bytes) and of the KV cache
+        HD = H_ * D_
+
+        def pack_parts(shapes, role, seed0):
+            N = sum(n for n, _ in shapes)
+            K = shapes[0][1]
+            wp = t.empty(N * K // 4, dtype=t.uint8, device=dev)
+            bp = t.empty(N, dtype=t.float32, device=dev)
+            off = 0
+            for i, (n, k) in enumerate(shapes):
+                bw.bw_pack_ternary(f32(synth.weight_tensor(seed0 + i, n, k)), role,
+                                   wp[off * K // 4 : (off + n) * K // 4], bp[off : off + n])
+                off += n
+            return wp, bp
+
+        lw = (*pack_parts([(HD, HD)] * 3, bw.BW_ROLE_A4, S + 40), *pack_parts([(HD, HD)], bw.BW_ROLE_A8, S + 43),
+              *pack_parts([(FFN, HD)] * 2, bw.BW_ROLE_A4, S + 44), *pack_parts([(HD, FFN)], bw.BW_ROLE_A8, S + 46))
+        self.blk_pos = S_ - 1
+        self.blk_x = f32(synth.normal(S + 47, (B_, HD)))
+        self.blk_out = t.empty((B_, HD), dtype=t.float32, device=dev)
+        self.blk_ws = t.empty(bw.bw_block_decode_workspace_bytes(B_, S_, H_, D_, FFN), dtype=t.uint8, device=dev)
+        self.blk_layers = [(tuple(w.clone() for w in lw), tuple(a.clone() for a in self.kvp[0]),
+                            tuple(a.clone() for a in self.kvp[1])) for _ in range(LAYERS)]
+        self.blk_weight_bytes = sum(w.numel() * w.element_size() for w in lw)
+        del lw
         # ---------------- weight packing (offline row): one 4096x4096 fp32 tensor
         self.pk = t.empty(HIDDEN * HIDDEN // 4, dtype=t.uint8, device=dev)
         self.pk_b = t.empty(HIDDEN, dtype=t.float32, device=dev)
@@ -330,6 +358,15 @@ class Bench:
         R.append(("k11_attn_decode_kv3", "GB/s", att_bytes,
                   [lambda: bw.bw_attn_decode_kv3(self.q_att, self.kvp[0], self.kvp[1], self.slot_of, self.n_special,
                                                  self.att_out)]))
+        # one decoder layer per new token: algorithmic bytes = the layer's packed weights and
+        # beta + the attended cache (as the attention row) + small activations
+        blk_bytes = self.blk_weight_bytes + att_bytes
+        R.append(("_evict_cache_blk", None, 0, [lambda: self.evict.fill_(6.0)]))
+        R.append(("k12_block_decode_b8", "GB/s", blk_bytes,
+                  [lambda lw=lw, kc=kc, vc=vc: bw.bw_block_decode(self.blk_x, lw, kc, vc, self.slot_of, self.n_special,
+                                                                  self.blk_pos, H_, x_out=self.blk_out,
+                                                                  workspace=self.blk_ws)
+                   for lw, kc, vc in self.blk_layers]))
         R.append(("a3_pack_ternary_4096x4096", "GB/s", HIDDEN * HIDDEN * 4 + HIDDEN * HIDDEN / 4 + 4 * HIDDEN,
                   [lambda: bw.bw_pack_ternary(self.w_q, bw.BW_ROLE_A4, self.pk, self.pk_b, self.pk_ws)]))
         return R
@@ -519,6 +556,12 @@ def main():
     if gemv:
         dec_bytes = sum(table[n]["amount_per_launch"] * table[n]["launches_per_step"] for n in gemv)
         decode_gbs = dec_bytes / (row_ms(gemv) * 1e-3) / 1e9
+    block = None
+    if "k12_block_decode_b8" in table:
+        block = {"us_per_layer": table["k12_block_decode_b8"]["avg_us"],
+                 "basis": "one decoder layer for one new token of each of 8 sequences with 4096 cached positions "
+                          "(INT4 q/k/v, 3-bit KV append and attention, top-k INT8 out_proj, INT4 gate/up, "
+                          "ReLU^2 top-k INT8 down_proj, residuals), averaged over 32 layers of weights and caches"}
     gather = {}
     for name, o in b.one.items():
         rt, rg = f"a9_gemv_a8_{name}_m1", f"k10_gather_a8_{name}_m1"
@@ -565,6 +608,7 @@ def main():
             "basis": "same ops / time of INT8 absmax (all entries, no top-k) + both W1.58A8 GEMMs, back to back (row b0)",
             "a48_over_b158": None if value is None else round(value / b158, 3)},
         "gather_decode_m1": gather or None,
+        "block_decode": block,
         "decode_gbs": None if decode_gbs is None else round(decode_gbs, 1),
         "decode_frac_hbm": None if decode_gbs is None else round(decode_gbs / HBM_PEAK_GBS, 4),
         "roofline": roof,
