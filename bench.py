@@ -470,14 +470,18 @@ def cpu_baseline(target_s: float):
     while dt < target_s / 4 and rows < M_PREFILL:
         rows = min(M_PREFILL, rows * 4)
         dt = run(rows)
-    ops = 2.0 * rows * HIDDEN * (FFN + HIDDEN)
+    # the whole workload finishes well under the target: repeat it to about target_s
+    reps = max(1, min(64, int(target_s / max(dt, 1e-3))))
+    if reps > 1:
+        dt = sum(run(rows) for _ in range(reps))
+    ops = 2.0 * rows * HIDDEN * (FFN + HIDDEN) * reps
     return {
         "value": ops / dt / 1e12,
         "unit": "TOPS",
         "cores": int(cores),
         "kind": "oracle",
         "sample": f"W1.58A4 prefill (INT4 quantize + exact contraction + epilogue) on {rows} of 2048 token rows, "
-                  f"K=4096, N=11008 and N=4096; {dt:.1f} s",
+                  f"K=4096, N=11008 and N=4096, {reps} passes; {dt:.1f} s",
     }
 
 
