@@ -15,8 +15,9 @@
 //   c, s   = INT4(x1)                        g = W_gate (c, s), u = W_up (c, s)
 //   x_out  = x1 + W_down SparseA8(relu(g)^2 * u, top-k F/2)
 // Launches: quantizer, q/k/v GEMV, KV append, attention (2), top-k INT8,
-// out_proj GEMV, add, quantizer, gate GEMV, up GEMV, ReLU^2 top-k INT8,
-// down GEMV, add.
+// out_proj GEMV with the residual added in its epilogue, quantizer, one
+// gate/up GEMV writing g and u as two [B][F] arrays, ReLU^2 top-k INT8, down
+// GEMV with the residual added in its epilogue.
 #include "bw_internal.h"
 
 namespace bw {
@@ -107,23 +108,6 @@ __global__ __launch_bounds__(kAppendThreads) void k_kv_append3(
   }
 }
 
-__global__ __launch_bounds__(256) void k_add(const float4* __restrict__ a, const float4* __restrict__ b,
-                                             float4* __restrict__ o, int64_t n4) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i < n4) {
-    const float4 x = a[i], y = b[i];
-    o[i] = make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
-  }
-}
-
-hipError_t launch_add(const float* a, const float* b, float* o, int64_t n, hipStream_t s) {
-  const int64_t n4 = n / 4;
-  hipLaunchKernelGGL(k_add, dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, s,
-                     reinterpret_cast<const float4*>(a), reinterpret_cast<const float4*>(b),
-                     reinterpret_cast<float4*>(o), n4);
-  return hipGetLastError();
-}
-
 // Attention workspace for any attended length in [1, S_cap]: the chunk count
 // is at most max(count at S_cap, 256 / B + 2) (chunks hold about S * B / 256
 // positions until a cap binds, which only happens at the largest lengths).
@@ -141,13 +125,10 @@ struct BlockWs {
   void* attn_ws;
   int8_t* c8;
   float* s8;
-  float* y_o;
   float* x1;
-  float* y_g;
-  float* y_u;
+  float* y_gu;  // g [B][F], then u [B][F]
   int8_t* c8d;
   float* s8d;
-  float* y_d;
   size_t bytes;
 };
 
@@ -168,13 +149,10 @@ BlockWs block_ws(void* base, int64_t B, int64_t S_cap, int64_t H, int64_t D, int
   w.attn_ws = take(attn_ws_bound(B, S_cap, H, D));
   w.c8 = reinterpret_cast<int8_t*>(take(static_cast<size_t>(B) * hd));
   w.s8 = reinterpret_cast<float*>(take(4 * B));
-  w.y_o = reinterpret_cast<float*>(take(4 * static_cast<size_t>(B) * hd));
   w.x1 = reinterpret_cast<float*>(take(4 * static_cast<size_t>(B) * hd));
-  w.y_g = reinterpret_cast<float*>(take(4 * static_cast<size_t>(B) * F));
-  w.y_u = reinterpret_cast<float*>(take(4 * static_cast<size_t>(B) * F));
+  w.y_gu = reinterpret_cast<float*>(take(8 * static_cast<size_t>(B) * F));
   w.c8d = reinterpret_cast<int8_t*>(take(static_cast<size_t>(B) * F));
   w.s8d = reinterpret_cast<float*>(take(4 * B));
-  w.y_d = reinterpret_cast<float*>(take(4 * static_cast<size_t>(B) * hd));
   w.bytes = off;
   return w;
 }
@@ -215,15 +193,12 @@ hipError_t launch_block_decode(const float* x, float* x_out, int64_t B, int64_t 
                                      B, pos + 1, S_cap, H, D, w.att, w.attn_ws, s));
   // out_proj on the top-k 50 % INT8 codes, residual
   BW_TRY(launch_sparse_a8(w.att, nullptr, false, B, hd, hd / 2, w.c8, w.s8, nullptr, s));
-  BW_TRY(launch_bitlinear(2, w.c8, w.s8, B, hd, w_o, b_o, hd, w.y_o, nullptr, s));
-  BW_TRY(launch_add(x, w.y_o, w.x1, B * hd, s));
+  BW_TRY(launch_gemv_ex(2, w.c8, w.s8, B, hd, w_o, b_o, hd, w.x1, nullptr, x, hd, s));
   // feed-forward: gate and up on INT4 codes, ReLU^2 * up top-k 50 % INT8, down_proj, residual
   BW_TRY(launch_quantize_act4(w.x1, false, B, hd, 0, w.c4, w.sx4, s));
-  BW_TRY(launch_bitlinear(0, w.c4, w.sx4, B, hd, w_gu, b_gu, F, w.y_g, nullptr, s));
-  BW_TRY(launch_bitlinear(0, w.c4, w.sx4, B, hd, w_gu + F * hd / 4, b_gu + F, F, w.y_u, nullptr, s));
-  BW_TRY(launch_sparse_a8(w.y_g, w.y_u, false, B, F, F / 2, w.c8d, w.s8d, nullptr, s));
-  BW_TRY(launch_bitlinear(2, w.c8d, w.s8d, B, F, w_down, b_down, hd, w.y_d, nullptr, s));
-  BW_TRY(launch_add(w.x1, w.y_d, x_out, B * hd, s));
+  BW_TRY(launch_gemv_ex(0, w.c4, w.sx4, B, hd, w_gu, b_gu, 2 * F, w.y_gu, nullptr, nullptr, F, s));
+  BW_TRY(launch_sparse_a8(w.y_gu, w.y_gu + B * F, false, B, F, F / 2, w.c8d, w.s8d, nullptr, s));
+  BW_TRY(launch_gemv_ex(2, w.c8d, w.s8d, B, F, w_down, b_down, hd, x_out, nullptr, w.x1, hd, s));
   return hipSuccess;
 }
 

@@ -23,6 +23,12 @@ constexpr int64_t kGemvMaxM = 16;
 hipError_t launch_gemv(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
                        const uint8_t* w_packed, const float* beta, int64_t N, float* y, void* acc_dbg,
                        hipStream_t s);
+// GEMV with an optional residual (y[m][n] = resid[m][n] + product, resid in
+// the [M][N] layout) and column planes: column n goes to plane n / split, a
+// row-major [M][split] array at y + (n / split) * M * split (split = N: [M][N]).
+hipError_t launch_gemv_ex(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
+                          const uint8_t* w_packed, const float* beta, int64_t N, float* y, void* acc_dbg,
+                          const float* resid, int64_t split, hipStream_t s);
 hipError_t launch_gemm(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
                        const uint8_t* w_packed, const float* beta, int64_t N, float* y, void* acc_dbg,
                        hipStream_t s);

@@ -15,7 +15,10 @@
 //     (i8 16x16x64, or scaled f8f6f4 16x16x128 for e2m1); activations are read
 //     straight from L2-resident global memory;
 //   * the waves' partial int32/fp32 tiles are summed through LDS (exact) and
-//     the epilogue writes y for the M real rows.
+//     the epilogue writes y for the M real rows; optionally it adds a residual
+//     (y = r + W x, the decoder layer's skip connections) and splits the
+//     columns into row-major planes (a fused gate/up product written as two
+//     [M][F] arrays).
 #include "bw_internal.h"
 #include "bw_widen.h"
 
@@ -29,7 +32,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(const uint8_t* __restrict__
                                                    const float* __restrict__ sx, int M, int64_t K,
                                                    const uint8_t* __restrict__ Wp,
                                                    const float* __restrict__ beta, int64_t N,
-                                                   float* __restrict__ y, void* __restrict__ acc_dbg) {
+                                                   float* __restrict__ y, void* __restrict__ acc_dbg,
+                                                   const float* __restrict__ resid, int64_t split) {
   using acc_t = typename std::conditional<MODE == MODE_FP4, v4f, v4i>::type;
   __shared__ acc_t part[WAVES][64];
 
@@ -116,6 +120,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(const uint8_t* __restrict__
     s[0] += p[0]; s[1] += p[1]; s[2] += p[2]; s[3] += p[3];
   }
   const int64_t n = n_out;
+  // output plane of this column: columns [p*split, (p+1)*split) go to the
+  // row-major [M][split] plane p (split = N: the plain [M][N] layout)
+  const int64_t plane = n / split;
+  float* __restrict__ yp = y + plane * M * split;
+  const int64_t nc = n - plane * split;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int m = 4 * g + e;
@@ -129,18 +138,21 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv(const uint8_t* __restrict__
       if (acc_dbg) static_cast<int32_t*>(acc_dbg)[m * N + n] = a;
       accf = static_cast<float>(a);
     }
-    y[m * N + n] = dequant(accf, sxm[e], bn);
+    float o = dequant(accf, sxm[e], bn);
+    if (resid) o = o + resid[m * N + n];  // residual: one fp32 rounding
+    yp[m * split + nc] = o;
   }
 }
 
 template <int MODE>
 void launch_waves(int waves, const uint8_t* A, const float* sx, int m, int64_t K, const uint8_t* w,
-                  const float* beta, int64_t N, float* y, void* acc_dbg, hipStream_t s) {
+                  const float* beta, int64_t N, float* y, void* acc_dbg, const float* resid, int64_t split,
+                  hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(N / 16));
   if (waves == 8) {
-    hipLaunchKernelGGL((k_gemv<MODE, 8>), grid, dim3(512), 0, s, A, sx, m, K, w, beta, N, y, acc_dbg);
+    hipLaunchKernelGGL((k_gemv<MODE, 8>), grid, dim3(512), 0, s, A, sx, m, K, w, beta, N, y, acc_dbg, resid, split);
   } else {
-    hipLaunchKernelGGL((k_gemv<MODE, 4>), grid, dim3(256), 0, s, A, sx, m, K, w, beta, N, y, acc_dbg);
+    hipLaunchKernelGGL((k_gemv<MODE, 4>), grid, dim3(256), 0, s, A, sx, m, K, w, beta, N, y, acc_dbg, resid, split);
   }
 }
 
@@ -157,24 +169,30 @@ int gemv_waves(int64_t K, int64_t N) {
 
 }  // namespace
 
-hipError_t launch_gemv(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
-                       const uint8_t* w_packed, const float* beta, int64_t N, float* y, void* acc_dbg,
-                       hipStream_t s) {
+hipError_t launch_gemv_ex(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
+                          const uint8_t* w_packed, const float* beta, int64_t N, float* y, void* acc_dbg,
+                          const float* resid, int64_t split, hipStream_t s) {
   const uint8_t* A = static_cast<const uint8_t*>(codes);
   const int m = static_cast<int>(M);
   const int waves = gemv_waves(K, N);
   switch (mode) {
     case MODE_INT4:
-      launch_waves<MODE_INT4>(waves, A, sx, m, K, w_packed, beta, N, y, acc_dbg, s);
+      launch_waves<MODE_INT4>(waves, A, sx, m, K, w_packed, beta, N, y, acc_dbg, resid, split, s);
       break;
     case MODE_FP4:
-      launch_waves<MODE_FP4>(waves, A, sx, m, K, w_packed, beta, N, y, acc_dbg, s);
+      launch_waves<MODE_FP4>(waves, A, sx, m, K, w_packed, beta, N, y, acc_dbg, resid, split, s);
       break;
     default:
-      launch_waves<MODE_INT8>(waves, A, sx, m, K, w_packed, beta, N, y, acc_dbg, s);
+      launch_waves<MODE_INT8>(waves, A, sx, m, K, w_packed, beta, N, y, acc_dbg, resid, split, s);
       break;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemv(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
+                       const uint8_t* w_packed, const float* beta, int64_t N, float* y, void* acc_dbg,
+                       hipStream_t s) {
+  return launch_gemv_ex(mode, codes, sx, M, K, w_packed, beta, N, y, acc_dbg, nullptr, N, s);
 }
 
 }  // namespace bw

@@ -19,7 +19,8 @@
 // ballot per register slot, counted with mbcnt, chunk by chunk.  Codes are
 // written as 8-byte runs per lane.
 //
-// Longer rows (up to 16384) use one workgroup (256 threads) per row: entries
+// Up to 256 rows of at most 16384 entries: one workgroup of 16 waves per row
+// (below).  Longer rows (up to 16384) use one workgroup (256 threads) per row: entries
 // t + 256*r in registers, tau found by bisection over the magnitude bits with
 // one ballot + popcount per register and one barrier per step.
 #include "bw_device.h"
@@ -506,12 +507,316 @@ void k_sparse_a8_wave(const void* __restrict__ g,
   if (lane == 0) scales[m] = div_rn(a, 127.0f);
 }
 
+// ------------------------------------------------------ one workgroup per row
+// For few rows (single-token decode) one wave per row leaves the chip idle and
+// each row pays one wave's load and selection latency.  Here a row is spread
+// over 16 waves: wave w holds the 512-entry chunks w, w + 16, ... in the same
+// per-lane arrangement as the one-wave kernel (entries 512c + 8l + i).  The
+// radix passes share one LDS histogram (LDS atomics); wave 0 scans it and the
+// result goes to every wave through LDS.  Ties at tau are ranked in index
+// order with per-chunk counts exchanged through LDS and one ballot + mbcnt per
+// register slot inside a chunk.
+constexpr int kBlkThreads = 1024;
+constexpr int kBlkWaves = kBlkThreads / kWave;
+constexpr int kBlkList = 1024;  // capacity of the list of entries in the chosen first-pass bin
+constexpr int64_t kBlockRowsMax = 256;  // up to this many rows: one workgroup per row
+
+// Bin of hist[0, 64 * per) holding the need-th largest (bins scanned from the
+// top); returns the bin, the count in bins above it and its own count.
+// Called by one whole wave.
+__device__ __forceinline__ void find_bin_wave(const int* hist, int per, int need, int lane, int& bin,
+                                              int& cum, int& cnt_bin) {
+  int sum = 0;
+  for (int b = 0; b < per; b += 4) {
+    const int4 q = *reinterpret_cast<const int4*>(&hist[lane * per + b]);
+    sum += q.x + q.y + q.z + q.w;
+  }
+  const int incl = wave_incl_scan(sum, lane);
+  const int total = lane_value(incl, kWave - 1);
+  const int over_l = total - incl;
+  const int L = __ffsll(static_cast<long long>(__ballot(over_l < need && need <= over_l + sum))) - 1;
+  const int over = lane_value(over_l, L);
+  const int cnt = (lane < per) ? hist[L * per + per - 1 - lane] : 0;
+  const int run = wave_incl_scan(cnt, lane);
+  const int J = __ffsll(static_cast<long long>(__ballot(lane < per && over + run >= need))) - 1;
+  bin = L * per + per - 1 - J;
+  cum = over + lane_value(run - cnt, J);
+  cnt_bin = lane_value(cnt, J);
+}
+
+template <bool BF16, bool GATED, int CH>
+__global__ __launch_bounds__(kBlkThreads) void k_sparse_a8_block(const void* __restrict__ g,
+                                                                 const void* __restrict__ u, int K, int k_keep,
+                                                                 int8_t* __restrict__ codes,
+                                                                 float* __restrict__ scales,
+                                                                 uint32_t* __restrict__ mask) {
+  __shared__ __attribute__((aligned(16))) int hist[kHist];
+  __shared__ int list[kBlkList];
+  __shared__ uint32_t w_max[kBlkWaves];
+  __shared__ int w_nz[kBlkWaves];
+  __shared__ int sel[4];  // list fill, then (bin, count above, count in bin) of the last scan
+  __shared__ int tiecnt[kBlkWaves * CH];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int m = blockIdx.x;
+  const int64_t row = static_cast<int64_t>(m) * K;
+  constexpr int SW = (CH + 3) / 4;
+
+  // ---- |h| bits and sign bits of this lane's entries (same scheme as above)
+  uint32_t key[CH][8];
+  uint32_t sg[SW];
+#pragma unroll
+  for (int w = 0; w < SW; ++w) sg[w] = 0;
+  auto ent = [&](int c) { return 512 * (wave + kBlkWaves * c) + 8 * lane; };
+  auto put = [&](int c, int i, float v, bool ok) {
+    const uint32_t b = __float_as_uint(v);
+    key[c][i] = ok ? (b & 0x7FFFFFFFu) : 0u;
+    sg[c >> 2] |= (b >> 31) << (8 * (c & 3) + i);
+  };
+  {
+    float gv[CH][8], uv[CH][8];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int e = ent(c);
+      const int64_t off = row + ((e < K) ? e : 0);
+      load8<BF16>(g, off, gv[c]);
+      if constexpr (GATED) load8<BF16>(u, off, uv[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const bool ok = ent(c) < K;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float v = gv[c][i];
+        if constexpr (GATED) {
+          const float r = v > 0.0f ? v : 0.0f;
+          v = mul_rn(mul_rn(r, r), uv[c][i]);
+        }
+        put(c, i, v, ok);
+      }
+    }
+  }
+
+  // ---- clear the histogram; per-wave maximum and nonzero count
+  hist[tid] = 0;
+  hist[tid + kBlkThreads] = 0;
+  if (tid < kWave) hist[2 * kBlkThreads + tid] = 0;
+  if (tid == 0) sel[0] = 0;
+  {
+    uint32_t kmax = 0;
+    int nz = 0;
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        kmax = max(kmax, key[c][i]);
+        nz += static_cast<int>(min(key[c][i], 1u));
+      }
+    kmax = static_cast<uint32_t>(lane_value(static_cast<int>(wave_incl_umax(kmax)), kWave - 1));
+    nz = lane_value(wave_incl_scan(nz, lane), kWave - 1);
+    if (lane == 0) {
+      w_max[wave] = kmax;
+      w_nz[wave] = nz;
+    }
+  }
+  __syncthreads();
+
+  // ---- first radix pass (bits 30..20 of the nonzero magnitudes) by every wave
+  const uint32_t discard = static_cast<uint32_t>(kBins + lane);
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t k = key[c][i];
+      const uint32_t nzf = 1u - ((k - 1u) >> 31);
+      atomicAdd(&hist[discard + nzf * ((k >> 20) - discard)], 1);
+    }
+  __syncthreads();
+  uint32_t kmax = 0;
+  int nnz = 0;
+#pragma unroll
+  for (int w = 0; w < kBlkWaves; ++w) {
+    kmax = max(kmax, w_max[w]);
+    nnz += w_nz[w];
+  }
+  const float amax = __uint_as_float(kmax);
+
+  uint32_t tau = 0;
+  int n_gt = nnz;
+  int n_eq = K - nnz;
+  if (nnz >= k_keep && k_keep < K) {  // uniform over the workgroup
+    int need = k_keep;
+    int above = 0;
+    if (wave == 0) {
+      int bin, cum, cnt;
+      find_bin_wave(hist, kBins / kWave, need, lane, bin, cum, cnt);
+      if (lane == 0) {
+        sel[1] = bin;
+        sel[2] = cum;
+        sel[3] = cnt;
+      }
+    }
+    __syncthreads();
+    const int bin1 = sel[1];
+    const int cum1 = sel[2];
+    const int c1 = sel[3];
+    need -= cum1;
+    above += cum1;
+    uint32_t prefix = static_cast<uint32_t>(bin1) << 20;
+    // entries of the chosen bin -> list[0, c1) when they fit
+    const bool gathered = c1 <= kBlkList;
+    if (gathered) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t k = key[c][i];
+          const bool f = k != 0u && (k >> 20) == static_cast<uint32_t>(bin1);
+          const uint64_t bm = __ballot(f);
+          if (bm != 0) {  // wave-uniform
+            int base = 0;
+            if (lane == 0) base = atomicAdd(&sel[0], __popcll(bm));
+            base = __shfl(base, 0, kWave);
+            const int pos = base + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                       static_cast<uint32_t>(bm >> 32),
+                                       __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bm), 0u)));
+            if (f) list[pos] = static_cast<int>(k);
+          }
+        }
+    }
+    // passes 2 and 3: bits 19..10, then 9..0, over the list (or every entry)
+#pragma unroll 1
+    for (int pass = 1; pass < 3; ++pass) {
+      const int shift = (pass == 1) ? 10 : 0;
+      const uint32_t want = prefix >> (shift + 10);
+      __syncthreads();  // the previous scan's reads (and the list writes) are done
+      hist[tid] = 0;
+      if (tid < kWave) hist[kBins + tid] = 0;
+      __syncthreads();
+      if (gathered) {
+        for (int t = tid; t < c1; t += kBlkThreads) {
+          const uint32_t k = static_cast<uint32_t>(list[t]);
+          const bool cand = (k >> (shift + 10)) == want;
+          atomicAdd(&hist[cand ? static_cast<int>((k >> shift) & 1023u) : static_cast<int>(discard)], 1);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t k = key[c][i];
+            const bool cand = k != 0u && (k >> (shift + 10)) == want;
+            atomicAdd(&hist[cand ? static_cast<int>((k >> shift) & 1023u) : static_cast<int>(discard)], 1);
+          }
+      }
+      __syncthreads();
+      if (wave == 0) {
+        int bin, cum, cnt;
+        find_bin_wave(hist, 1024 / kWave, need, lane, bin, cum, cnt);
+        if (lane == 0) {
+          sel[1] = bin;
+          sel[2] = cum;
+          sel[3] = cnt;
+        }
+      }
+      __syncthreads();
+      prefix |= static_cast<uint32_t>(sel[1]) << shift;
+      need -= sel[2];
+      above += sel[2];
+      n_eq = sel[3];
+    }
+    tau = prefix;
+    n_gt = above;
+  }
+  const int need = k_keep - n_gt;  // >= 1 entries equal to tau, lowest index first
+
+  const float a = fmaxf(amax, 1e-5f);
+  const float inv = div_rn(127.0f, a);
+  const bool no_rank = n_eq == need || (tau == 0u && mask == nullptr);  // uniform
+  auto code_of = [&](int c, int i, uint32_t keep) {
+    const uint32_t k = key[c][i];
+    const float h = __uint_as_float(k | (((sg[c >> 2] >> (8 * (c & 3) + i)) & 1u) << 31));
+    return __float_as_uint(mul_rn(keep ? h : 0.0f, inv) + 12582912.0f);
+  };
+  auto pack4 = [](uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3) {
+    return __builtin_amdgcn_perm(c1, c0, 0x0c0c0400u) | __builtin_amdgcn_perm(c3, c2, 0x04000c0cu);
+  };
+  int8_t* out = codes + row;
+  // entries equal to tau in lower chunks (index order) of each chunk of this wave
+  int taken[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) taken[c] = 0;
+  if (!no_rank) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      int tc = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) tc += __popcll(__ballot(key[c][i] == tau && ent(c) < K));
+      if (lane == 0) tiecnt[wave + kBlkWaves * c] = tc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int gc = wave + kBlkWaves * c;
+      int t = 0;
+      for (int j = 0; j < gc; ++j) t += tiecnt[j];
+      taken[c] = t;
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int e = ent(c);
+    uint32_t q[8];
+    uint32_t kbits = 0;
+    if (no_rank) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t keep = static_cast<uint32_t>(key[c][i] >= tau);
+        q[i] = code_of(c, i, keep);
+        kbits |= keep << i;
+      }
+    } else {
+      int rank = taken[c];
+      int lower = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint64_t bm = __ballot(key[c][i] == tau && e < K);
+        lower = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bm >> 32),
+                                          __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bm), lower));
+      }
+      rank += lower;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t k = key[c][i];
+        const int is_eq = static_cast<int>(k == tau);
+        const uint32_t keep = static_cast<uint32_t>(k > tau) | static_cast<uint32_t>(is_eq & (rank < need));
+        rank += is_eq;
+        q[i] = code_of(c, i, keep);
+        kbits |= keep << i;
+      }
+    }
+    if (e < K) {
+      *reinterpret_cast<uint2*>(out + e) = make_uint2(pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]));
+      if (mask) reinterpret_cast<uint8_t*>(mask)[(row + e) >> 3] = static_cast<uint8_t>(kbits);
+    }
+  }
+  if (tid == 0) scales[m] = div_rn(a, 127.0f);
+}
+
 template <bool BF16, bool GATED>
 hipError_t launch_t(const void* g, const void* u, int64_t M, int64_t K, int64_t k_keep, int8_t* codes,
                     float* scales, uint32_t* mask, hipStream_t s) {
   const int m = static_cast<int>(M), k = static_cast<int>(K), kk = static_cast<int>(k_keep);
   const dim3 wgrid(static_cast<unsigned>((M + kRowsPerBlock - 1) / kRowsPerBlock)), block(kThreads);
-  if (K <= 4096) {
+  if (M <= kBlockRowsMax && K <= 2 * 8192) {
+    const dim3 bgrid(static_cast<unsigned>(M)), bblock(kBlkThreads);
+    if (K <= 8192)
+      hipLaunchKernelGGL((k_sparse_a8_block<BF16, GATED, 1>), bgrid, bblock, 0, s, g, u, k, kk, codes, scales, mask);
+    else
+      hipLaunchKernelGGL((k_sparse_a8_block<BF16, GATED, 2>), bgrid, bblock, 0, s, g, u, k, kk, codes, scales, mask);
+  } else if (K <= 4096) {
     hipLaunchKernelGGL((k_sparse_a8_wave<BF16, GATED, 8>), wgrid, block, 0, s, g, u, m, k, kk, codes, scales, mask);
   } else if (K <= 8192) {
     hipLaunchKernelGGL((k_sparse_a8_wave<BF16, GATED, 16>), wgrid, block, 0, s, g, u, m, k, kk, codes, scales, mask);

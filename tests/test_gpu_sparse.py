@@ -40,13 +40,21 @@ def test_out_proj_student_t(M, K):
 
 
 @pytest.mark.parametrize("k", [1, 2, 63, 64, 65, 2047, 4095, 4096])
-def test_k_keep_range(k):
-    M, K = 6, 4096
+@pytest.mark.parametrize("M", [6, 260])
+def test_k_keep_range(k, M):
+    K = 4096
     x = synth.heavy_tailed(seed=k, M=M, K=K)
     check(bf16_dev(x), None, x.f32, None, k, f"k={k}")
 
 
-def test_fp32_inputs_and_ties():
+def tile_rows(a, reps):
+    return None if a is None else np.ascontiguousarray(np.tile(a, (reps, 1)))
+
+
+@pytest.mark.parametrize("reps", [1, 22])
+def test_fp32_inputs_and_ties(reps):
+    """reps = 22 gives 264 rows, above the 256 rows that the one-workgroup-per-row
+    kernel takes, so both selection kernels see every case."""
     M, K = 12, 1024
     rs = np.random.default_rng(3)
     g = rs.integers(-3, 4, size=(M, K)).astype(np.float32)  # heavy exact ties in |h|
@@ -55,8 +63,21 @@ def test_fp32_inputs_and_ties():
     g[1] = 1.0
     u[1] = 1.0  # constant row: every key ties
     g[2] = -1.0  # ReLU kills the whole row
+    g, u = tile_rows(g, reps), tile_rows(u, reps)
     for k in (1, K // 2, K - 1, K):
-        check(f32_dev(g), f32_dev(u), g, u, k, f"ties k={k}")
+        check(f32_dev(g), f32_dev(u), g, u, k, f"ties k={k} reps={reps}")
+
+
+@pytest.mark.parametrize("M,K", [(3, 16384), (2, 8256), (260, 12288)])
+def test_long_rows_heavy_ties(M, K):
+    """Integer-valued inputs: |h| takes a handful of values, so the chosen first-pass
+    bin holds thousands of entries (more than the gathered list takes) and ties at tau
+    straddle many 512-entry chunks held by different waves."""
+    rs = np.random.default_rng(K + M)
+    g = rs.integers(-3, 4, size=(M, K)).astype(np.float32)
+    u = rs.integers(-2, 3, size=(M, K)).astype(np.float32)
+    for k in (K // 2, K // 4 + 7, K - 64):
+        check(f32_dev(g), f32_dev(u), g, u, k, f"long ties {M}x{K} k={k}")
 
 
 @pytest.mark.parametrize("k", [255, 256, 257])
@@ -70,6 +91,8 @@ def test_nonzero_count_around_k(k):
         idx = rs.choice(K, size=nz, replace=False)
         x[m, idx] = rs.standard_normal(nz).astype(np.float32)
     check(f32_dev(x), None, x, None, k, f"nnz around k={k}")
+    x = tile_rows(x, 44)
+    check(f32_dev(x), None, x, None, k, f"nnz around k={k}, 264 rows")
 
 
 def test_full_down_proj_shape_sampled():
