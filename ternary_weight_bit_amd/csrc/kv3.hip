@@ -18,7 +18,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kSteps = 4;         // vectors per lane in flight
-constexpr int64_t kMaxBlocks = 4096;
+constexpr int64_t kMaxBlocks = int64_t{1} << 20;  // one pass over the grid for caches up to 2^20 blocks of work
 // 1.5 * 2^23: adding it to |t| < 2^22 rounds t to an integer (ties to even) that
 // sits, two's complement, in the low mantissa bits; OR-ing a small integer n
 // into its bits gives the float 1.5 * 2^23 + n.
