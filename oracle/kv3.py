@@ -13,8 +13,12 @@ Readings:
 * the caller marks special positions with slot_of[b][s] >= 0 (the index of a
   side-slab slot); every token also gets its 3-bit main-slab codes;
 * main slab: per vector 3*D/8 bytes; per group of 32 codes three little-endian
-  uint32 bit planes, plane j holding bit j of each code's 3-bit two's
-  complement in bit position (code index mod 32);
+  uint32 words W0, W1, W2 holding the fields u = q + 4 in [0, 7].  Byte i of
+  the three words carries the eight codes 8i .. 8i+7 of the group (u_0 .. u_7
+  below): W0 byte = u_0 | u_1 << 3 | (u_6 & 3) << 6,
+  W1 byte = u_2 | u_3 << 3 | (u_6 >> 2) << 6 | (u_7 & 1) << 7,
+  W2 byte = u_4 | u_5 << 3 | (u_7 >> 1) << 6 (a storage format of this
+  library: the pages fix the bit width, not the bit order);
 * side slab: per slot and head D/2 bytes of 4-bit codes, even d in the low nibble.
 """
 from __future__ import annotations
@@ -39,21 +43,22 @@ def quantize(x: np.ndarray, qmax: int, lo: int, hi: int):
 
 
 def planes_encode(q3: np.ndarray) -> np.ndarray:
-    """int8 codes [..., D] in [-4, 3] -> uint8 [..., 3*D/8] bit planes."""
+    """int8 codes [..., D] in [-4, 3] -> uint8 [..., 3*D/8] (three words per 32 codes)."""
     D = q3.shape[-1]
-    u = (q3.astype(np.int16) & 7).astype(np.uint64).reshape(q3.shape[:-1] + (D // 32, 32))
-    bits = np.arange(32, dtype=np.uint64)
-    planes = np.stack([(((u >> np.uint64(j)) & 1) << bits).sum(axis=-1) for j in range(3)], axis=-1)
-    return planes.astype("<u4").view(np.uint8).reshape(q3.shape[:-1] + (3 * D // 8,))
+    u = (q3.astype(np.int16) + 4).astype(np.uint8).reshape(q3.shape[:-1] + (D // 32, 4, 8))
+    w0 = u[..., 0] | (u[..., 1] << 3) | ((u[..., 6] & 3) << 6)
+    w1 = u[..., 2] | (u[..., 3] << 3) | ((u[..., 6] >> 2) << 6) | ((u[..., 7] & 1) << 7)
+    w2 = u[..., 4] | (u[..., 5] << 3) | ((u[..., 7] >> 1) << 6)
+    words = np.stack([w0, w1, w2], axis=-2).astype(np.uint8)  # [..., group][word][byte i]
+    return words.reshape(q3.shape[:-1] + (3 * D // 8,))
 
 
 def planes_decode(p: np.ndarray, D: int) -> np.ndarray:
-    words = np.ascontiguousarray(p, dtype=np.uint8).view("<u4").astype(np.uint64)
-    words = words.reshape(p.shape[:-1] + (D // 32, 3))
-    bits = np.arange(32, dtype=np.uint64)
-    u = sum((((words[..., j : j + 1] >> bits) & 1) << np.uint64(j)) for j in range(3)).astype(np.int16)
-    u = np.where(u >= 4, u - 8, u).astype(np.int8)
-    return u.reshape(p.shape[:-1] + (D,))
+    b = np.ascontiguousarray(p, dtype=np.uint8).reshape(p.shape[:-1] + (D // 32, 3, 4)).astype(np.int16)
+    b0, b1, b2 = b[..., 0, :], b[..., 1, :], b[..., 2, :]
+    u = np.stack([b0 & 7, (b0 >> 3) & 7, b1 & 7, (b1 >> 3) & 7, b2 & 7, (b2 >> 3) & 7,
+                  (b0 >> 6) | (((b1 >> 6) & 1) << 2), (b1 >> 7) | ((b2 >> 6) << 1)], axis=-1)
+    return (u - 4).astype(np.int8).reshape(p.shape[:-1] + (D,))
 
 
 def nibbles_encode(q4: np.ndarray) -> np.ndarray:

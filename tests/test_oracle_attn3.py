@@ -18,12 +18,16 @@ def _brute_dequant(p3, s3, p4, s4, slot_of, b, s, h, D):
             out.append(float(np.float32(np.float32(c) * s4[slot, h])))
         return out
     words = [int.from_bytes(bytes(p3[b, s, h, 4 * i : 4 * i + 4]), "little") for i in range(3 * D // 32)]
+    # (word, bit within the byte) of bits 0, 1, 2 of field u = code + 4, by code index mod 8
+    field_bits = [[(0, 0), (0, 1), (0, 2)], [(0, 3), (0, 4), (0, 5)], [(1, 0), (1, 1), (1, 2)],
+                  [(1, 3), (1, 4), (1, 5)], [(2, 0), (2, 1), (2, 2)], [(2, 3), (2, 4), (2, 5)],
+                  [(0, 6), (0, 7), (1, 6)], [(1, 7), (2, 6), (2, 7)]]
     out = []
     for d in range(D):
-        g, i = divmod(d, 32)
-        u = sum(((words[3 * g + j] >> i) & 1) << j for j in range(3))
-        c = u - 8 if u >= 4 else u
-        out.append(float(np.float32(np.float32(c) * s3[b, s, h])))
+        g, r = divmod(d, 32)
+        i, j = divmod(r, 8)
+        u = sum(((words[3 * g + w] >> (8 * i + bit)) & 1) << k for k, (w, bit) in enumerate(field_bits[j]))
+        out.append(float(np.float32(np.float32(u - 4) * s3[b, s, h])))
     return out
 
 

@@ -23,21 +23,47 @@ def test_worked_example():
     assert q4.tolist() == g["codes4"] and hex(np.float32(s4).view(np.uint32)) == g["scale4_f32_bits"]
 
 
+# Bit positions (word, bit) of the three bits of field u_j (j = code index mod 8)
+# inside byte i = (code index mod 32) // 8 of each word, written out per field.
+FIELD_BITS = {
+    0: [(0, 0), (0, 1), (0, 2)], 1: [(0, 3), (0, 4), (0, 5)],
+    2: [(1, 0), (1, 1), (1, 2)], 3: [(1, 3), (1, 4), (1, 5)],
+    4: [(2, 0), (2, 1), (2, 2)], 5: [(2, 3), (2, 4), (2, 5)],
+    6: [(0, 6), (0, 7), (1, 6)], 7: [(1, 7), (2, 6), (2, 7)],
+}
+
+
+def _scatter(q):
+    """Reference placement of every code by the per-bit table (bit k of u = q + 4)."""
+    D = q.size
+    words = np.zeros((D // 32, 3), dtype=np.uint32)
+    for c in range(D):
+        g, r = divmod(c, 32)
+        i, j = divmod(r, 8)
+        u = int(q[c]) + 4
+        for k, (w, b) in enumerate(FIELD_BITS[j]):
+            if (u >> k) & 1:
+                words[g, w] |= np.uint32(1 << (8 * i + b))
+    return words.reshape(-1)
+
+
 def test_plane_layout_single_codes():
     D = 64
-    for pos, code in [(0, 1), (0, -1), (31, -4), (32, 3), (45, -2), (63, 2)]:
+    for pos, code in [(0, 1), (0, -1), (6, -4), (7, 3), (31, -4), (32, 3), (45, -2), (62, 2), (63, -3)]:
         q = np.zeros(D, dtype=np.int8)
         q[pos] = code
         p = kv3.planes_encode(q)
         assert p.size == 3 * D // 8
-        words = p.view("<u4")
-        g, i = divmod(pos, 32)
-        u = code & 7
-        expect = np.zeros(6, dtype=np.uint32)
-        for j in range(3):
-            if (u >> j) & 1:
-                expect[3 * g + j] = 1 << i
-        assert np.array_equal(words, expect), (pos, code)
+        assert np.array_equal(p.view("<u4"), _scatter(q)), (pos, code)
+        assert np.array_equal(kv3.planes_decode(p, D), q)
+
+
+def test_plane_layout_all_codes():
+    rs = np.random.default_rng(5)
+    for D in (32, 128):
+        q = rs.integers(-4, 4, size=D).astype(np.int8)
+        p = kv3.planes_encode(q)
+        assert np.array_equal(p.view("<u4"), _scatter(q))
         assert np.array_equal(kv3.planes_decode(p, D), q)
 
 
@@ -83,4 +109,6 @@ def test_idempotence():
 def test_zero_vector():
     x = np.zeros((1, 1, 1, 32), dtype=np.float32)
     p3, s3, p4, s4 = kv3.kv_pack3(x, np.full((1, 1), -1, np.int32), 0)
-    assert np.all(p3 == 0) and s3[0, 0, 0] == np.float32(1e-5) / np.float32(3)
+    # every field holds u = 0 + 4: bytes 0x24 (W0), 0x64 (W1), 0xA4 (W2)
+    assert p3.reshape(-1).tolist() == [0x24] * 4 + [0x64] * 4 + [0xA4] * 4
+    assert s3[0, 0, 0] == np.float32(1e-5) / np.float32(3)
