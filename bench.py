@@ -244,6 +244,11 @@ class Bench:
         self.blk_x = f32(synth.normal(S + 47, (B_, HD)))
         self.blk_out = t.empty((B_, HD), dtype=t.float32, device=dev)
         self.blk_ws = t.empty(bw.bw_block_decode_workspace_bytes(B_, S_, H_, D_, FFN), dtype=t.uint8, device=dev)
+        # the layers' caches start as copies of this layer's packed K and V (real codes of
+        # the synthetic K/V, not uninitialized slabs)
+        for i in range(2):
+            bw.bw_kv_pack3(self.kv[i], self.slot_of, self.n_special, *self.kvp[i])
+        t.cuda.synchronize()
         self.blk_layers = [(tuple(w.clone() for w in lw), tuple(a.clone() for a in self.kvp[0]),
                             tuple(a.clone() for a in self.kvp[1])) for _ in range(LAYERS)]
         self.blk_weight_bytes = sum(w.numel() * w.element_size() for w in lw)

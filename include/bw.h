@@ -45,7 +45,7 @@ extern "C" {
 #endif
 
 #define BW_ABI_VERSION 2
-#define BW_PACK_LAYOUT_VERSION 1
+#define BW_PACK_LAYOUT_VERSION 2
 
 typedef enum {
   BW_OK = 0,
@@ -74,6 +74,8 @@ typedef enum {
 } bw_weight_role;
 
 /* host */ int bw_abi_version(void);
+/* Version of the stored formats (packed ternary weights and the 3-bit KV
+ * slab); data written under another version must be packed again. */
 /* host */ int bw_pack_layout_version(void);
 /* host: message for the last non-OK status returned on this thread ("" if none) */
 const char* bw_last_error(void);
@@ -222,8 +224,10 @@ bw_status bw_bitlinear_sparse_a8_gather(const int8_t* codes, const float* x_scal
  *   if 0 <= slot_of[b][s] < n_special (a special token): also
  *          s4 = fl(a'/7), q4 = clamp(rne(fl(v*fl(7/a'))), -8, 7) into that slot.
  * p3: uint8 [B][S][H][3*D/8]; per group of 32 codes three little-endian
- *     uint32 bit planes, plane j holding bit j of each code's 3-bit two's
- *     complement at bit (index mod 32).  s3: fp32 [B][S][H].
+ *     uint32 words W0, W1, W2 of fields u = q + 4 (0..7); byte i of the three
+ *     words holds codes 8i..8i+7 (u0..u7):  W0 = u0 | u1<<3 | (u6&3)<<6,
+ *     W1 = u2 | u3<<3 | (u6>>2)<<6 | (u7&1)<<7,  W2 = u4 | u5<<3 | (u7>>1)<<6.
+ *     s3: fp32 [B][S][H].
  * p4: uint8 [n_special][H][D/2], even d in the low nibble.  s4: fp32
  *     [n_special][H].  Slots no position names are left untouched.
  * slot_of: int32 [B][S]; values outside [0, n_special) mark ordinary tokens.

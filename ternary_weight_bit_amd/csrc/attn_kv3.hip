@@ -14,10 +14,9 @@
 //      one batch for every head, so each position's H vectors (H * 3D/8
 //      contiguous bytes) and H scales are read whole.  Thread t owns head h,
 //      32-dim group g and position phase t % 4 (positions 4j + phase):
-//      pass 1: the group's three plane words are unpacked four codes per
-//        32-bit word: ((P >> k) & 0x01010101) holds bit j of codes k, k+8,
-//        k+16, k+24 in its bytes, so u = b0 + 2 b1 + 4 (1 - b2) = code + 4
-//        is built with shifts and masks; with q in fixed point (four
+//      pass 1: the group's three words are unpacked four codes per 32-bit
+//        word (u = code + 4 of codes k, k+8, k+16, k+24 in its bytes, mostly
+//        one shift and one mask each); with q in fixed point (four
 //        base-256 digits of q * 2^30 / max|q|) sum q*u is four integer dot4
 //        per word, exact; minus 4 * sum q it is summed over the G groups and
 //        scaled.  Special positions (slot_of in [0, n_special)) are rescored
@@ -39,37 +38,23 @@ namespace {
 constexpr int kAttnThreads = 512;
 constexpr int kUnroll = 8;  // positions per thread with loads in flight together
 constexpr int kAttnMergeMax = 4096;  // chunks per (batch, head) the merge holds in LDS
-constexpr uint32_t kBytes = 0x01010101u;
-
-// x shifted right by n (left by -n); n is a compile-time constant
-template <int n>
-__device__ __forceinline__ uint32_t shift_r(uint32_t x) {
-  if constexpr (n >= 0) return x >> n;
-  else return x << (-n);
-}
 
 // Unpacked codes of one 32-code group: u[k] holds code+4 of codes k, k+8,
-// k+16, k+24 in bytes 0..3.  Bit j of code i sits at bit i of plane j; it is
-// moved to bit j of byte i / 8 by one shift of the whole plane (right by
-// k - j, or left where k < j), so no bit is shifted out of the word.
-template <int k>
-__device__ __forceinline__ uint32_t unpack_k(uint32_t p0, uint32_t p1, uint32_t p2n) {
-  uint32_t x = shift_r<k>(p0) & kBytes;
-  x |= shift_r<k - 1>(p1) & (kBytes << 1);
-  x |= shift_r<k - 2>(p2n) & (kBytes << 2);
-  return x;
-}
-
-__device__ __forceinline__ void unpack_group(uint32_t p0, uint32_t p1, uint32_t p2, uint32_t (&u)[8]) {
-  const uint32_t p2n = ~p2;  // 4 (1 - b2): code + 4 is b0 + 2 b1 + 4 (1 - b2)
-  u[0] = unpack_k<0>(p0, p1, p2n);
-  u[1] = unpack_k<1>(p0, p1, p2n);
-  u[2] = unpack_k<2>(p0, p1, p2n);
-  u[3] = unpack_k<3>(p0, p1, p2n);
-  u[4] = unpack_k<4>(p0, p1, p2n);
-  u[5] = unpack_k<5>(p0, p1, p2n);
-  u[6] = unpack_k<6>(p0, p1, p2n);
-  u[7] = unpack_k<7>(p0, p1, p2n);
+// k+16, k+24 in bytes 0..3.  Byte i of the group's words w0, w1, w2 carries
+// the fields u = code + 4 of codes 8i .. 8i+7 (w0: u0 | u1 << 3 | low two bits
+// of u6 at 6; w1: u2 | u3 << 3 | bit 2 of u6 at 6 | bit 0 of u7 at 7; w2:
+// u4 | u5 << 3 | bits 1..2 of u7 at 6), so six slices are one shift and one
+// mask of a word and the other two take two of each and an OR.
+__device__ __forceinline__ void unpack_group(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t (&u)[8]) {
+  constexpr uint32_t M7 = 0x07070707u;
+  u[0] = w0 & M7;
+  u[1] = (w0 >> 3) & M7;
+  u[2] = w1 & M7;
+  u[3] = (w1 >> 3) & M7;
+  u[4] = w2 & M7;
+  u[5] = (w2 >> 3) & M7;
+  u[6] = ((w0 >> 6) & 0x03030303u) | ((w1 >> 4) & 0x04040404u);
+  u[7] = ((w1 >> 7) & 0x01010101u) | ((w2 >> 5) & 0x06060606u);
 }
 
 // bytes 2w and 2w+1 of x (w = HI_WORD) read as fp8 values: a byte 0..7 is an fp8 subnormal,
@@ -126,7 +111,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_chunk(
     int64_t q_stride, int CH, int nch, float* __restrict__ part) {
   constexpr int G = D / 32;                   // 32-dim groups per vector
   constexpr int HS = kAttnThreads / (4 * G);  // heads per head block
-  constexpr int VB = 3 * D / 8;               // plane bytes per vector
+  constexpr int VB = 3 * D / 8;               // 3-bit code bytes per vector
   extern __shared__ float s_dyn[];            // s_z[CH][H + 1], then s_m[H], s_l[H]
   __shared__ uint16_t s_list[kAttnMaxChunk];  // special positions of the chunk, ascending
   __shared__ uint32_t s_spec[kAttnMaxChunk / 32];

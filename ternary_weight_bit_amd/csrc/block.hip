@@ -34,16 +34,20 @@ __device__ __forceinline__ float wave_absmax(float v) {
 // Write the 3-bit codes (and, at a special position, the 4-bit slot) of the
 // new token's K and V vectors at position pos, exactly as the cache packer
 // defines them: a' = max(max|v|, 1e-5); 3-bit q = clamp(rne(fl(v * fl(3/a'))),
-// -4, 3) with s3 = fl(a'/3), stored as three bit planes per 32 codes; 4-bit
+// -4, 3) with s3 = fl(a'/3), stored as fields u = q + 4, byte i of the three
+// words of a 32-code group holding codes 8i .. 8i+7; 4-bit
 // q = clamp(rne(fl(v * fl(7/a'))), -8, 7) with s4 = fl(a'/7), even d in the
-// low nibble.  blockIdx.y selects K (0) or V (1).
+// low nibble.  One wave per vector; lane l < D/8 holds d = 8l .. 8l+7 and
+// writes byte l % 4 of the three words of group l / 4, as the packer's lanes
+// do.  blockIdx.y selects K (0) or V (1).
 template <int D>
 __global__ __launch_bounds__(kAppendThreads) void k_kv_append3(
     const float* __restrict__ y_qkv, int64_t row_stride, int64_t B, int64_t H, int64_t pos, int64_t S_cap,
     const int32_t* __restrict__ slot_of, int64_t n_special, uint8_t* __restrict__ kp3, float* __restrict__ ks3,
     uint8_t* __restrict__ kp4, float* __restrict__ ks4, uint8_t* __restrict__ vp3, float* __restrict__ vs3,
     uint8_t* __restrict__ vp4, float* __restrict__ vs4) {
-  constexpr int NV = D / 64;  // values per lane
+  constexpr int LPV = D / 8;  // lanes holding the vector
+  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: adding it rounds to an integer, ties to even
   const int lane = threadIdx.x & 63;
   const int64_t wid = static_cast<int64_t>(blockIdx.x) * (kAppendThreads / 64) + (threadIdx.x >> 6);
   if (wid >= B * H) return;  // whole wave leaves together
@@ -57,54 +61,40 @@ __global__ __launch_bounds__(kAppendThreads) void k_kv_append3(
   uint8_t* __restrict__ p4 = is_v ? vp4 : kp4;
   float* __restrict__ s4 = is_v ? vs4 : ks4;
 
-  float x[NV];
+  const bool mine = lane < LPV;
+  const int l = mine ? lane : 0;
+  const float4 xa = *reinterpret_cast<const float4*>(src + 8 * l);
+  const float4 xb = *reinterpret_cast<const float4*>(src + 8 * l + 4);
+  const float x[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
   float a = 0.0f;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    x[i] = src[lane + 64 * i];
-    a = fmaxf(a, fabsf(x[i]));
-  }
-  const float ap = fmaxf(wave_absmax(a), 1e-5f);
+  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
+  const float ap = fmaxf(wave_absmax(mine ? a : 0.0f), 1e-5f);
   const int64_t vec = (b * S_cap + pos) * H + h;
 
-  // 3-bit codes; plane j of the 32 codes of group g is a ballot of bit j
-  const float inv3 = 3.0f / ap;
-  uint32_t planes[2 * NV][3];
+  // |x| <= a' keeps |x * fl(3/a')| < 3.5 (and |x * fl(7/a')| < 7.5): the clamps never act
+  const float inv3 = __fdiv_rn(3.0f, ap);
+  uint32_t f[8];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int q = static_cast<int>(fminf(fmaxf(rintf(__fmul_rn(x[i], inv3)), -4.0f), 3.0f));
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      const uint64_t bal = __ballot((q >> j) & 1);
-      planes[2 * i][j] = static_cast<uint32_t>(bal);
-      planes[2 * i + 1][j] = static_cast<uint32_t>(bal >> 32);
-    }
+  for (int i = 0; i < 8; ++i) f[i] = (__float_as_uint(__fmul_rn(x[i], inv3) + kMagic) & 7u) ^ 4u;
+  if (mine) {
+    uint8_t* out = p3 + vec * (3 * D / 8) + 12 * (l >> 2) + (l & 3);
+    out[0] = static_cast<uint8_t>(f[0] | (f[1] << 3) | ((f[6] & 3u) << 6));
+    out[4] = static_cast<uint8_t>(f[2] | (f[3] << 3) | ((f[6] >> 2) << 6) | ((f[7] & 1u) << 7));
+    out[8] = static_cast<uint8_t>(f[4] | (f[5] << 3) | ((f[7] >> 1) << 6));
   }
-  if (lane < 3 * 2 * NV) {
-    const int g = lane / 3, j = lane % 3;  // dword 3g + j of the vector
-    uint32_t w = 0;
-#pragma unroll
-    for (int gg = 0; gg < 2 * NV; ++gg)
-#pragma unroll
-      for (int jj = 0; jj < 3; ++jj)
-        if (gg == g && jj == j) w = planes[gg][jj];
-    reinterpret_cast<uint32_t*>(p3 + vec * (3 * D / 8))[lane] = w;
-  }
-  if (lane == 0) s3[vec] = ap / 3.0f;
+  if (lane == 0) s3[vec] = __fdiv_rn(ap, 3.0f);
 
   // 4-bit slot of a special position
   const int32_t slot = slot_of[b * S_cap + pos];
   if (slot >= 0 && slot < n_special) {
-    const float inv7 = 7.0f / ap;
+    const float inv7 = __fdiv_rn(7.0f, ap);
+    uint32_t w = 0;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int q = static_cast<int>(fminf(fmaxf(rintf(__fmul_rn(x[i], inv7)), -8.0f), 7.0f));
-      const uint32_t nib = static_cast<uint32_t>(q) & 0xFu;
-      const uint32_t hi = static_cast<uint32_t>(__shfl_down(static_cast<int>(nib), 1));
-      if ((lane & 1) == 0) p4[(static_cast<int64_t>(slot) * H + h) * (D / 2) + (lane >> 1) + 32 * i] =
-          static_cast<uint8_t>(nib | (hi << 4));
-    }
-    if (lane == 0) s4[static_cast<int64_t>(slot) * H + h] = ap / 7.0f;
+    for (int i = 0; i < 8; ++i) w |= (__float_as_uint(__fmul_rn(x[i], inv7) + kMagic) & 0xFu) << (4 * i);
+    const int64_t sv = static_cast<int64_t>(slot) * H + h;
+    if (mine) reinterpret_cast<uint32_t*>(p4 + sv * (D / 2))[l] = w;
+    if (lane == 0) s4[sv] = __fdiv_rn(ap, 7.0f);
   }
 }
 

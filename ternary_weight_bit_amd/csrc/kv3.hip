@@ -8,8 +8,13 @@
 // of D elements spans D/8 lanes and a wave holds 512/D vectors per step; a
 // wave runs kSteps steps at once with every load issued before the first use.
 // The absmax is reduced across the vector's lanes with shuffles; four lanes
-// make one group of 32 codes, and each lane writes its byte of the group's
-// three bit-plane words.
+// make one group of 32 codes, and lane i of the group (codes 8i .. 8i+7)
+// writes byte i of each of the group's three words: with u_j = q_j + 4,
+//   W0 = u0 | u1 << 3 | (u6 & 3) << 6
+//   W1 = u2 | u3 << 3 | (u6 >> 2) << 6 | (u7 & 1) << 7
+//   W2 = u4 | u5 << 3 | (u7 >> 1) << 6,
+// so a reader gets code+4 of four codes per 32-bit word with one shift and
+// one mask for six of the eight slices.
 #include "bw_device.h"
 #include "bw_internal.h"
 
@@ -67,20 +72,19 @@ __global__ __launch_bounds__(kThreads) void k_kv_pack3(const void* __restrict__ 
       amax = vec_max<LPV>(amax);
       const float a = fmaxf(amax, 1e-5f);
       const float inv3 = div_rn(3.0f, a);
-      // bit planes of this lane's 8 codes: byte j holds bit j of each code.
-      // |x| <= a' makes |x * fl(3/a')| < 3.5, so rne() lands in [-3, 3] and the
-      // clamp to [-4, 3] never acts; adding 1.5 * 2^23 rounds to an integer (ties
-      // to even) and leaves it, two's complement, in the low mantissa bits.
-      uint32_t pl0 = 0, pl1 = 0, pl2 = 0;
+      // fields u = q + 4 of this lane's 8 codes.  |x| <= a' makes
+      // |x * fl(3/a')| < 3.5, so rne() lands in [-3, 3] and the clamp to
+      // [-4, 3] never acts; adding 1.5 * 2^23 rounds to an integer (ties to
+      // even) and leaves it, two's complement, in the low mantissa bits, so
+      // (bits & 7) ^ 4 = q + 4.
+      uint32_t f[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t c = __float_as_uint(mul_rn(x[i], inv3) + kRoundMagic);
-        pl0 |= (c & 1u) << i;
-        pl1 |= ((c >> 1) & 1u) << i;
-        pl2 |= ((c >> 2) & 1u) << i;
-      }
+      for (int i = 0; i < 8; ++i) f[i] = (__float_as_uint(mul_rn(x[i], inv3) + kRoundMagic) & 7u) ^ 4u;
+      const uint32_t pl0 = f[0] | (f[1] << 3) | ((f[6] & 3u) << 6);
+      const uint32_t pl1 = f[2] | (f[3] << 3) | ((f[6] >> 2) << 6) | ((f[7] & 1u) << 7);
+      const uint32_t pl2 = f[4] | (f[5] << 3) | ((f[7] >> 1) << 6);
       // group of 32 codes = 4 lanes; lane q of the group writes byte q of each
-      // of the group's three plane words (bytes, not shuffles: cheaper here)
+      // of the group's three words (bytes, not shuffles: cheaper here)
       if (active) {
         const int grp = sub >> 2;
         uint8_t* out = p3 + v * (3 * D / 8) + 12 * grp + (sub & 3);
@@ -180,12 +184,12 @@ __global__ __launch_bounds__(kThreads) void k_kv_unpack3(const uint8_t* __restri
         const uint32_t b0 = (pw[u][0] >> sh) & 0xFFu;
         const uint32_t b1 = (pw[u][1] >> sh) & 0xFFu;
         const uint32_t b2 = (pw[u][2] >> sh) & 0xFFu;
-        // (code ^ 4) = q + 4 in [0, 7], turned into the float q exactly as above
+        // fields u = q + 4 in [0, 7], turned into the float q exactly as above
+        const uint32_t f[8] = {b0 & 7u, (b0 >> 3) & 7u, b1 & 7u, (b1 >> 3) & 7u, b2 & 7u, (b2 >> 3) & 7u,
+                               (b0 >> 6) | (((b1 >> 6) & 1u) << 2), (b1 >> 7) | ((b2 >> 6) << 1)};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t c = ((b0 >> i) & 1u) | (((b1 >> i) & 1u) << 1) | (((b2 >> i) & 1u) << 2);
-          x[i] = mul_rn(__uint_as_float(kRoundMagicBits | (c ^ 4u)) - (kRoundMagic + 4.0f), sc[u]);
-        }
+        for (int i = 0; i < 8; ++i)
+          x[i] = mul_rn(__uint_as_float(kRoundMagicBits | f[i]) - (kRoundMagic + 4.0f), sc[u]);
       }
       store8<BF16>(out, v * D + sub * 8, x);
     }

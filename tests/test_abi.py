@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 def test_versions():
     assert bw.bw_abi_version() == 2
-    assert bw.bw_pack_layout_version() == 1
+    assert bw.bw_pack_layout_version() == 2
     assert bw.bw_ternary_packed_bytes(4096, 4096) == 4096 * 4096 // 4
     assert bw.bw_ternary_packed_bytes(0, 64) == 0
     assert bw.bw_pack_ternary_workspace_bytes(16, 64) >= 4096 + 4
