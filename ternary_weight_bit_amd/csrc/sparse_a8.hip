@@ -19,7 +19,7 @@
 // ballot per register slot, counted with mbcnt, chunk by chunk.  Codes are
 // written as 8-byte runs per lane.
 //
-// Up to 256 rows of at most 16384 entries: one workgroup of 16 waves per row
+// Up to 256 rows of at most 16384 entries: one workgroup of 8 or 16 waves per row
 // (below).  Longer rows (up to 16384) use one workgroup (256 threads) per row: entries
 // t + 256*r in registers, tau found by bisection over the magnitude bits with
 // one ballot + popcount per register and one barrier per step.
@@ -510,14 +510,12 @@ void k_sparse_a8_wave(const void* __restrict__ g,
 // ------------------------------------------------------ one workgroup per row
 // For few rows (single-token decode) one wave per row leaves the chip idle and
 // each row pays one wave's load and selection latency.  Here a row is spread
-// over 16 waves: wave w holds the 512-entry chunks w, w + 16, ... in the same
+// over NW = 8 or 16 waves: wave w holds the 512-entry chunks w, w + NW, ... in the same
 // per-lane arrangement as the one-wave kernel (entries 512c + 8l + i).  The
 // radix passes share one LDS histogram (LDS atomics); wave 0 scans it and the
 // result goes to every wave through LDS.  Ties at tau are ranked in index
 // order with per-chunk counts exchanged through LDS and one ballot + mbcnt per
 // register slot inside a chunk.
-constexpr int kBlkThreads = 1024;
-constexpr int kBlkWaves = kBlkThreads / kWave;
 constexpr int kBlkList = 1024;  // capacity of the list of entries in the chosen first-pass bin
 constexpr int64_t kBlockRowsMax = 256;  // up to this many rows: one workgroup per row
 
@@ -544,14 +542,16 @@ __device__ __forceinline__ void find_bin_wave(const int* hist, int per, int need
   cnt_bin = lane_value(cnt, J);
 }
 
-template <bool BF16, bool GATED, int CH>
-__global__ __launch_bounds__(kBlkThreads) void k_sparse_a8_block(const void* __restrict__ g,
+template <bool BF16, bool GATED, int CH, int NW>
+__global__ __launch_bounds__(NW * kWave) void k_sparse_a8_block(const void* __restrict__ g,
                                                                  const void* __restrict__ u, int K, int k_keep,
                                                                  int8_t* __restrict__ codes,
                                                                  float* __restrict__ scales,
                                                                  uint32_t* __restrict__ mask) {
   __shared__ __attribute__((aligned(16))) int hist[kHist];
   __shared__ int list[kBlkList];
+  constexpr int kBlkWaves = NW;
+  constexpr int kBlkThreads = NW * kWave;
   __shared__ uint32_t w_max[kBlkWaves];
   __shared__ int w_nz[kBlkWaves];
   __shared__ int sel[4];  // list fill, then (bin, count above, count in bin) of the last scan
@@ -600,9 +600,7 @@ __global__ __launch_bounds__(kBlkThreads) void k_sparse_a8_block(const void* __r
   }
 
   // ---- clear the histogram; per-wave maximum and nonzero count
-  hist[tid] = 0;
-  hist[tid + kBlkThreads] = 0;
-  if (tid < kWave) hist[2 * kBlkThreads + tid] = 0;
+  for (int i = tid; i < kHist; i += kBlkThreads) hist[i] = 0;
   if (tid == 0) sel[0] = 0;
   {
     uint32_t kmax = 0;
@@ -692,7 +690,7 @@ __global__ __launch_bounds__(kBlkThreads) void k_sparse_a8_block(const void* __r
       const int shift = (pass == 1) ? 10 : 0;
       const uint32_t want = prefix >> (shift + 10);
       __syncthreads();  // the previous scan's reads (and the list writes) are done
-      hist[tid] = 0;
+      for (int i = tid; i < 1024; i += kBlkThreads) hist[i] = 0;
       if (tid < kWave) hist[kBins + tid] = 0;
       __syncthreads();
       if (gathered) {
@@ -811,11 +809,14 @@ hipError_t launch_t(const void* g, const void* u, int64_t M, int64_t K, int64_t 
   const int m = static_cast<int>(M), k = static_cast<int>(K), kk = static_cast<int>(k_keep);
   const dim3 wgrid(static_cast<unsigned>((M + kRowsPerBlock - 1) / kRowsPerBlock)), block(kThreads);
   if (M <= kBlockRowsMax && K <= 2 * 8192) {
-    const dim3 bgrid(static_cast<unsigned>(M)), bblock(kBlkThreads);
-    if (K <= 8192)
-      hipLaunchKernelGGL((k_sparse_a8_block<BF16, GATED, 1>), bgrid, bblock, 0, s, g, u, k, kk, codes, scales, mask);
+    // 8 waves while one 512-entry chunk per wave covers the row, else 16
+    const dim3 bgrid(static_cast<unsigned>(M));
+    if (K <= 4096)
+      hipLaunchKernelGGL((k_sparse_a8_block<BF16, GATED, 1, 8>), bgrid, dim3(512), 0, s, g, u, k, kk, codes, scales, mask);
+    else if (K <= 8192)
+      hipLaunchKernelGGL((k_sparse_a8_block<BF16, GATED, 1, 16>), bgrid, dim3(1024), 0, s, g, u, k, kk, codes, scales, mask);
     else
-      hipLaunchKernelGGL((k_sparse_a8_block<BF16, GATED, 2>), bgrid, bblock, 0, s, g, u, k, kk, codes, scales, mask);
+      hipLaunchKernelGGL((k_sparse_a8_block<BF16, GATED, 2, 16>), bgrid, dim3(1024), 0, s, g, u, k, kk, codes, scales, mask);
   } else if (K <= 4096) {
     hipLaunchKernelGGL((k_sparse_a8_wave<BF16, GATED, 8>), wgrid, block, 0, s, g, u, m, k, kk, codes, scales, mask);
   } else if (K <= 8192) {

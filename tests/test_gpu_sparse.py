@@ -27,7 +27,7 @@ def check(g_dev, u_dev, g32, u32, k, label):
     assert np.all(np.unpackbits(m.view(np.uint8), axis=1).sum(axis=1) == k)
 
 
-@pytest.mark.parametrize("M,K", [(64, 11008), (7, 64), (33, 4096), (5, 16384), (3, 320)])
+@pytest.mark.parametrize("M,K", [(64, 11008), (7, 64), (33, 4096), (5, 16384), (3, 320), (4, 8192), (3, 6144)])
 def test_relu2_gate_bf16(M, K):
     g, u = synth.gate_up(seed=M * 31 + K, M=M, K=K)
     check(bf16_dev(g), bf16_dev(u), g.f32, u.f32, K // 2, f"relu2 {M}x{K}")
