@@ -1,0 +1,14 @@
+"""bench.py's command line on a host without a GPU: the one-GPU contract."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2", "--steps", "1"],
+                       capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
+    assert r.stdout.strip() == "" or not r.stdout.lstrip().startswith("{")
