@@ -53,8 +53,9 @@ def tile_rows(a, reps):
 
 @pytest.mark.parametrize("reps", [1, 22])
 def test_fp32_inputs_and_ties(reps):
-    """reps = 22 gives 264 rows, above the 256 rows that the one-workgroup-per-row
-    kernel takes, so both selection kernels see every case."""
+    """reps = 22 gives 264 rows: rows of at most 4096 entries then go to the
+    one-wave-per-row kernel (256 rows or fewer take a workgroup per row), so both
+    selection kernels see every case."""
     M, K = 12, 1024
     rs = np.random.default_rng(3)
     g = rs.integers(-3, 4, size=(M, K)).astype(np.float32)  # heavy exact ties in |h|
