@@ -36,7 +36,7 @@ namespace bw {
 namespace {
 
 constexpr int kAttnThreads = 512;
-constexpr int kUnroll = 8;  // positions per thread with loads in flight together
+constexpr int kUnroll = 4;  // positions per thread with loads in flight together (8 measured slower)
 constexpr int kAttnMergeMax = 4096;  // chunks per (batch, head) the merge holds in LDS
 
 // Unpacked codes of one 32-code group: u[k] holds code+4 of codes k, k+8,
