@@ -173,11 +173,11 @@ def test_a8_extreme_codes():
 
 
 # ---------------------------------------------------------------- b1.58 baseline path
-@pytest.mark.parametrize("M,K,N", [(37, 4096, 208), (5, 16384, 144), (130, 4096, 272)])
+@pytest.mark.parametrize("M,K,N", [(37, 4096, 208), (5, 16384, 144), (130, 4096, 272), (260, 4096, 144)])
 def test_b158_int8_keep_all(M, K, N):
     """BitNet b1.58's activation path, which a4.8 is compared against: INT8 absmax of every
-    entry (the sparse front end with k = K, no top-k), then the W1.58A8 contraction.  K=16384
-    takes the one-workgroup-per-row front end, K=4096 the one-wave-per-row one."""
+    entry (the sparse front end with k = K, no top-k), then the W1.58A8 contraction.  260
+    rows of 4096 take the one-wave-per-row front end, the other shapes a workgroup per row."""
     x = synth.prefill_activations(seed=M + K + N, M=M, K=K)
     w = synth.to_bf16(synth.normal(N + 3 * K, (N, K), 0.02))
     codes, scales = bw.bw_quantize_sparse_a8(bf16_dev(x), None, K)
