@@ -94,3 +94,8 @@ def test_small_layer_d64():
 def test_7b_layer_shapes():
     """7B shapes: hidden 4096 (32 heads x 128), FFN 11008, 8 sequences, a 512-position cache."""
     run_layer(synth.SEED_BASE + 92, B=8, H=32, D=128, F=11008, S_cap=512, pos=300)
+
+
+def test_max_batch_last_position():
+    """The largest batch the layer takes (16 sequences) writing the cache's last position."""
+    run_layer(synth.SEED_BASE + 93, B=16, H=2, D=64, F=192, S_cap=33, pos=32)
