@@ -607,7 +607,9 @@ def main():
         "config": {"workload": "a4.8 BitLinear hot path at 7B shapes: prefill M=2048 K=4096 N=11008/4096 "
                                "(INT4+FP4), sparse A8 down/out_proj M=2048, decode GEMV M=1,2,4,8 over 32 layers "
                                "of qkv (N=12288) + gate/up (N=22016), KV 3-bit pack/unpack 8x4096x32x128, "
-                               "ternary pack 4096x4096", "global_batch": M_PREFILL, "seq_len": KV_SHAPE[1],
+                               "ternary pack 4096x4096; also the M=1 gather GEMV (down/out_proj), attention over "
+                               "the 3-bit cache 8x4096x32x128 and one decoder layer for 8 sequences x 4096 cached "
+                               "positions", "global_batch": M_PREFILL, "seq_len": KV_SHAPE[1],
                    "parallelism": "none (1 GPU)"},
         "value_basis": "2*2048*4096*(11008+4096) int ops / time of the INT4 quantizer + both W1.58A4 GEMMs, "
                        "launched back to back as one stream sequence (row a0)",
