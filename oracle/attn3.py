@@ -19,11 +19,12 @@ import numpy as np
 from . import kv3
 
 
-def decode_attention(q, k_pack, v_pack, slot_of, D: int):
+def decode_attention(q, k_pack, v_pack, slot_of, D: int, n_special: int | None = None):
     """q float32 [B][H][D]; k_pack / v_pack = (p3, s3, p4, s4) as written by kv3.kv_pack3;
-    slot_of int32 [B][S].  Returns (out float64 [B][H][D], p float64 [B][H][S])."""
-    Kd = kv3.kv_unpack3(*k_pack, slot_of, D).astype(np.float64)  # [B][S][H][D]
-    Vd = kv3.kv_unpack3(*v_pack, slot_of, D).astype(np.float64)
+    slot_of int32 [B][S]; n_special as for kv3.kv_unpack3.  Returns (out float64
+    [B][H][D], p float64 [B][H][S])."""
+    Kd = kv3.kv_unpack3(*k_pack, slot_of, D, n_special).astype(np.float64)  # [B][S][H][D]
+    Vd = kv3.kv_unpack3(*v_pack, slot_of, D, n_special).astype(np.float64)
     qd = np.asarray(q, dtype=np.float64)
     z = np.einsum("bhd,bshd->bhs", qd, Kd) / np.sqrt(D)
     z = z - z.max(axis=-1, keepdims=True)

@@ -64,13 +64,14 @@ def decode_block(x, t_qkv, b_qkv, t_o, b_o, t_gu, b_gu, t_down, b_down, k_pack, 
     att, _ = attn3.decode_attention(y_qkv[:, :HD].reshape(B, H, D), upto(kp), upto(vp),
                                     slot_of[:, : pos + 1], D)
     a32 = att.reshape(B, HD).astype(np.float32)
-    _, _, q8, s8 = sparse8.sparse_a8(a32, None, HD // 2)
+    _, keep_o, q8, s8 = sparse8.sparse_a8(a32, None, HD // 2)
     y_o = fp32_handoff(bitlinear.contract(q8, t_o), s8, b_o)
     x1 = (x + y_o).astype(np.float32)
     q4b, sb = act4.quantize_int4(x1)
     g = fp32_handoff(bitlinear.contract(q4b, t_gu[:F]), sb, b_gu[:F])
     u = fp32_handoff(bitlinear.contract(q4b, t_gu[F:]), sb, b_gu[F:])
-    _, _, q8d, s8d = sparse8.sparse_a8(g, u, F // 2)
+    h_d, keep_d, q8d, s8d = sparse8.sparse_a8(g, u, F // 2)
     y_d = fp32_handoff(bitlinear.contract(q8d, t_down), s8d, b_down)
     x_out = (x1 + y_d).astype(np.float32)
-    return x_out, kp, vp, dict(y_qkv=y_qkv, att=a32, y_o=y_o, x1=x1, g=g, u=u, y_d=y_d)
+    return x_out, kp, vp, dict(y_qkv=y_qkv, att=a32, keep_o=keep_o, q8=q8, s8=s8, y_o=y_o, x1=x1, g=g, u=u,
+                               h_d=h_d, keep_d=keep_d, q8d=q8d, s8d=s8d, y_d=y_d)

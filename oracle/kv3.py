@@ -10,8 +10,9 @@ Readings:
 * 4-bit (special positions): inv = fl(7 / a'), s4 = fl(a' / 7),
   q = clamp(rne(fl(x * inv)), -8, 7);
 * a' = max(max |x|, 1e-5); dequantized value = fl(q * s) in fp32;
-* the caller marks special positions with slot_of[b][s] >= 0 (the index of a
-  side-slab slot); every token also gets its 3-bit main-slab codes;
+* the caller marks special positions with 0 <= slot_of[b][s] < n_special (the
+  index of a side-slab slot); any other value marks an ordinary token; every
+  token also gets its 3-bit main-slab codes;
 * main slab: per vector 3*D/8 bytes; per group of 32 codes three little-endian
   uint32 words W0, W1, W2 holding the fields u = q + 4 in [0, 7].  Byte i of
   the three words carries the eight codes 8i .. 8i+7 of the group (u_0 .. u_7
@@ -74,6 +75,12 @@ def nibbles_decode(p: np.ndarray) -> np.ndarray:
     return np.where(out >= 8, out - 16, out).astype(np.int8)
 
 
+def is_special(slot_of: np.ndarray, n_special: int) -> np.ndarray:
+    """bool mask of the positions whose slot_of names a side-slab slot."""
+    slot_of = np.asarray(slot_of)
+    return (slot_of >= 0) & (slot_of < n_special)
+
+
 def kv_pack3(x: np.ndarray, slot_of: np.ndarray, n_special: int):
     """x float32 [B][S][H][D] -> (p3 uint8 [B][S][H][3D/8], s3 f32 [B][S][H],
     p4 uint8 [n_special][H][D/2], s4 f32 [n_special][H]).  Side-slab slots that
@@ -84,7 +91,7 @@ def kv_pack3(x: np.ndarray, slot_of: np.ndarray, n_special: int):
     p3 = planes_encode(q3)
     p4 = np.zeros((n_special, H, D // 2), dtype=np.uint8)
     s4 = np.zeros((n_special, H), dtype=np.float32)
-    bs = np.argwhere(slot_of >= 0)
+    bs = np.argwhere(is_special(slot_of, n_special))
     if len(bs):
         xs = x[bs[:, 0], bs[:, 1]]  # [n][H][D]
         q4, sc4 = quantize(xs, 7, -8, 7)
@@ -94,11 +101,14 @@ def kv_pack3(x: np.ndarray, slot_of: np.ndarray, n_special: int):
     return p3, s3, p4, s4
 
 
-def kv_unpack3(p3, s3, p4, s4, slot_of, D: int) -> np.ndarray:
-    """Dequantize to float32 [B][S][H][D]; special positions read their 4-bit slot."""
+def kv_unpack3(p3, s3, p4, s4, slot_of, D: int, n_special: int | None = None) -> np.ndarray:
+    """Dequantize to float32 [B][S][H][D]; special positions (slot_of naming one of
+    the n_special side slots, by default every row of p4) read their 4-bit slot."""
+    if n_special is None:
+        n_special = np.asarray(p4).shape[0]
     q3 = planes_decode(p3, D)
     out = (q3.astype(np.float32) * np.asarray(s3, dtype=np.float32)[..., None]).astype(np.float32)
-    bs = np.argwhere(slot_of >= 0)
+    bs = np.argwhere(is_special(slot_of, n_special))
     if len(bs):
         slots = slot_of[bs[:, 0], bs[:, 1]]
         q4 = nibbles_decode(p4[slots])

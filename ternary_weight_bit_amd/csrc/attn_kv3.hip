@@ -443,18 +443,25 @@ struct AttnGrid {
   int ch, nch;
 };
 
-// Positions per chunk: about one workgroup per CU over the batch, a multiple of
-// 4, with the chunk's scores (CH * (H + 1) + 2H floats) within kAttnLdsFloats
-// and at most kAttnMergeMax chunks; nch = 0 marks a shape beyond those limits.
-AttnGrid attn_grid(int64_t B, int64_t S, int64_t H) {
-  int64_t ch = (S * B) / 256;
-  const int64_t min_ch = (S + kAttnMergeMax - 1) / kAttnMergeMax;
-  if (ch < min_ch) ch = min_ch;
+// Largest chunk the LDS score array allows for H heads (a multiple of 4; below
+// 4 the shape is unsupported).
+int64_t attn_chunk_cap(int64_t H) {
   int64_t cap = (kAttnLdsFloats - 2 * H) / (H + 1);
   if (cap > kAttnMaxChunk) cap = kAttnMaxChunk;
+  return cap / 4 * 4;
+}
+
+// Positions per chunk: about one workgroup per CU over the batch (at least
+// S * B / 256 positions, so at most ceil(256 / B) chunks), a multiple of 4,
+// with the chunk's scores (CH * (H + 1) + 2H floats) within kAttnLdsFloats and
+// at most kAttnMergeMax chunks; nch = 0 marks a shape beyond those limits.
+AttnGrid attn_grid(int64_t B, int64_t S, int64_t H) {
+  int64_t ch = (S * B + 255) / 256;
+  const int64_t min_ch = (S + kAttnMergeMax - 1) / kAttnMergeMax;
+  if (ch < min_ch) ch = min_ch;
+  int64_t cap = attn_chunk_cap(H);
   const int64_t s4 = (S + 3) / 4 * 4;
   if (cap > s4) cap = s4;
-  cap = cap / 4 * 4;
   ch = (ch + 3) / 4 * 4;
   if (ch > cap) ch = cap;
   if (ch < 4) ch = 4;
@@ -468,6 +475,22 @@ AttnGrid attn_grid(int64_t B, int64_t S, int64_t H) {
 }  // namespace
 
 bool attn_decode3_supported(int64_t B, int64_t S, int64_t H) { return attn_grid(B, S, H).nch > 0; }
+
+// Chunk count bound over every attended length S in [1, S_cap]: a chunk that no
+// cap shortens holds at least S * B / 256 positions (ceil(256 / B) chunks at
+// most); one the LDS cap shortens holds attn_chunk_cap(H) positions
+// (ceil(S_cap / cap) chunks at most); one capped at the rounded length S is the
+// only chunk.
+int64_t attn_decode3_max_chunks(int64_t B, int64_t S_cap, int64_t H) {
+  const int64_t by_batch = (256 + B - 1) / B;
+  const int64_t cap = attn_chunk_cap(H);
+  const int64_t by_cap = cap >= 4 ? (S_cap + cap - 1) / cap : 0;
+  return by_batch > by_cap ? by_batch : by_cap;
+}
+
+size_t attn_decode3_workspace_bound(int64_t B, int64_t S_cap, int64_t H, int64_t D) {
+  return static_cast<size_t>(B) * attn_decode3_max_chunks(B, S_cap, H) * H * (D + 4) * sizeof(float);
+}
 
 size_t attn_decode3_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D) {
   const AttnGrid g = attn_grid(B, S, H);

@@ -98,15 +98,6 @@ __global__ __launch_bounds__(kAppendThreads) void k_kv_append3(
   }
 }
 
-// Attention workspace for any attended length in [1, S_cap]: the chunk count
-// is at most max(count at S_cap, 256 / B + 2) (chunks hold about S * B / 256
-// positions until a cap binds, which only happens at the largest lengths).
-size_t attn_ws_bound(int64_t B, int64_t S_cap, int64_t H, int64_t D) {
-  const size_t at_cap = attn_decode3_workspace_bytes(B, S_cap, H, D);
-  const size_t small = static_cast<size_t>(B) * H * (D + 4) * sizeof(float) * static_cast<size_t>(256 / B + 2);
-  return at_cap > small ? at_cap : small;
-}
-
 struct BlockWs {
   uint8_t* c4;
   float* sx4;
@@ -136,7 +127,7 @@ BlockWs block_ws(void* base, int64_t B, int64_t S_cap, int64_t H, int64_t D, int
   w.sx4 = reinterpret_cast<float*>(take(4 * B));
   w.y_qkv = reinterpret_cast<float*>(take(4 * static_cast<size_t>(B) * 3 * hd));
   w.att = reinterpret_cast<float*>(take(4 * static_cast<size_t>(B) * hd));
-  w.attn_ws = take(attn_ws_bound(B, S_cap, H, D));
+  w.attn_ws = take(attn_decode3_workspace_bound(B, S_cap, H, D));
   w.c8 = reinterpret_cast<int8_t*>(take(static_cast<size_t>(B) * hd));
   w.s8 = reinterpret_cast<float*>(take(4 * B));
   w.x1 = reinterpret_cast<float*>(take(4 * static_cast<size_t>(B) * hd));

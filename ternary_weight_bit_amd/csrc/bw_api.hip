@@ -288,6 +288,11 @@ bw_status bw_block_decode(const float* x, float* x_out, int64_t B, int64_t H, in
   const size_t need = bw::block_decode_workspace_bytes(B, S_cap, H, D, F);
   BW_REQUIRE(workspace_bytes >= need, BW_ERR_ARG, "bw_block_decode: workspace needs %zu bytes, got %zu", need,
              workspace_bytes);
+  // the attention region is sized for every attended length up to S_cap; the
+  // launch at this position must fit in it
+  BW_REQUIRE(bw::attn_decode3_workspace_bytes(B, pos + 1, H, D) <= bw::attn_decode3_workspace_bound(B, S_cap, H, D),
+             BW_ERR_UNSUPPORTED, "bw_block_decode: attention workspace at pos=%lld exceeds its region",
+             (long long)pos);
   return hip_status(bw::launch_block_decode(x, x_out, B, H, D, F, w_qkv, b_qkv, w_o, b_o, w_gate_up, b_gate_up, w_down,
                                             b_down, k_p3, k_s3, k_p4, k_s4, v_p3, v_s3, v_p4, v_s4, slot_of,
                                             n_special, S_cap, pos, workspace, static_cast<hipStream_t>(stream)),

@@ -61,6 +61,9 @@ constexpr int64_t kAttnLdsFloats = 16384;  // chunk scores + per-head max/sum in
 constexpr int64_t kAttnMaxH = 1024;
 bool attn_decode3_supported(int64_t B, int64_t S, int64_t H);  // S within the chunk x merge limits
 size_t attn_decode3_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D);
+// Workspace that covers every attended length S in [1, S_cap] (the decoder
+// layer attends over 0..pos of a cache of S_cap positions).
+size_t attn_decode3_workspace_bound(int64_t B, int64_t S_cap, int64_t H, int64_t D);
 hipError_t launch_attn_decode3(const float* q, const uint8_t* kp3, const float* ks3, const uint8_t* kp4,
                                const float* ks4, const uint8_t* vp3, const float* vs3, const uint8_t* vp4,
                                const float* vs4, const int32_t* slot_of, int64_t n_special, int64_t B, int64_t S,

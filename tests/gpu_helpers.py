@@ -48,3 +48,32 @@ def assert_same(a: np.ndarray, b: np.ndarray, what: str):
             f"{what}: {len(bad)} of {a.size} differ; first {bad[:5].tolist()}: "
             f"gpu {[a[tuple(i)] for i in bad[:5]]} ref {[b[tuple(i)] for i in bad[:5]]}"
         )
+
+
+U = 2.0**-24
+
+
+def gamma(n):
+    return n * U / (1 - n * U)
+
+
+def attn_bound(qd: np.ndarray, kd: np.ndarray, vd: np.ndarray, p: np.ndarray) -> np.ndarray:
+    """First-order rounding bound [D] on one fp32 single-token attention output
+    (fixed-point query, integer dot products, fp32 softmax and value sums) against
+    the exact evaluation over the same dequantized cache.  qd [D], kd / vd [S][D]
+    the dequantized keys / values (fp64), p [S] the exact softmax weights.  With
+    u = 2^-24 and gamma_n = n u / (1 - n u):
+      score error  E_z = max_s [gamma_D sum_d |q_d k_sd| + 2^-31 max|q| sum_d |k_sd|
+                               + 2^-23 max|q| s_s] / sqrt(D) + 4u |z_s|
+    (the second term is the query rounded to multiples of 2^-30 max|q| for the
+    integer dot products, the third the two fp32 roundings of the exact integer
+    sum at the position's scale s_s = max|k_s| / 3),
+      weight error E_p = 2 E_z + gamma_S + 2u,
+      |out_d - ref_d| <= (E_p + gamma_S + 2u) sum_s p_s |v_sd|  (+ 1e-30)."""
+    S, D = kd.shape
+    z = kd @ qd / np.sqrt(D)
+    s_pos = np.abs(kd).max(axis=1) / 3.0 + 1e-30
+    fixed = 2.0**-31 * np.abs(qd).max() * np.abs(kd).sum(axis=1) + 2.0**-23 * np.abs(qd).max() * s_pos
+    e_z = np.max((gamma(D) * (np.abs(kd) @ np.abs(qd)) + fixed) / np.sqrt(D) + 4 * U * np.abs(z))
+    e_p = 2 * e_z + gamma(S) + 2 * U
+    return (e_p + gamma(S) + 2 * U) * (p @ np.abs(vd)) + 1e-30

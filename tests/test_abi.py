@@ -151,3 +151,27 @@ def test_block_validation():
     assert f(*args(x=None)) == 1
     assert f(*args(nsp=3)) == 1  # side slabs missing
     assert f(*args(w=MIS)) == 3
+
+
+def _block_regions_except_attention(B, H, D, F):
+    """Bytes of the decoder layer's workspace regions other than the attention's,
+    each rounded up to 256 (codes, scales, q/k/v, attention output, INT8 codes,
+    scales, x1, gate/up, INT8 codes, scales)."""
+    r = lambda n: (n + 255) // 256 * 256
+    hd = H * D
+    return (r(B * hd // 2) + r(4 * B) + r(4 * B * 3 * hd) + r(4 * B * hd) + r(B * hd) + r(4 * B) + r(4 * B * hd)
+            + r(8 * B * F) + r(B * F) + r(4 * B))
+
+
+@pytest.mark.parametrize("H,D,S_cap", [(32, 128, 2048), (32, 128, 4096), (8, 64, 1500), (2, 128, 700)])
+def test_block_workspace_covers_attention_at_every_position(H, D, S_cap):
+    """For every batch size the layer takes and every attended length S <= S_cap, the
+    attention launch's workspace fits inside the attention region of the layer's
+    workspace (a launch at pos = S - 1 writes that many bytes)."""
+    F = 256
+    for B in range(1, 17):
+        total = bw.bw_block_decode_workspace_bytes(B, S_cap, H, D, F)
+        assert total > 0
+        region = total - _block_regions_except_attention(B, H, D, F)
+        worst = max(bw.bw_attn_decode_kv3_workspace_bytes(B, S, H, D) for S in range(1, S_cap + 1))
+        assert 0 < worst <= region, (B, worst, region)

@@ -21,15 +21,9 @@ import torch
 import synth
 import ternary_weight_bit_amd as bw
 from oracle import attn3, kv3
-from tests.gpu_helpers import bf16_dev, f32_dev, host
+from tests.gpu_helpers import attn_bound, bf16_dev, f32_dev, host
 
 pytestmark = pytest.mark.gpu
-
-U = 2.0**-24
-
-
-def gamma(n):
-    return n * U / (1 - n * U)
 
 
 def check_attention(q32, k16, v16, slot_of, n_special, label, pairs=None):
@@ -59,14 +53,7 @@ def check_attention(q32, k16, v16, slot_of, n_special, label, pairs=None):
         ref, p = attn3.decode_attention(q32[b : b + 1, h : h + 1], sub(okp), sub(ovp), so, D)
         kd = kv3.kv_unpack3(*sub(okp), so, D)[0, :, 0].astype(np.float64)  # [S][D]
         vd = kv3.kv_unpack3(*sub(ovp), so, D)[0, :, 0].astype(np.float64)
-        qd = q32[b, h].astype(np.float64)
-        z = kd @ qd / np.sqrt(D)
-        s_pos = np.abs(kd).max(axis=1) / 3.0 + 1e-30  # the position's scale (3-bit: max|k| = 3 s3)
-        fixed = 2.0**-31 * np.abs(qd).max() * np.abs(kd).sum(axis=1) + 2.0**-23 * np.abs(qd).max() * s_pos
-        e_z = np.max((gamma(D) * (np.abs(kd) @ np.abs(qd)) + fixed) / np.sqrt(D) + 4 * U * np.abs(z))
-        e_p = 2 * e_z + gamma(S) + 2 * U
-        mag = p[0, 0] @ np.abs(vd)  # [D]
-        bound = (e_p + gamma(S) + 2 * U) * mag + 1e-30
+        bound = attn_bound(q32[b, h].astype(np.float64), kd, vd, p[0, 0])
         err = np.abs(out[b, h].astype(np.float64) - ref[0, 0])
         bad = err > bound
         assert not bad.any(), (f"{label} (b={b}, h={h}): {int(bad.sum())} dims outside the bound; "

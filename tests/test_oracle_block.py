@@ -79,3 +79,96 @@ def test_handoff_is_the_fp32_epilogue():
     for m in range(3):
         for n in range(5):
             assert y[m, n] == np.float32(np.float32(np.float32(acc[m, n]) * s[m]) * b[n])
+
+
+def _run(w, seed=44, B=3, H=2, D=64, F=256, S=11, pos=7):
+    rs = np.random.default_rng(seed)
+    (kp, vp), slot_of, ns = _cache(rs, B, S, H, D)
+    x = rs.standard_normal((B, H * D)).astype(np.float32)
+    return block.decode_block(x, *w, kp, vp, slot_of, ns, pos, H), (kp, vp, slot_of, ns, x)
+
+
+def test_up_rows_enter_linearly_gate_rows_through_relu2():
+    """W_gate_up holds gate rows [0, F) and up rows [F, 2F).  The up branch enters
+    h linearly: negating the up rows negates h, keeps the same top-k survivors
+    (|h| unchanged), negates every INT8 code and so negates the down projection
+    exactly, x1 untouched.  The gate goes through ReLU^2: negating the gate rows
+    zeroes h where g was positive and opens it where g was negative, so the down
+    projection changes.  With gate and up swapped the first identity fails."""
+    rs = np.random.default_rng(45)
+    HD, F = 128, 256
+    w = list(_layer(rs, HD, F))
+    (x_out, _, _, mid), _ = _run(w)
+    w_up = list(w)
+    w_up[4] = np.concatenate([w[4][:F], -w[4][F:]])
+    (x_out2, _, _, mid2), _ = _run(w_up)
+    assert np.array_equal(mid2["x1"], mid["x1"])
+    assert np.array_equal(mid2["h_d"], -mid["h_d"])
+    assert np.array_equal(mid2["keep_d"], mid["keep_d"])
+    assert np.array_equal(mid2["q8d"], -mid["q8d"])
+    assert np.array_equal(mid2["y_d"], -mid["y_d"])
+    w_gate = list(w)
+    w_gate[4] = np.concatenate([-w[4][:F], w[4][F:]])
+    (_, _, _, mid3), _ = _run(w_gate)
+    assert np.array_equal(mid3["x1"], mid["x1"])
+    assert not np.array_equal(np.abs(mid3["y_d"]), np.abs(mid["y_d"]))
+    # h is zero exactly where the gate is not positive
+    assert np.array_equal(mid["h_d"] == 0, (mid["g"] <= 0) | (mid["u"] == 0))
+
+
+def test_zero_gate_rows_leave_x1():
+    """Gate rows all zero: g = 0, ReLU^2 gives 0, h = 0, every INT8 code is 0 and
+    x_out == x1 bit for bit."""
+    rs = np.random.default_rng(46)
+    HD, F = 128, 256
+    w = list(_layer(rs, HD, F))
+    w[4] = np.concatenate([np.zeros_like(w[4][:F]), w[4][F:]])
+    (x_out, _, _, mid), _ = _run(w)
+    assert not mid["q8d"].any() and not mid["y_d"].any()
+    assert np.array_equal(x_out, mid["x1"])
+
+
+def test_top_k_keeps_half_of_each_input():
+    """Exactly HD/2 of the out_proj inputs and F/2 of the down_proj inputs survive per
+    token, and every survivor's magnitude is at least every dropped one's."""
+    rs = np.random.default_rng(47)
+    HD, F = 128, 256
+    (_, _, _, mid), _ = _run(_layer(rs, HD, F))
+    for keep, h, k in ((mid["keep_o"], mid["att"], HD // 2), (mid["keep_d"], mid["h_d"], F // 2)):
+        assert (keep.sum(axis=1) == k).all()
+        for m in range(keep.shape[0]):
+            assert np.abs(h[m][keep[m]]).min() >= np.abs(h[m][~keep[m]]).max()
+        assert not np.any(np.where(keep, 0, 1) * (mid["q8"] if h is mid["att"] else mid["q8d"]))
+
+
+def test_query_is_the_first_slice():
+    """With the q rows of W_qkv zero every score is 0, so the attention output is
+    the plain mean of the dequantized values over positions 0..pos (the softmax of
+    equal scores is uniform).  Taking q from another slice would not give it."""
+    rs = np.random.default_rng(48)
+    HD, F, H, D, pos = 128, 256, 2, 64, 7
+    w = list(_layer(rs, HD, F))
+    w[0] = np.concatenate([np.zeros_like(w[0][:HD]), w[0][HD:]])
+    (_, _, vp2, mid), (kp, vp, slot_of, ns, x) = _run(w, H=H, D=D, pos=pos)
+    vd = kv3.kv_unpack3(vp2[0][:, : pos + 1], vp2[1][:, : pos + 1], vp2[2], vp2[3], slot_of[:, : pos + 1], D)
+    mean = vd.astype(np.float64).mean(axis=1).reshape(x.shape[0], HD)
+    assert np.allclose(mid["att"], mean, rtol=1e-6, atol=1e-7 * np.abs(mean).max())
+
+
+def test_key_and_value_slices_feed_their_caches():
+    """Zeroing the v rows of W_qkv (columns 2HD..3HD of y_qkv) writes all-zero codes at
+    pos into the V cache and leaves the K cache's new entry nonzero; zeroing the k
+    rows does the opposite."""
+    rs = np.random.default_rng(49)
+    HD, F, D, pos = 128, 256, 64, 7
+    base = list(_layer(rs, HD, F))
+    for zero_rows, zero_cache in ((slice(2 * HD, 3 * HD), 1), (slice(HD, 2 * HD), 0)):
+        w = list(base)
+        t = w[0].copy()
+        t[zero_rows] = 0
+        w[0] = t
+        (_, kp2, vp2, _), _ = _run(w, D=D, pos=pos)
+        caches = (kp2, vp2)
+        q_zero = kv3.planes_decode(caches[zero_cache][0][:, pos], D)
+        q_other = kv3.planes_decode(caches[1 - zero_cache][0][:, pos], D)
+        assert not q_zero.any() and q_other.any()
