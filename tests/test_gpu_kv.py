@@ -87,3 +87,21 @@ def test_full_layer_shape_sampled():
     assert_same(hs4[sp[special]].view(np.uint32), rs4[np.arange(len(bs))[special]].view(np.uint32), "full s4")
     rout = kv3.kv_unpack3(r3, rs3, r4, rs4, sub_slots, D)[0]
     assert_same(hout[bi, si], kv3.to_bf16_bits(rout), "full unpack bf16")
+
+
+def test_slot_ids_beyond_n_special_against_the_oracle():
+    """slot_of values >= n_special (and negative ones other than -1) mark ordinary
+    tokens on both sides: pack and unpack (fp32, bf16) bit-exact against the oracle
+    fed the same slot ids."""
+    B, S, H, D = 2, 40, 3, 128
+    x = synth.kv_tensor(seed=6, B=B, S=S, H=H, D=D)
+    slot_of, ns = synth.kv_special_slots(seed=6, B=B, S=S, frac=0.05)
+    slot_of[0, 5] = ns  # one past the last slot
+    slot_of[1, 9] = ns + 100
+    slot_of[1, 11] = -3
+    gpu, ref, sd = check_pack(bf16_dev(x), x.f32, slot_of, ns, "slot ids beyond n_special")
+    out = bw.bw_kv_unpack3(*gpu, sd, ns, out_dtype=torch.float32)
+    rout = kv3.kv_unpack3(*ref, slot_of, D)
+    assert_same(host(out).view(np.uint32), rout.view(np.uint32), "unpack f32")
+    outb = bw.bw_kv_unpack3(*gpu, sd, ns, out_dtype=torch.bfloat16)
+    assert_same(host(outb), kv3.to_bf16_bits(rout), "unpack bf16")
