@@ -19,7 +19,8 @@
  * Conventions (all calls):
  *   - Pointers are DEVICE pointers unless marked (host).  The caller allocates
  *     and owns every buffer; the library allocates nothing and keeps no
- *     device state.  Device pointers must be 16-byte aligned.
+ *     device state, except the one static workspace array per GPU that
+ *     bw_block_decode_noalloc uses.  Device pointers must be 16-byte aligned.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue work
  *     on it and return without waiting.
  *   - Arguments are validated on the host before anything is launched.  A
@@ -310,6 +311,34 @@ bw_status bw_block_decode(const float* x, float* x_out, int64_t B, int64_t H, in
                           uint8_t* v_p3, float* v_s3, uint8_t* v_p4, float* v_s4, const int32_t* slot_of,
                           int64_t n_special, int64_t S_cap, int64_t pos, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Decoder layer without allocation, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.
+ * Computes exactly what bw_block_decode computes, with the same arguments
+ * except the workspace, which is a static device array of
+ * bw_block_decode_noalloc_max_bytes() bytes (16 MiB) that the library holds on
+ * every GPU it runs on until the process ends.  The array of the current
+ * device (hipGetDevice) is used; `stream` must belong to that device.  The
+ * call allocates and frees nothing; its first call on a device looks up the
+ * array's device address there.
+ * A shape whose workspace (bw_block_decode_workspace_bytes) exceeds the array
+ * is rejected with BW_ERR_UNSUPPORTED before anything is launched (7B shapes:
+ * about 7 MB at 16 sequences).
+ * All calls on one GPU share that GPU's array, which keeps the last call's
+ * contents (nothing in it has to start at zero): calls that overlap on one GPU
+ * (on different streams, or from host threads without ordering) race; the
+ * caller serializes them.
+ * ------------------------------------------------------------------------ */
+/* host */ size_t bw_block_decode_noalloc_max_bytes(void);
+bw_status bw_block_decode_noalloc(const float* x, float* x_out, int64_t B, int64_t H, int64_t D, int64_t F,
+                                  const uint8_t* w_qkv, const float* b_qkv, const uint8_t* w_o, const float* b_o,
+                                  const uint8_t* w_gate_up, const float* b_gate_up, const uint8_t* w_down,
+                                  const float* b_down, uint8_t* k_p3, float* k_s3, uint8_t* k_p4, float* k_s4,
+                                  uint8_t* v_p3, float* v_s3, uint8_t* v_p4, float* v_s4,
+                                  const int32_t* slot_of, int64_t n_special, int64_t S_cap, int64_t pos,
+                                  void* stream);
 
 #ifdef __cplusplus
 }

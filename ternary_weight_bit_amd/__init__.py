@@ -20,7 +20,7 @@ __all__ = [
     "bw_ternary_packed_bytes", "bw_pack_ternary_workspace_bytes", "bw_pack_ternary", "bw_quantize",
     "bw_bitlinear_a4", "bw_quantize_sparse_a8", "bw_bitlinear_sparse_a8", "bw_kv_pack3", "bw_kv_unpack3",
     "bw_attn_decode_kv3_workspace_bytes", "bw_attn_decode_kv3", "bw_block_decode_workspace_bytes",
-    "bw_block_decode",
+    "bw_block_decode", "bw_block_decode_noalloc_max_bytes", "bw_block_decode_noalloc",
 ]
 
 BW_OK = 0
@@ -67,6 +67,8 @@ def _load() -> ctypes.CDLL:
         "bw_attn_decode_kv3": ([P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P, P, SZ, P], I),
         "bw_block_decode_workspace_bytes": ([I64, I64, I64, I64, I64], SZ),
         "bw_block_decode": ([P, P, I64, I64, I64, I64] + [P] * 8 + [P] * 8 + [P, I64, I64, I64, P, SZ, P], I),
+        "bw_block_decode_noalloc_max_bytes": ([], SZ),
+        "bw_block_decode_noalloc": ([P, P, I64, I64, I64, I64] + [P] * 8 + [P] * 8 + [P, I64, I64, I64, P], I),
     }
     for name, (argt, rest) in sig.items():
         fn = getattr(lib, name)
@@ -312,21 +314,12 @@ def bw_block_decode_workspace_bytes(B: int, S_cap: int, H: int, D: int, F: int) 
     return _lib.bw_block_decode_workspace_bytes(B, S_cap, H, D, F)
 
 
-def bw_block_decode(x: torch.Tensor, weights, k_pack, v_pack, slot_of: torch.Tensor, n_special: int, pos: int,
-                    H: int, x_out=None, workspace=None):
-    """One decoder layer for one new token per sequence.  x fp32 [B][H*D]; weights =
-    (w_qkv, b_qkv, w_o, b_o, w_gate_up, b_gate_up, w_down, b_down) from bw_pack_ternary;
-    k_pack / v_pack = (p3, s3, p4, s4) cache slabs [B][S_cap]...; returns x_out fp32 [B][H*D]."""
+def _block_args(x, weights, k_pack, v_pack, slot_of, n_special, pos, H, x_out):
     B, HD = x.shape
     D = HD // H
     w_qkv, b_qkv, w_o, b_o, w_gu, b_gu, w_down, b_down = weights
     F = b_gu.shape[0] // 2
     S_cap = k_pack[0].shape[1]
-    if x_out is None:
-        x_out = torch.empty_like(x)
-    if workspace is None:
-        workspace = torch.empty(max(bw_block_decode_workspace_bytes(B, S_cap, H, D, F), 16), dtype=torch.uint8,
-                                device=x.device)
     u8, f32 = (torch.uint8,), (torch.float32,)
     shp3, shs = (B, S_cap, H, 3 * D // 8), (B, S_cap, H)
     shp4, shs4 = (n_special, H, D // 2), (n_special, H)
@@ -334,12 +327,41 @@ def bw_block_decode(x: torch.Tensor, weights, k_pack, v_pack, slot_of: torch.Ten
     for name, (p3, s3, p4, s4) in (("k", k_pack), ("v", v_pack)):
         cache += [_dev(p3, name + "_p3", u8, shp3), _dev(s3, name + "_s3", f32, shs),
                   _opt(p4, name + "_p4", u8, shp4), _opt(s4, name + "_s4", f32, shs4)]
-    _check(_lib.bw_block_decode(
+    return [
         _dev(x, "x", f32, (B, HD)), _dev(x_out, "x_out", f32, (B, HD)), B, H, D, F,
         _dev(w_qkv, "w_qkv", u8, (3 * HD * HD // 4,)), _dev(b_qkv, "b_qkv", f32, (3 * HD,)),
         _dev(w_o, "w_o", u8, (HD * HD // 4,)), _dev(b_o, "b_o", f32, (HD,)),
         _dev(w_gu, "w_gate_up", u8, (2 * F * HD // 4,)), _dev(b_gu, "b_gate_up", f32, (2 * F,)),
         _dev(w_down, "w_down", u8, (HD * F // 4,)), _dev(b_down, "b_down", f32, (HD,)),
-        *cache, _dev(slot_of, "slot_of", (torch.int32,), (B, S_cap)), n_special, S_cap, pos,
-        _dev(workspace, "workspace", u8), workspace.numel(), _stream(x)))
+        *cache, _dev(slot_of, "slot_of", (torch.int32,), (B, S_cap)), n_special, S_cap, pos]
+
+
+def bw_block_decode(x: torch.Tensor, weights, k_pack, v_pack, slot_of: torch.Tensor, n_special: int, pos: int,
+                    H: int, x_out=None, workspace=None):
+    """One decoder layer for one new token per sequence.  x fp32 [B][H*D]; weights =
+    (w_qkv, b_qkv, w_o, b_o, w_gate_up, b_gate_up, w_down, b_down) from bw_pack_ternary;
+    k_pack / v_pack = (p3, s3, p4, s4) cache slabs [B][S_cap]...; returns x_out fp32 [B][H*D]."""
+    B, HD = x.shape
+    F = weights[5].shape[0] // 2
+    S_cap = k_pack[0].shape[1]
+    if x_out is None:
+        x_out = torch.empty_like(x)
+    if workspace is None:
+        workspace = torch.empty(max(bw_block_decode_workspace_bytes(B, S_cap, H, HD // H, F), 16),
+                                dtype=torch.uint8, device=x.device)
+    args = _block_args(x, weights, k_pack, v_pack, slot_of, n_special, pos, H, x_out)
+    _check(_lib.bw_block_decode(*args, _dev(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(x)))
+    return x_out
+
+
+def bw_block_decode_noalloc_max_bytes() -> int:
+    return _lib.bw_block_decode_noalloc_max_bytes()
+
+
+def bw_block_decode_noalloc(x: torch.Tensor, weights, k_pack, v_pack, slot_of: torch.Tensor, n_special: int,
+                            pos: int, H: int, x_out: torch.Tensor):
+    """bw_block_decode with the library's static per-GPU workspace: allocates nothing
+    (x_out, like every other buffer, is the caller's)."""
+    args = _block_args(x, weights, k_pack, v_pack, slot_of, n_special, pos, H, x_out)
+    _check(_lib.bw_block_decode_noalloc(*args, _stream(x)))
     return x_out

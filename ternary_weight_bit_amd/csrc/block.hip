@@ -18,9 +18,18 @@
 // out_proj GEMV with the residual added in its epilogue, quantizer, one
 // gate/up GEMV writing g and u as two [B][F] arrays, ReLU^2 top-k INT8, down
 // GEMV with the residual added in its epilogue.
+#include <mutex>
+
 #include "bw_internal.h"
 
 namespace bw {
+
+// Workspace of the allocation-free decoder-layer entry point: one array per
+// GPU, held from library load until the process ends.  Host code never uses
+// this name as an address (on the host it is only a stand-in for the symbol);
+// the device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) uint8_t scratch[kBlockScratchBytes];
+
 namespace {
 
 constexpr int kAppendThreads = 256;  // four waves, one (batch, head) vector each
@@ -148,6 +157,27 @@ BlockWs block_ws(void* base, int64_t B, int64_t S_cap, int64_t H, int64_t D, int
 
 size_t block_decode_workspace_bytes(int64_t B, int64_t S_cap, int64_t H, int64_t D, int64_t F) {
   return block_ws(nullptr, B, S_cap, H, D, F).bytes;
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once looked up
+}  // namespace
+
+hipError_t block_scratch(void** ptr) {
+  int dev = -1;
+  BW_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    BW_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));  // with device dev current
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_block_decode(const float* x, float* x_out, int64_t B, int64_t H, int64_t D, int64_t F,

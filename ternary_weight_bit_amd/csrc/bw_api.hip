@@ -263,6 +263,34 @@ size_t bw_block_decode_workspace_bytes(int64_t B, int64_t S_cap, int64_t H, int6
   return bw::block_decode_workspace_bytes(B, S_cap, H, D, F);
 }
 
+static bw_status check_block(const char* who, const float* x, float* x_out, int64_t B, int64_t H, int64_t D,
+                             int64_t F, const uint8_t* w_qkv, const float* b_qkv, const uint8_t* w_o,
+                             const float* b_o, const uint8_t* w_gate_up, const float* b_gate_up,
+                             const uint8_t* w_down, const float* b_down, uint8_t* k_p3, float* k_s3, uint8_t* k_p4,
+                             float* k_s4, uint8_t* v_p3, float* v_s3, uint8_t* v_p4, float* v_s4,
+                             const int32_t* slot_of, int64_t n_special, int64_t S_cap, int64_t pos) {
+  BW_REQUIRE(block_shape_ok(B, S_cap, H, D, F), BW_ERR_SHAPE,
+             "%s: need 1 <= B <= %lld, D = 64 or 128, H*D %% 64 == 0 and <= %lld, F %% 64 == 0 and "
+             "<= %lld, S_cap within the attention limits (B=%lld H=%lld D=%lld F=%lld S_cap=%lld)",
+             who, (long long)bw::kGemvMaxM, (long long)kMaxKSparse, (long long)kMaxKSparse, (long long)B,
+             (long long)H, (long long)D, (long long)F, (long long)S_cap);
+  BW_REQUIRE(pos >= 0 && pos < S_cap && n_special >= 0, BW_ERR_ARG,
+             "%s: need 0 <= pos < S_cap and n_special >= 0 (pos=%lld)", who, (long long)pos);
+  BW_REQUIRE(x && x_out && w_qkv && b_qkv && w_o && b_o && w_gate_up && b_gate_up && w_down && b_down && k_p3 &&
+                 k_s3 && v_p3 && v_s3 && slot_of,
+             BW_ERR_NULL, "%s: NULL pointer", who);
+  BW_REQUIRE(n_special == 0 || (k_p4 && k_s4 && v_p4 && v_s4), BW_ERR_NULL,
+             "%s: 4-bit slabs required when n_special > 0", who);
+  const void* ptrs[] = {x, x_out, w_qkv, b_qkv, w_o, b_o, w_gate_up, b_gate_up, w_down, b_down, k_p3, k_s3, k_p4,
+                        k_s4, v_p3, v_s3, v_p4, v_s4, slot_of};
+  for (const void* p : ptrs) BW_REQUIRE(!misaligned(p), BW_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", who);
+  // the attention region is sized for every attended length up to S_cap; the
+  // launch at this position must fit in it
+  BW_REQUIRE(bw::attn_decode3_workspace_bytes(B, pos + 1, H, D) <= bw::attn_decode3_workspace_bound(B, S_cap, H, D),
+             BW_ERR_UNSUPPORTED, "%s: attention workspace at pos=%lld exceeds its region", who, (long long)pos);
+  return ok();
+}
+
 bw_status bw_block_decode(const float* x, float* x_out, int64_t B, int64_t H, int64_t D, int64_t F,
                           const uint8_t* w_qkv, const float* b_qkv, const uint8_t* w_o, const float* b_o,
                           const uint8_t* w_gate_up, const float* b_gate_up, const uint8_t* w_down,
@@ -270,33 +298,45 @@ bw_status bw_block_decode(const float* x, float* x_out, int64_t B, int64_t H, in
                           uint8_t* v_p3, float* v_s3, uint8_t* v_p4, float* v_s4, const int32_t* slot_of,
                           int64_t n_special, int64_t S_cap, int64_t pos, void* workspace, size_t workspace_bytes,
                           void* stream) {
-  BW_REQUIRE(block_shape_ok(B, S_cap, H, D, F), BW_ERR_SHAPE,
-             "bw_block_decode: need 1 <= B <= %lld, D = 64 or 128, H*D %% 64 == 0 and <= %lld, F %% 64 == 0 and "
-             "<= %lld, S_cap within the attention limits (B=%lld H=%lld D=%lld F=%lld S_cap=%lld)",
-             (long long)bw::kGemvMaxM, (long long)kMaxKSparse, (long long)kMaxKSparse, (long long)B, (long long)H,
-             (long long)D, (long long)F, (long long)S_cap);
-  BW_REQUIRE(pos >= 0 && pos < S_cap && n_special >= 0, BW_ERR_ARG,
-             "bw_block_decode: need 0 <= pos < S_cap and n_special >= 0 (pos=%lld)", (long long)pos);
-  BW_REQUIRE(x && x_out && w_qkv && b_qkv && w_o && b_o && w_gate_up && b_gate_up && w_down && b_down && k_p3 &&
-                 k_s3 && v_p3 && v_s3 && slot_of && workspace,
-             BW_ERR_NULL, "bw_block_decode: NULL pointer");
-  BW_REQUIRE(n_special == 0 || (k_p4 && k_s4 && v_p4 && v_s4), BW_ERR_NULL,
-             "bw_block_decode: 4-bit slabs required when n_special > 0");
-  const void* ptrs[] = {x, x_out, w_qkv, b_qkv, w_o, b_o, w_gate_up, b_gate_up, w_down, b_down, k_p3, k_s3, k_p4,
-                        k_s4, v_p3, v_s3, v_p4, v_s4, slot_of, workspace};
-  for (const void* p : ptrs) BW_REQUIRE(!misaligned(p), BW_ERR_ALIGN, "bw_block_decode: device pointers must be 16-byte aligned");
+  bw_status st = check_block("bw_block_decode", x, x_out, B, H, D, F, w_qkv, b_qkv, w_o, b_o, w_gate_up, b_gate_up,
+                             w_down, b_down, k_p3, k_s3, k_p4, k_s4, v_p3, v_s3, v_p4, v_s4, slot_of, n_special,
+                             S_cap, pos);
+  if (st != BW_OK) return st;
+  BW_REQUIRE(workspace, BW_ERR_NULL, "bw_block_decode: NULL workspace");
+  BW_REQUIRE(!misaligned(workspace), BW_ERR_ALIGN, "bw_block_decode: device pointers must be 16-byte aligned");
   const size_t need = bw::block_decode_workspace_bytes(B, S_cap, H, D, F);
   BW_REQUIRE(workspace_bytes >= need, BW_ERR_ARG, "bw_block_decode: workspace needs %zu bytes, got %zu", need,
              workspace_bytes);
-  // the attention region is sized for every attended length up to S_cap; the
-  // launch at this position must fit in it
-  BW_REQUIRE(bw::attn_decode3_workspace_bytes(B, pos + 1, H, D) <= bw::attn_decode3_workspace_bound(B, S_cap, H, D),
-             BW_ERR_UNSUPPORTED, "bw_block_decode: attention workspace at pos=%lld exceeds its region",
-             (long long)pos);
   return hip_status(bw::launch_block_decode(x, x_out, B, H, D, F, w_qkv, b_qkv, w_o, b_o, w_gate_up, b_gate_up, w_down,
                                             b_down, k_p3, k_s3, k_p4, k_s4, v_p3, v_s3, v_p4, v_s4, slot_of,
                                             n_special, S_cap, pos, workspace, static_cast<hipStream_t>(stream)),
                     "bw_block_decode");
+}
+
+size_t bw_block_decode_noalloc_max_bytes(void) { return bw::kBlockScratchBytes; }
+
+bw_status bw_block_decode_noalloc(const float* x, float* x_out, int64_t B, int64_t H, int64_t D, int64_t F,
+                                  const uint8_t* w_qkv, const float* b_qkv, const uint8_t* w_o, const float* b_o,
+                                  const uint8_t* w_gate_up, const float* b_gate_up, const uint8_t* w_down,
+                                  const float* b_down, uint8_t* k_p3, float* k_s3, uint8_t* k_p4, float* k_s4,
+                                  uint8_t* v_p3, float* v_s3, uint8_t* v_p4, float* v_s4, const int32_t* slot_of,
+                                  int64_t n_special, int64_t S_cap, int64_t pos, void* stream) {
+  bw_status st = check_block("bw_block_decode_noalloc", x, x_out, B, H, D, F, w_qkv, b_qkv, w_o, b_o, w_gate_up,
+                             b_gate_up, w_down, b_down, k_p3, k_s3, k_p4, k_s4, v_p3, v_s3, v_p4, v_s4, slot_of,
+                             n_special, S_cap, pos);
+  if (st != BW_OK) return st;
+  const size_t need = bw::block_decode_workspace_bytes(B, S_cap, H, D, F);
+  BW_REQUIRE(need <= bw::kBlockScratchBytes, BW_ERR_UNSUPPORTED,
+             "bw_block_decode_noalloc: this shape needs %zu bytes of workspace, above the %zu-byte static scratch "
+             "(use bw_block_decode with a caller workspace)",
+             need, bw::kBlockScratchBytes);
+  void* ws = nullptr;
+  st = hip_status(bw::block_scratch(&ws), "bw_block_decode_noalloc (scratch address)");
+  if (st != BW_OK) return st;
+  return hip_status(bw::launch_block_decode(x, x_out, B, H, D, F, w_qkv, b_qkv, w_o, b_o, w_gate_up, b_gate_up, w_down,
+                                            b_down, k_p3, k_s3, k_p4, k_s4, v_p3, v_s3, v_p4, v_s4, slot_of,
+                                            n_special, S_cap, pos, ws, static_cast<hipStream_t>(stream)),
+                    "bw_block_decode_noalloc");
 }
 
 }  // extern "C"

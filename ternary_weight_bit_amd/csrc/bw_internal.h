@@ -78,6 +78,10 @@ hipError_t launch_attn_decode3_strided(const float* q, int64_t q_stride, const u
 
 // One decoder layer for one new token per sequence (block.hip).
 size_t block_decode_workspace_bytes(int64_t B, int64_t S_cap, int64_t H, int64_t D, int64_t F);
+// Static per-device workspace of the allocation-free variant: its size, and its
+// device address on the current device (looked up once per device).
+constexpr size_t kBlockScratchBytes = size_t(16) << 20;
+hipError_t block_scratch(void** ptr);
 hipError_t launch_block_decode(const float* x, float* x_out, int64_t B, int64_t H, int64_t D, int64_t F,
                                const uint8_t* w_qkv, const float* b_qkv, const uint8_t* w_o, const float* b_o,
                                const uint8_t* w_gu, const float* b_gu, const uint8_t* w_down, const float* b_down,

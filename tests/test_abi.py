@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -175,3 +175,21 @@ def test_block_workspace_covers_attention_at_every_position(H, D, S_cap):
         region = total - _block_regions_except_attention(B, H, D, F)
         worst = max(bw.bw_attn_decode_kv3_workspace_bytes(B, S, H, D) for S in range(1, S_cap + 1))
         assert 0 < worst <= region, (B, worst, region)
+
+
+def test_block_noalloc_validation():
+    """The allocation-free layer states its static workspace size and rejects, on the
+    host, a shape whose workspace would not fit (32 MB of attention partials for 16
+    sequences of 128 heads over 4096 positions) before it touches the device."""
+    assert bw.bw_block_decode_noalloc_max_bytes() == 16 << 20
+    f = lib.bw_block_decode_noalloc
+    B, H, D, F, S_cap = 16, 128, 128, 16384, 4096
+    assert bw.bw_block_decode_workspace_bytes(B, S_cap, H, D, F) > 16 << 20
+    args = lambda B, pos: [A, A, B, H, D, F] + [A] * 16 + [A, 1, S_cap, pos, None]
+    assert f(*args(B, 100)) == 7
+    assert "static scratch" in bw.bw_last_error()
+    assert f(*args(B, S_cap)) == 5  # pos out of range
+    assert f(*args(17, 100)) == 2
+    a = args(B, 100)
+    a[0] = None
+    assert f(*a) == 1
