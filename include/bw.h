@@ -154,6 +154,22 @@ bw_status bw_bitlinear_a4(const uint8_t* codes, const float* x_scales, int64_t M
                           int64_t N, float* y, void* acc_dbg, void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * 4-bit quantizer and W1.58A4 BitLinear in one call.
+ * Source: as bw_quantize and bw_bitlinear_a4 (BitNet a4.8 abstract: 4-bit
+ * activations for the attention and FFN inputs, INT4/FP4 kernels).
+ * Computes exactly bw_quantize(x) followed by bw_bitlinear_a4 on its codes:
+ * writes codes[M][K/2] and scales[M] (bw_quantize's bytes) and y[M][N]
+ * (bw_bitlinear_a4's values).  For one or two tokens (M <= 2, K <= 8192) it
+ * is one launch in which every workgroup quantizes the tokens itself;
+ * otherwise the two launches of the separate calls.
+ * acc_dbg: as bw_bitlinear_a4.
+ * Shapes: K % 64 == 0, K <= 131072, N % 16 == 0.  x dtype BW_F32 or BW_BF16.
+ * ------------------------------------------------------------------------ */
+bw_status bw_quantize_bitlinear_a4(const void* x, bw_dtype x_dtype, int64_t M, int64_t K, bw_act4_fmt fmt,
+                                   const uint8_t* w_packed, const float* beta, int64_t N, uint8_t* codes,
+                                   float* scales, float* y, void* acc_dbg, void* stream);
+
+/* ------------------------------------------------------------------------ *
  * Sparsified 8-bit activations (inputs of out_proj and down_proj).
  * Source: BitNet a4.8 abstract (intermediate states sparsified, then 8-bit);
  * toshoseti review «Метод» (top-k at 50 % for the out projection input;

@@ -18,7 +18,7 @@ __all__ = [
     "BW_ROLE_A8_KMAJOR", "bw_bitlinear_sparse_a8_gather_workspace_bytes", "bw_bitlinear_sparse_a8_gather",
     "BwError", "lib_path", "bw_abi_version", "bw_pack_layout_version", "bw_last_error",
     "bw_ternary_packed_bytes", "bw_pack_ternary_workspace_bytes", "bw_pack_ternary", "bw_quantize",
-    "bw_bitlinear_a4", "bw_quantize_sparse_a8", "bw_bitlinear_sparse_a8", "bw_kv_pack3", "bw_kv_unpack3",
+    "bw_bitlinear_a4", "bw_quantize_bitlinear_a4", "bw_quantize_sparse_a8", "bw_bitlinear_sparse_a8", "bw_kv_pack3", "bw_kv_unpack3",
     "bw_attn_decode_kv3_workspace_bytes", "bw_attn_decode_kv3", "bw_block_decode_workspace_bytes",
     "bw_block_decode", "bw_block_decode_noalloc_max_bytes", "bw_block_decode_noalloc",
 ]
@@ -57,6 +57,7 @@ def _load() -> ctypes.CDLL:
         "bw_pack_ternary": ([P, I, I64, I64, I, P, P, P, SZ, P], I),
         "bw_quantize": ([P, I, I64, I64, I, P, P, P], I),
         "bw_bitlinear_a4": ([P, P, I64, I64, I, P, P, I64, P, P, P], I),
+        "bw_quantize_bitlinear_a4": ([P, I, I64, I64, I, P, P, I64, P, P, P, P, P], I),
         "bw_quantize_sparse_a8": ([P, P, I, I64, I64, I64, P, P, P, P], I),
         "bw_bitlinear_sparse_a8": ([P, P, I64, I64, P, P, I64, P, P, P], I),
         "bw_bitlinear_sparse_a8_gather_workspace_bytes": ([I64, I64, I64], SZ),
@@ -186,6 +187,28 @@ def bw_bitlinear_a4(codes: torch.Tensor, x_scales: torch.Tensor, fmt: int, w_pac
         _dev(y, "y", (torch.float32,), (M, N)),
         _opt(acc_dbg, "acc_dbg", acc_dt, (M, N)), _stream(codes)))
     return y
+
+
+def bw_quantize_bitlinear_a4(x: torch.Tensor, fmt: int, w_packed: torch.Tensor, beta: torch.Tensor, y=None,
+                             codes=None, scales=None, acc_dbg=None):
+    """bw_quantize followed by bw_bitlinear_a4 in one call (one launch for M <= 2);
+    returns (y fp32 [M][N], codes uint8 [M][K/2], scales fp32 [M])."""
+    M, K = x.shape
+    N = beta.shape[0]
+    dev = x.device
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    if codes is None:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(M, dtype=torch.float32, device=dev)
+    acc_dt = (torch.int32,) if fmt == BW_ACT_INT4 else (torch.float32,)
+    _check(_lib.bw_quantize_bitlinear_a4(
+        _dev(x, "x", _FLOATS), _fdtype(x), M, K, fmt,
+        _dev(w_packed, "w_packed", (torch.uint8,), (N * K // 4,)), _dev(beta, "beta", (torch.float32,), (N,)), N,
+        _dev(codes, "codes", (torch.uint8,), (M, K // 2)), _dev(scales, "scales", (torch.float32,), (M,)),
+        _dev(y, "y", (torch.float32,), (M, N)), _opt(acc_dbg, "acc_dbg", acc_dt, (M, N)), _stream(x)))
+    return y, codes, scales
 
 
 def bw_quantize_sparse_a8(gate_or_x: torch.Tensor, up=None, k_keep=None, codes=None, scales=None,

@@ -17,7 +17,8 @@
 // Launches: quantizer, q/k/v GEMV, KV append, attention (2), top-k INT8,
 // out_proj GEMV with the residual added in its epilogue, quantizer, one
 // gate/up GEMV writing g and u as two [B][F] arrays, ReLU^2 top-k INT8, down
-// GEMV with the residual added in its epilogue.
+// GEMV with the residual added in its epilogue.  For one or two sequences the
+// quantizers run inside the q/k/v and gate/up GEMV launches (9 launches).
 #include <mutex>
 
 #include "bw_internal.h"
@@ -189,8 +190,14 @@ hipError_t launch_block_decode(const float* x, float* x_out, int64_t B, int64_t 
   const int64_t hd = H * D;
   const BlockWs w = block_ws(ws, B, S_cap, H, D, F);
   // attention input side: q/k/v projection and KV append
-  BW_TRY(launch_quantize_act4(x, false, B, hd, 0, w.c4, w.sx4, s));
-  BW_TRY(launch_bitlinear(0, w.c4, w.sx4, B, hd, w_qkv, b_qkv, 3 * hd, w.y_qkv, nullptr, s));
+  const bool fused = gemv_quant_supported(B, hd);  // quantizer inside the GEMV launch
+  if (fused) {
+    BW_TRY(launch_gemv_quant(x, false, 0, B, hd, w_qkv, b_qkv, 3 * hd, w.y_qkv, w.c4, w.sx4, nullptr, nullptr, 3 * hd,
+                             s));
+  } else {
+    BW_TRY(launch_quantize_act4(x, false, B, hd, 0, w.c4, w.sx4, s));
+    BW_TRY(launch_bitlinear(0, w.c4, w.sx4, B, hd, w_qkv, b_qkv, 3 * hd, w.y_qkv, nullptr, s));
+  }
   const dim3 agrid(static_cast<unsigned>((B * H + kAppendThreads / 64 - 1) / (kAppendThreads / 64)), 2);
   if (D == 64) {
     hipLaunchKernelGGL(k_kv_append3<64>, agrid, dim3(kAppendThreads), 0, s, w.y_qkv, 3 * hd, B, H, pos, S_cap,
@@ -206,8 +213,12 @@ hipError_t launch_block_decode(const float* x, float* x_out, int64_t B, int64_t 
   BW_TRY(launch_sparse_a8(w.att, nullptr, false, B, hd, hd / 2, w.c8, w.s8, nullptr, s));
   BW_TRY(launch_gemv_ex(2, w.c8, w.s8, B, hd, w_o, b_o, hd, w.x1, nullptr, x, hd, s));
   // feed-forward: gate and up on INT4 codes, ReLU^2 * up top-k 50 % INT8, down_proj, residual
-  BW_TRY(launch_quantize_act4(w.x1, false, B, hd, 0, w.c4, w.sx4, s));
-  BW_TRY(launch_gemv_ex(0, w.c4, w.sx4, B, hd, w_gu, b_gu, 2 * F, w.y_gu, nullptr, nullptr, F, s));
+  if (fused) {
+    BW_TRY(launch_gemv_quant(w.x1, false, 0, B, hd, w_gu, b_gu, 2 * F, w.y_gu, w.c4, w.sx4, nullptr, nullptr, F, s));
+  } else {
+    BW_TRY(launch_quantize_act4(w.x1, false, B, hd, 0, w.c4, w.sx4, s));
+    BW_TRY(launch_gemv_ex(0, w.c4, w.sx4, B, hd, w_gu, b_gu, 2 * F, w.y_gu, nullptr, nullptr, F, s));
+  }
   BW_TRY(launch_sparse_a8(w.y_gu, w.y_gu + B * F, false, B, F, F / 2, w.c8d, w.s8d, nullptr, s));
   BW_TRY(launch_gemv_ex(2, w.c8d, w.s8d, B, F, w_down, b_down, hd, x_out, nullptr, w.x1, hd, s));
   return hipSuccess;

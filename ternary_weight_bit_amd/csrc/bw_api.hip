@@ -117,6 +117,31 @@ bw_status bw_bitlinear_a4(const uint8_t* codes, const float* x_scales, int64_t M
                     "bw_bitlinear_a4");
 }
 
+bw_status bw_quantize_bitlinear_a4(const void* x, bw_dtype x_dtype, int64_t M, int64_t K, bw_act4_fmt fmt,
+                                   const uint8_t* w_packed, const float* beta, int64_t N, uint8_t* codes,
+                                   float* scales, float* y, void* acc_dbg, void* stream) {
+  BW_REQUIRE(x_dtype == BW_F32 || x_dtype == BW_BF16, BW_ERR_DTYPE, "bw_quantize_bitlinear_a4: bad dtype %d",
+             (int)x_dtype);
+  BW_REQUIRE(fmt == BW_ACT_INT4 || fmt == BW_ACT_FP4_E2M1, BW_ERR_DTYPE, "bw_quantize_bitlinear_a4: bad format %d",
+             (int)fmt);
+  bw_status st = check_gemm("bw_quantize_bitlinear_a4", codes, scales, M, K, w_packed, beta, N, y, acc_dbg);
+  if (st != BW_OK || M == 0) return st;
+  BW_REQUIRE(x, BW_ERR_NULL, "bw_quantize_bitlinear_a4: NULL pointer");
+  BW_REQUIRE(!misaligned(x), BW_ERR_ALIGN, "bw_quantize_bitlinear_a4: device pointers must be 16-byte aligned");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = x_dtype == BW_BF16;
+  const int f = fmt == BW_ACT_INT4 ? 0 : 1;
+  if (bw::gemv_quant_supported(M, K)) {
+    return hip_status(bw::launch_gemv_quant(x, bf16, f, M, K, w_packed, beta, N, y, codes, scales, acc_dbg, nullptr,
+                                            N, s),
+                      "bw_quantize_bitlinear_a4");
+  }
+  st = hip_status(bw::launch_quantize_act4(x, bf16, M, K, f, codes, scales, s), "bw_quantize_bitlinear_a4");
+  if (st != BW_OK) return st;
+  return hip_status(bw::launch_bitlinear(f, codes, scales, M, K, w_packed, beta, N, y, acc_dbg, s),
+                    "bw_quantize_bitlinear_a4");
+}
+
 bw_status bw_quantize_sparse_a8(const void* gate_or_x, const void* up, bw_dtype dtype, int64_t M, int64_t K,
                                 int64_t k_keep, int8_t* codes, float* scales, uint32_t* mask_dbg, void* stream) {
   BW_REQUIRE(dtype == BW_F32 || dtype == BW_BF16, BW_ERR_DTYPE, "bw_quantize_sparse_a8: bad dtype %d", (int)dtype);

@@ -29,6 +29,14 @@ hipError_t launch_gemv(int mode, const void* codes, const float* sx, int64_t M, 
 hipError_t launch_gemv_ex(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
                           const uint8_t* w_packed, const float* beta, int64_t N, float* y, void* acc_dbg,
                           const float* resid, int64_t split, hipStream_t s);
+// 4-bit quantizer and GEMV in one launch (every workgroup quantizes the token
+// rows itself; workgroup 0 also stores codes and scales): M <= 2, K <= 8192.
+constexpr int64_t kGemvQuantMaxM = 2;
+constexpr int64_t kGemvQuantMaxK = 8192;
+bool gemv_quant_supported(int64_t M, int64_t K);
+hipError_t launch_gemv_quant(const void* x, bool bf16, int fmt, int64_t M, int64_t K, const uint8_t* w_packed,
+                             const float* beta, int64_t N, float* y, uint8_t* codes, float* scales, void* acc_dbg,
+                             const float* resid, int64_t split, hipStream_t s);
 hipError_t launch_gemm(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
                        const uint8_t* w_packed, const float* beta, int64_t N, float* y, void* acc_dbg,
                        hipStream_t s);

@@ -12,27 +12,13 @@
 // read hits L2).  The absmax is exact and order-free.
 #include "bw_device.h"
 #include "bw_internal.h"
+#include "bw_quant.h"
 
 namespace bw {
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRowsPerBlock = kThreads / kWave;
-
-// INT4 code of t = fl(x * inv): clamp(rne(t), -8, 7) as a 4-bit field.
-__device__ __forceinline__ uint32_t int4_code(float t) {
-  const float q = fminf(fmaxf(__builtin_rintf(t), -8.0f), 7.0f);
-  return static_cast<uint32_t>(static_cast<int>(q)) & 0xFu;
-}
-
-// e2m1 code of t: nearest of {0,.5,1,1.5,2,3,4,6}; at a midpoint the
-// neighbour with the even code wins; saturates at 6; sign bit from t.
-__device__ __forceinline__ uint32_t e2m1_code(float t) {
-  const float m = fabsf(t);
-  uint32_t c = (m > 0.25f) + (m >= 0.75f) + (m > 1.25f) + (m >= 1.75f) + (m > 2.5f) + (m >= 3.5f) +
-               (m > 5.0f);
-  return c | ((__float_as_uint(t) >> 31) << 3);
-}
 
 template <int FMT>
 __device__ __forceinline__ uint32_t encode8(const float (&v)[8], float inv) {
