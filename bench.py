@@ -10,7 +10,11 @@ that are resident in HBM before timing starts:
                                      top-k 50% + INT8 of a Student-t(3) input (K=4096) -> W1.58A8 out_proj
   decode, M = 1, 2, 4, 8 tokens:     INT4 quantizer -> W1.58A4 GEMV over 32 layers of fused q/k/v
                                      (N=12288) and gate/up (N=22016) weights (1.12 GB, > 4x the
-                                     256 MB Infinity Cache, so weights stream from HBM)
+                                     256 MB Infinity Cache, so weights stream from HBM); the same as
+                                     one call (bw_quantize_bitlinear_a4: one launch for M <= 2);
+                                     a bare read of the same weight bytes in the GEMV's launch shape
+                                     (the read ceiling); one layer's q/k/v + gate/up projections on
+                                     a4.8's 4-bit path against b1.58's INT8 path
   decode down_proj / out_proj, M = 1: W1.58A8 GEMV on the tiled weights vs the gather product on
                                      K-major weights (reads only the rows of nonzero codes),
                                      32 layers each
@@ -37,8 +41,11 @@ bracketed rows a1 + a4 (each of which also pays its own launch latency).
 `b158_baseline` runs the same two projections on BitNet b1.58's activation
 path (INT8 absmax of every entry, no top-k, W1.58A8 GEMMs; row b0) and gives
 the ratio of the two.  `decode_gbs` is the decode GEMV rate in algorithmic
-bytes; `gather_decode_m1` sets the single-token gather product beside the
-tiled GEMV; `roofline` covers the N=11008 prefill GEMM.
+bytes (`decode_quant_gemv_gbs` with the quantizer in the same call);
+`decode_read_ceiling` sets each GEMV beside the bare read of its weight bytes;
+`decode_b158` compares the decode projections on the two activation paths;
+`gather_decode_m1` sets the single-token gather product beside the tiled
+GEMV; `roofline` covers the N=11008 prefill GEMM.
 """
 from __future__ import annotations
 
@@ -175,6 +182,18 @@ class Bench:
         # distinct addresses per layer (copies of one layer's packed bytes)
         self.layers = [(qkv_p.clone(), qkv_b.clone(), gu_p.clone(), gu_b.clone()) for _ in range(LAYERS)]
         del qkv_p, gu_p
+        # the same projections packed for 8-bit codes (BitNet b1.58's decode path)
+        qkv_p8 = t.empty(self.n_qkv * HIDDEN // 4, dtype=t.uint8, device=dev)
+        gu_p8 = t.empty(self.n_gu * HIDDEN // 4, dtype=t.uint8, device=dev)
+        for parts, seed, P, B in ((synth.QKV_PARTS, S + 21, qkv_p8, qkv_b), (synth.GATE_UP_PARTS, S + 22, gu_p8, gu_b)):
+            off = 0
+            for w in synth.fused_weights(seed, parts, HIDDEN):
+                n = w.shape[0]
+                bw.bw_pack_ternary(f32(w), bw.BW_ROLE_A8, P[off * HIDDEN // 4 : (off + n) * HIDDEN // 4], B[off : off + n])
+                off += n
+        self.layers8 = [(qkv_p8.clone(), gu_p8.clone()) for _ in range(LAYERS)]
+        del qkv_p8, gu_p8
+        self.sink = t.empty(4 * ((self.n_gu * HIDDEN // 4 + 16383) // 16384), dtype=t.int32, device=dev)
         self.dec = {}
         for M in DECODE_MS:
             xa = bf16(synth.decode_activations(S + 1 + M, M, HIDDEN))
@@ -185,6 +204,8 @@ class Bench:
                 cf=t.empty((M, HIDDEN // 2), dtype=t.uint8, device=dev), sf=t.empty(M, dtype=t.float32, device=dev),
                 ya=t.empty((M, self.n_qkv), dtype=t.float32, device=dev),
                 yf=t.empty((M, self.n_gu), dtype=t.float32, device=dev),
+                c8a=t.empty((M, HIDDEN), dtype=t.int8, device=dev), s8a=t.empty(M, dtype=t.float32, device=dev),
+                c8f=t.empty((M, HIDDEN), dtype=t.int8, device=dev), s8f=t.empty(M, dtype=t.float32, device=dev),
             )
         # ---------------- decode down_proj / out_proj, one token: sparsified INT8 codes
         # and 32 layers of weights in both the tiled and the K-major layout
@@ -322,6 +343,13 @@ class Bench:
                   [lambda: bw.bw_quantize_sparse_a8(self.x_out, None, HIDDEN // 2, self.c8_out, self.s8_out)]))
         R.append(("a9_gemm_a8_outproj", "TOPS", gemm_ops(M, HIDDEN, HIDDEN),
                   [lambda: bw.bw_bitlinear_sparse_a8(self.c8_out, self.s8_out, self.wp_o, self.b_o, self.y_o)]))
+
+        def quant_gemv_bytes(M, N, K):  # bf16 x in, codes + scales + y out, weights + beta
+            return N * K / 4 + 4 * N + 2 * M * K + M * K / 2 + 4 * M + 4 * M * N
+
+        def gemv8_bytes(M, N, K):
+            return N * K / 4 + 4 * N + M * K + 4 * M + 4 * M * N
+
         for Md in DECODE_MS:
             d = self.dec[Md]
             R.append((f"a1_quantize_int4_decode_m{Md}", "GB/s", Md * K * 2 + Md * K / 2 + 4 * Md,
@@ -333,6 +361,46 @@ class Bench:
             R.append((f"a5_gemv_gateup_m{Md}", "GB/s", gemv_bytes(Md, self.n_gu, K),
                       [lambda d=d, gp=gp, gb=gb: bw.bw_bitlinear_a4(d["cf"], d["sf"], bw.BW_ACT_INT4, gp, gb, d["yf"])
                        for _, _, gp, gb in self.layers]))
+            if Md == DECODE_MS[0]:
+                # read ceilings: the same 32 layers' weight bytes read once in the GEMV's access
+                # pattern, right behind GEMV rows (same cache state: no dirty output lines of the
+                # prefill rows left to write back)
+                R.append(("c0_read_qkv_weights", "GB/s", self.n_qkv * K / 4,
+                          [lambda qp=qp: bw.bw_stream_read(qp, self.sink) for qp, _, _, _ in self.layers]))
+                R.append(("c0_read_gateup_weights", "GB/s", self.n_gu * K / 4,
+                          [lambda gp=gp: bw.bw_stream_read(gp, self.sink) for _, _, gp, _ in self.layers]))
+            # the 4-bit quantizer and the GEMV as one call (one launch for M <= 2)
+            R.append((f"a5q_quant_gemv_qkv_m{Md}", "GB/s", quant_gemv_bytes(Md, self.n_qkv, K),
+                      [lambda d=d, qp=qp, qb=qb: bw.bw_quantize_bitlinear_a4(d["xa"], bw.BW_ACT_INT4, qp, qb, d["ya"],
+                                                                             d["ca"], d["sa"])
+                       for qp, qb, _, _ in self.layers]))
+            R.append((f"a5q_quant_gemv_gateup_m{Md}", "GB/s", quant_gemv_bytes(Md, self.n_gu, K),
+                      [lambda d=d, gp=gp, gb=gb: bw.bw_quantize_bitlinear_a4(d["xf"], bw.BW_ACT_INT4, gp, gb, d["yf"],
+                                                                             d["cf"], d["sf"])
+                       for _, _, gp, gb in self.layers]))
+            # decode projections of one layer on each activation path, 32 layers: a4.8 (4-bit
+            # codes for the q/k/v and gate/up inputs) against b1.58 (INT8 absmax of every entry,
+            # W1.58A8 GEMV), the comparison the pages' speed claim makes
+            # (each entry is one layer: the row's average is a per-layer time)
+            def a48_layer(d=d, qp=None, qb=None, gp=None, gb=None):
+                bw.bw_quantize_bitlinear_a4(d["xa"], bw.BW_ACT_INT4, qp, qb, d["ya"], d["ca"], d["sa"])
+                bw.bw_quantize_bitlinear_a4(d["xf"], bw.BW_ACT_INT4, gp, gb, d["yf"], d["cf"], d["sf"])
+
+            def b158_layer(d=d, qp8=None, qb=None, gp8=None, gb=None):
+                bw.bw_quantize_sparse_a8(d["xa"], None, K, d["c8a"], d["s8a"])
+                bw.bw_bitlinear_sparse_a8(d["c8a"], d["s8a"], qp8, qb, d["ya"])
+                bw.bw_quantize_sparse_a8(d["xf"], None, K, d["c8f"], d["s8f"])
+                bw.bw_bitlinear_sparse_a8(d["c8f"], d["s8f"], gp8, gb, d["yf"])
+
+            R.append((f"d0_decode_a48_m{Md}", "GB/s",
+                      quant_gemv_bytes(Md, self.n_qkv, K) + quant_gemv_bytes(Md, self.n_gu, K),
+                      [lambda qp=qp, qb=qb, gp=gp, gb=gb, f=a48_layer: f(qp=qp, qb=qb, gp=gp, gb=gb)
+                       for qp, qb, gp, gb in self.layers]))
+            R.append((f"d1_decode_b158_m{Md}", "GB/s",
+                      2 * (Md * K * 2 + Md * K + 4 * Md) + gemv8_bytes(Md, self.n_qkv, K)
+                      + gemv8_bytes(Md, self.n_gu, K),
+                      [lambda qp8=qp8, qb=qb, gp8=gp8, gb=gb, f=b158_layer: f(qp8=qp8, qb=qb, gp8=gp8, gb=gb)
+                       for (qp8, gp8), (_, qb, _, gb) in zip(self.layers8, self.layers)]))
         for name, o in self.one.items():
             K1, N1 = o["K"], o["N"]
             # tiled W1.58A8 GEMV: every weight byte; gather: only the rows of nonzero codes.
@@ -444,19 +512,29 @@ def vendor_gemm_reference(reps: int = 20):
     return out
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
 def cpu_baseline(target_s: float):
     """The oracle, as it stands, on a bounded sample of the W1.58A4 prefill work:
     INT4 quantizer + exact contraction + epilogue for a sample of token rows
-    against the N=11008 and N=4096 weights (already ternarized, as on the GPU side)."""
+    against the N=11008 and N=4096 weights (already ternarized, as on the GPU side),
+    once with every host thread the BLAS library uses and once on one thread."""
     import synth
     from oracle import act4, bitlinear, ternary
 
     try:
-        from threadpoolctl import threadpool_info
-
-        cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+        threadpool_info = threadpool_limits = None
     S = synth.SEED_BASE
     x = synth.prefill_activations(S + 2, M_PREFILL, HIDDEN).f32
     weights = []
@@ -470,23 +548,37 @@ def cpu_baseline(target_s: float):
             bitlinear.bitlinear_a4_int4(x[:rows], tq, beta)
         return time.perf_counter() - t0
 
-    rows = 32
-    dt = run(rows)
-    while dt < target_s / 4 and rows < M_PREFILL:
-        rows = min(M_PREFILL, rows * 4)
+    def leg(budget_s):
+        rows = 32
         dt = run(rows)
-    # the whole workload finishes well under the target: repeat it to about target_s
-    reps = max(1, min(64, int(target_s / max(dt, 1e-3))))
-    if reps > 1:
-        dt = sum(run(rows) for _ in range(reps))
-    ops = 2.0 * rows * HIDDEN * (FFN + HIDDEN) * reps
+        while dt < budget_s / 4 and rows < M_PREFILL:
+            rows = min(M_PREFILL, rows * 4)
+            dt = run(rows)
+        # the whole workload finishes well under the budget: repeat it to about budget_s
+        reps = max(1, min(64, int(budget_s / max(dt, 1e-3))))
+        if reps > 1:
+            dt = sum(run(rows) for _ in range(reps))
+        ops = 2.0 * rows * HIDDEN * (FFN + HIDDEN) * reps
+        return ops / dt / 1e12, rows, reps, dt
+
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1]) if threadpool_info else os.cpu_count()
+    v_all, rows, reps, dt = leg(target_s)
+    single = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            v1, rows1, reps1, dt1 = leg(target_s / 3)
+        single = {"value": v1, "unit": "TOPS", "cores": 1,
+                  "sample": f"{rows1} of 2048 token rows, {reps1} passes; {dt1:.1f} s"}
     return {
-        "value": ops / dt / 1e12,
+        "value": v_all,
         "unit": "TOPS",
-        "cores": int(cores),
+        "cores": int(threads),
         "kind": "oracle",
         "sample": f"W1.58A4 prefill (INT4 quantize + exact contraction + epilogue) on {rows} of 2048 token rows, "
                   f"K=4096, N=11008 and N=4096, {reps} passes; {dt:.1f} s",
+        "single_thread": single,
+        "cpu_model": _cpu_model(),
+        "logical_cpus": os.cpu_count(),
     }
 
 
@@ -565,6 +657,31 @@ def main():
     if gemv:
         dec_bytes = sum(table[n]["amount_per_launch"] * table[n]["launches_per_step"] for n in gemv)
         decode_gbs = dec_bytes / (row_ms(gemv) * 1e-3) / 1e9
+    decode_q = None
+    gemvq = [n for n in table if n.startswith("a5q_quant_gemv")]
+    if gemvq:
+        dq_bytes = sum(table[n]["amount_per_launch"] * table[n]["launches_per_step"] for n in gemvq)
+        decode_q = round(dq_bytes / (row_ms(gemvq) * 1e-3) / 1e9, 1)
+    # the GEMV against a bare read of the same weight bytes in the same launch shape
+    read_ceiling = {}
+    for proj in ("qkv", "gateup"):
+        rn = f"c0_read_{proj}_weights"
+        if rn not in table:
+            continue
+        e = {"read_us": table[rn]["avg_us"], "read_gbs": table[rn]["rate"],
+             "read_frac_hbm": table[rn]["frac_of_peak"]}
+        for Md in DECODE_MS:
+            for kind, gn in (("gemv", f"a5_gemv_{proj}_m{Md}"), ("quant_gemv", f"a5q_quant_gemv_{proj}_m{Md}")):
+                if gn in table:
+                    e[f"{kind}_m{Md}_us"] = table[gn]["avg_us"]
+                    e[f"{kind}_m{Md}_read_over_time"] = round(table[rn]["avg_us"] / table[gn]["avg_us"], 3)
+        read_ceiling[proj] = e
+    decode_b158 = {}
+    for Md in DECODE_MS:
+        a, b_ = f"d0_decode_a48_m{Md}", f"d1_decode_b158_m{Md}"
+        if a in table and b_ in table:
+            decode_b158[f"m{Md}"] = {"a48_us_per_layer": table[a]["avg_us"], "b158_us_per_layer": table[b_]["avg_us"],
+                                     "a48_over_b158_speed": round(table[b_]["avg_us"] / table[a]["avg_us"], 3)}
     block = None
     if "k12_block_decode_b8" in table:
         block = {"us_per_layer": table["k12_block_decode_b8"]["avg_us"],
@@ -622,6 +739,13 @@ def main():
         "block_decode": block,
         "decode_gbs": None if decode_gbs is None else round(decode_gbs, 1),
         "decode_frac_hbm": None if decode_gbs is None else round(decode_gbs / HBM_PEAK_GBS, 4),
+        "decode_quant_gemv_gbs": decode_q,
+        "decode_read_ceiling": read_ceiling or None,
+        "decode_b158": None if not decode_b158 else {
+            "basis": "one layer's q/k/v and gate/up projections for M tokens, 32 layers: a4.8 = 4-bit quantizer + "
+                     "W1.58A4 GEMV (bw_quantize_bitlinear_a4, one launch for M <= 2) per projection; b1.58 = INT8 "
+                     "absmax of every entry + W1.58A8 GEMV per projection; speed ratio = b1.58 time / a4.8 time",
+            **decode_b158},
         "roofline": roof,
         "rows": table,
         "wall_s_timed": round(wall, 3),

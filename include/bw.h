@@ -329,6 +329,19 @@ bw_status bw_block_decode(const float* x, float* x_out, int64_t B, int64_t H, in
                           size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * Streaming read (measurement aid, not a step of the method).
+ * Reads src[0, bytes) once in the access pattern of the decode GEMV's weight
+ * stream (one 256-thread workgroup per 16 KB block, each wave reading a 4 KB
+ * quarter with 16-byte loads, all of a lane's loads in flight before the
+ * first is used) and writes sink[4b + q] = XOR of the little-endian 32-bit
+ * words of quarter q of block b (a partial block reads zeros past `bytes`).
+ * Timing it beside bw_bitlinear_a4 on the same weight bytes gives the read
+ * ceiling of that launch shape.
+ * sink: device uint32 [4 * ceil(bytes / 16384)].  Shapes: bytes % 16 == 0.
+ * ------------------------------------------------------------------------ */
+bw_status bw_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
+
+/* ------------------------------------------------------------------------ *
  * Decoder layer without allocation, for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc.

@@ -20,7 +20,7 @@ __all__ = [
     "bw_ternary_packed_bytes", "bw_pack_ternary_workspace_bytes", "bw_pack_ternary", "bw_quantize",
     "bw_bitlinear_a4", "bw_quantize_bitlinear_a4", "bw_quantize_sparse_a8", "bw_bitlinear_sparse_a8", "bw_kv_pack3", "bw_kv_unpack3",
     "bw_attn_decode_kv3_workspace_bytes", "bw_attn_decode_kv3", "bw_block_decode_workspace_bytes",
-    "bw_block_decode", "bw_block_decode_noalloc_max_bytes", "bw_block_decode_noalloc",
+    "bw_block_decode", "bw_block_decode_noalloc_max_bytes", "bw_block_decode_noalloc", "bw_stream_read",
 ]
 
 BW_OK = 0
@@ -68,6 +68,7 @@ def _load() -> ctypes.CDLL:
         "bw_attn_decode_kv3": ([P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P, P, SZ, P], I),
         "bw_block_decode_workspace_bytes": ([I64, I64, I64, I64, I64], SZ),
         "bw_block_decode": ([P, P, I64, I64, I64, I64] + [P] * 8 + [P] * 8 + [P, I64, I64, I64, P, SZ, P], I),
+        "bw_stream_read": ([P, I64, P, P], I),
         "bw_block_decode_noalloc_max_bytes": ([], SZ),
         "bw_block_decode_noalloc": ([P, P, I64, I64, I64, I64] + [P] * 8 + [P] * 8 + [P, I64, I64, I64, P], I),
     }
@@ -375,6 +376,19 @@ def bw_block_decode(x: torch.Tensor, weights, k_pack, v_pack, slot_of: torch.Ten
     args = _block_args(x, weights, k_pack, v_pack, slot_of, n_special, pos, H, x_out)
     _check(_lib.bw_block_decode(*args, _dev(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(x)))
     return x_out
+
+
+def bw_stream_read(src: torch.Tensor, sink=None):
+    """Measurement aid: read src's bytes once in the decode GEMV's access pattern; returns
+    sink uint32 [4 * ceil(bytes / 16384)], the XOR of each 4 KB quarter's 32-bit words."""
+    nbytes = src.numel() * src.element_size()
+    if sink is None:
+        sink = torch.empty(4 * ((nbytes + 16383) // 16384), dtype=torch.int32, device=src.device)
+    elif sink.numel() < 4 * ((nbytes + 16383) // 16384):
+        raise ValueError("sink needs 4 * ceil(bytes / 16384) words")
+    _check(_lib.bw_stream_read(_dev(src, "src"), nbytes, _dev(sink, "sink", (torch.int32, torch.uint32)),
+                               _stream(src)))
+    return sink
 
 
 def bw_block_decode_noalloc_max_bytes() -> int:

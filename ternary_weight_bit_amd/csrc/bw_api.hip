@@ -338,6 +338,15 @@ bw_status bw_block_decode(const float* x, float* x_out, int64_t B, int64_t H, in
                     "bw_block_decode");
 }
 
+bw_status bw_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+  BW_REQUIRE(bytes >= 0 && bytes % 16 == 0 && bytes < (int64_t(1) << 40), BW_ERR_SHAPE,
+             "bw_stream_read: need 0 <= bytes < 2^40 and bytes %% 16 == 0 (bytes=%lld)", (long long)bytes);
+  if (bytes == 0) return ok();
+  BW_REQUIRE(src && sink, BW_ERR_NULL, "bw_stream_read: NULL pointer");
+  BW_REQUIRE(!misaligned(src) && !misaligned(sink), BW_ERR_ALIGN, "bw_stream_read: device pointers must be 16-byte aligned");
+  return hip_status(bw::launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream)), "bw_stream_read");
+}
+
 size_t bw_block_decode_noalloc_max_bytes(void) { return bw::kBlockScratchBytes; }
 
 bw_status bw_block_decode_noalloc(const float* x, float* x_out, int64_t B, int64_t H, int64_t D, int64_t F,

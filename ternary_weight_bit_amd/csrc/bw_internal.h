@@ -97,6 +97,10 @@ hipError_t launch_block_decode(const float* x, float* x_out, int64_t B, int64_t 
                                uint8_t* vp4, float* vs4, const int32_t* slot_of, int64_t n_special, int64_t S_cap,
                                int64_t pos, void* ws, hipStream_t s);
 
+// Streaming read of `bytes` bytes (measurement): sink[4b + q] = XOR of the
+// 32-bit words of 4 KB quarter q of 16 KB block b.
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s);
+
 hipError_t launch_kv_pack3(const void* kv, bool bf16, int64_t B, int64_t S, int64_t H, int64_t D,
                            const int32_t* slot_of, int64_t n_special, uint8_t* p3, float* s3,
                            uint8_t* p4, float* s4, hipStream_t s);

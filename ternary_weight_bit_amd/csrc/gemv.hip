@@ -101,8 +101,10 @@ __device__ __forceinline__ void gemv_epilogue(typename TileOps<MODE>::acc_t acc,
   const int g = lane >> 4;
   const int64_t n = nb * 16 + (lane & 15);
   // output plane of this column: columns [p*split, (p+1)*split) go to the
-  // row-major [M][split] plane p (split = N: the plain [M][N] layout)
-  const int64_t plane = n / split;
+  // row-major [M][split] plane p (split = N: the plain [M][N] layout; 32-bit
+  // division, N < 2^31)
+  const int64_t plane =
+      (split == N) ? 0 : static_cast<int64_t>(static_cast<uint32_t>(n) / static_cast<uint32_t>(split));
   float* __restrict__ yp = y + plane * M * split;
   const int64_t nc = n - plane * split;
 #pragma unroll
