@@ -12,16 +12,10 @@
 
 namespace bw {
 
-// INT4 code of t as a 4-bit field: clamp(rne(t), -8, 7).
-__device__ __forceinline__ uint32_t int4_code(float t) {
-  const float q = fminf(fmaxf(__builtin_rintf(t), -8.0f), 7.0f);
-  return static_cast<uint32_t>(static_cast<int>(q)) & 0xFu;
-}
-
-// Same code for |t| <= 7.5 (always the case for an absmax scale:
-// |x * fl(7/a')| <= 7 (1 + 2^-24)): adding 1.5 * 2^23 rounds t to an integer
-// with ties to even, and the low 4 bits of the sum are that integer in two's
-// complement; the clamp can never act.
+// INT4 code clamp(rne(t), -8, 7) as a 4-bit field, for |t| <= 7.5 (always the
+// case for an absmax scale: |x * fl(7/a')| <= 7 (1 + 2^-24)): adding 1.5 * 2^23
+// rounds t to an integer with ties to even, and the low 4 bits of the sum are
+// that integer in two's complement; the clamp can never act.
 __device__ __forceinline__ uint32_t int4_code_absmax(float t) {
   return __float_as_uint(t + 12582912.0f) & 0xFu;
 }

@@ -20,15 +20,13 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kRowsPerBlock = kThreads / kWave;
 
+// Eight codes as one word (even k in the low nibble).  inv = fl(qmax / a') with
+// a' >= max|v|, so act4_code's INT4 rounding add applies (no clamp needed).
 template <int FMT>
 __device__ __forceinline__ uint32_t encode8(const float (&v)[8], float inv) {
   uint32_t w = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float t = mul_rn(v[i], inv);
-    const uint32_t c = (FMT == 0) ? int4_code(t) : e2m1_code(t);
-    w |= c << (4 * i);
-  }
+  for (int i = 0; i < 8; ++i) w |= act4_code<FMT>(v[i], inv) << (4 * i);
   return w;
 }
 
@@ -74,17 +72,42 @@ __global__ __launch_bounds__(kThreads) void k_quantize_act4_row(const void* __re
   const int64_t nchunk = K >> 3;
   const int64_t row = m * K;
   float v[CPT][8];
-#pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    const int64_t ch = tid + c * kThreads;
-    load8<BF16>(x, row + (ch < nchunk ? ch : 0) * 8, v[c]);
-  }
   uint32_t amax = 0;  // |x| bits: non-negative floats order as integers
+  if constexpr (BF16) {
+    // raw bf16 words: the row maximum on packed 16-bit magnitudes (one masked
+    // max per two elements), widened once at the end
+    typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+    us2 m2 = {0, 0};
+    uint4 w[CPT];
 #pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    const bool in_row = tid + c * kThreads < nchunk;
+    for (int c = 0; c < CPT; ++c) {
+      const int64_t ch = tid + c * kThreads;
+      w[c] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + row + (ch < nchunk ? ch : 0) * 8);
+    }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = max(amax, in_row ? (__float_as_uint(v[c][i]) & 0x7FFFFFFFu) : 0u);
+    for (int c = 0; c < CPT; ++c) {
+      const uint32_t keep = (tid + c * kThreads < nchunk) ? 0x7FFF7FFFu : 0u;
+      const uint32_t ws[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(us2, ws[j] & keep));
+        v[c][2 * j] = bf16_lo(ws[j]);
+        v[c][2 * j + 1] = bf16_hi(ws[j]);
+      }
+    }
+    amax = static_cast<uint32_t>(m2.x > m2.y ? m2.x : m2.y) << 16;
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int64_t ch = tid + c * kThreads;
+      load8<BF16>(x, row + (ch < nchunk ? ch : 0) * 8, v[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const bool in_row = tid + c * kThreads < nchunk;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = max(amax, in_row ? (__float_as_uint(v[c][i]) & 0x7FFFFFFFu) : 0u);
+    }
   }
   amax = static_cast<uint32_t>(lane_value(static_cast<int>(wave_incl_umax(amax)), kWave - 1));
   if ((tid & (kWave - 1)) == 0) wmax[tid / kWave] = amax;
