@@ -14,6 +14,31 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
 
+// Raw buffer resources: a load whose byte offset (the vector offset) lies at or
+// past the resource size returns zeros without touching memory.
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+constexpr uint32_t kOutOfRange = 0x80000000u;  // above every resource size used here
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), kRsrcWord3);
+}
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ void bload12(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t (&w)[3]) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+  w[0] = v[0];
+  w[1] = v[1];
+  w[2] = v[2];
+}
+
+__device__ __forceinline__ float bload_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

@@ -37,18 +37,6 @@
 namespace bw {
 namespace {
 
-constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
-constexpr uint32_t kOutOfRange = 0x80000000u;  // above every resource size used here
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), kRsrcWord3);
-}
-
-__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
 template <int MODE>
 struct TileOps {
   static constexpr int AW = (MODE == MODE_INT8) ? 4 : 2;  // 16-byte activation parts per tile

@@ -8,13 +8,11 @@
 // writes sink[4 * block + w] (no LDS, no barrier: each wave ends on its own,
 // as the GEMV's waves end on their data).  A bytes % 16384 tail reads zeros
 // past the end.
+#include "bw_device.h"
 #include "bw_internal.h"
 
 namespace bw {
 namespace {
-
-constexpr int kRsrcWord3 = 0x00020000;
-constexpr uint32_t kOutOfRange = 0x80000000u;
 
 // XOR over the 64 lanes (DPP row shifts, then the row results carried across
 // rows); lane 63 ends with the total.

@@ -122,3 +122,33 @@ def test_query_with_one_huge_entry():
     q = q.copy()
     q[0, :, 5] = np.float32(3.0e4)
     check_attention(q, k, v, slot_of, ns, "huge q entry")
+
+
+def test_chunk_at_lds_cap_sampled():
+    """128 heads of 64 dims over 8 x 4096 positions: the chunk is cut to the largest
+    one whose scores fit the LDS budget (124 positions, 34 chunks instead of 32), so
+    the workgroup holds its largest score array beside the phase-sum buffer.  The
+    oracle packs only the sampled heads (the codec works per vector)."""
+    B, S, H, D = 8, 4096, 128, 64
+    assert bw.bw_attn_decode_kv3_workspace_bytes(B, S, H, D) == B * 34 * H * (D + 4) * 4
+    seed = synth.SEED_BASE + 86
+    k16 = synth.kv_tensor(seed, B, S, H, D)
+    v16 = synth.kv_tensor(seed + 1, B, S, H, D)
+    q32 = synth.normal(seed + 2, (B, H, D))
+    slot_of, ns = synth.kv_special_slots(seed, B, S)
+    print(f"case LDS cap: B={B} S={S} H={H} D={D} specials={int((slot_of >= 0).sum())}", flush=True)
+    sl = torch.from_numpy(slot_of).to("cuda:0")
+    kp = bw.bw_kv_pack3(bf16_dev(k16), sl, ns)
+    vp = bw.bw_kv_pack3(bf16_dev(v16), sl, ns)
+    out = host(bw.bw_attn_decode_kv3(f32_dev(q32), kp, vp, sl, ns))
+    assert np.isfinite(out).all()
+    for b, h in [(0, 0), (7, 127), (3, 64), (5, 1), (2, 126), (6, 77)]:
+        so = slot_of[b : b + 1]
+        okp = kv3.kv_pack3(k16.f32[b : b + 1, :, h : h + 1], so, ns)
+        ovp = kv3.kv_pack3(v16.f32[b : b + 1, :, h : h + 1], so, ns)
+        ref, p = attn3.decode_attention(q32[b : b + 1, h : h + 1], okp, ovp, so, D)
+        kd = kv3.kv_unpack3(*okp, so, D)[0, :, 0].astype(np.float64)
+        vd = kv3.kv_unpack3(*ovp, so, D)[0, :, 0].astype(np.float64)
+        bound = attn_bound(q32[b, h].astype(np.float64), kd, vd, p[0, 0])
+        err = np.abs(out[b, h].astype(np.float64) - ref[0, 0])
+        assert not (err > bound).any(), f"LDS cap (b={b}, h={h}): worst err/bound {float((err / bound).max()):.3g}"
