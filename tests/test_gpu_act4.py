@@ -65,6 +65,30 @@ def test_edge_rows(fmt, name):
     check(f32_dev(x), x, fmt, f"edge rows {name}")
 
 
+@pytest.mark.parametrize("fmt,name", FMTS)
+@pytest.mark.parametrize("M,K", [(1024, 64), (1027, 1088), (1030, 2048), (1025, 2112), (1029, 4096)])
+def test_many_rows(fmt, name, M, K):
+    """Over a thousand rows of up to 4096 entries (ragged chunk counts per thread),
+    bf16 and fp32 inputs."""
+    x = synth.to_bf16(synth.normal(17 + M + K, (M, K)) * np.float32(2.5))
+    check(bf16_dev(x), x.f32, fmt, f"bf16 {M}x{K} {name}")
+    check(f32_dev(x.f32), x.f32, fmt, f"fp32 {M}x{K} {name}")
+
+
+@pytest.mark.parametrize("fmt,name", FMTS)
+def test_edge_rows_many(fmt, name):
+    """The edge rows repeated over 1032 rows."""
+    K = 128
+    base = np.array([
+        np.zeros(K), np.full(K, -2.5), np.where(np.arange(K) % 2, 1e-30, -1e-30),
+        np.where(np.arange(K) % 3 == 0, 3e30, 1.0), np.linspace(-7, 7, K),
+        np.tile([6, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], K // 8) * np.where(np.arange(K) % 2, 1, -1),
+        np.r_[[-0.0] * (K // 2), [1e-5] * (K // 2)], np.r_[[7.0], np.full(K - 1, 3.5)],
+    ], dtype=np.float32)
+    x = np.tile(base, (129, 1))
+    check(f32_dev(x), x, fmt, f"edge rows x129 {name}")
+
+
 def test_full_prefill_shape_sampled():
     """2048 x 4096 bf16: all scales, codes of 64 sampled rows."""
     x = synth.prefill_activations()
