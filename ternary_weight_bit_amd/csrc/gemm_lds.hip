@@ -42,7 +42,6 @@ constexpr int BM = 128;
 constexpr int BN = 256;
 constexpr int WN = 4;
 constexpr int kBStage = BN * 2 * 16;  // [group 16][slab 2][column 16] x 16 B
-constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
 #define BW_GP(p) ((const __attribute__((address_space(1))) void*)(p))
 #define BW_LP(p) ((__attribute__((address_space(3))) void*)(p))
