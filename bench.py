@@ -701,7 +701,7 @@ def main():
     if "a4_gemm_int4_n11008" in table:
         dom = table["a4_gemm_int4_n11008"]
         roof = {
-            "bound": "mfma", "kernel": "k_gemm_lds<INT4> (W1.58A4 GEMM, M=2048 K=4096 N=11008)",
+            "bound": "mfma", "kernel": "k_gemm_lds256<INT4> (W1.58A4 GEMM, M=2048 K=4096 N=11008)",
             "achieved": dom["rate"], "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
             "frac": round(dom["rate"] / INT8_PEAK_TOPS, 4), "traffic": gemm_traffic_bytes(),
             "note": "int8 MFMA int-ops (2*M*N*K per launch) / average launch duration from HIP events; "

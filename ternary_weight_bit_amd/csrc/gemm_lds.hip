@@ -279,6 +279,198 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
   }
 }
 
+
+// 4-bit codes with K a multiple of 256: stages of 256 k in two LDS buffers.
+// The same prefetch window as the three-buffer ring of 128-k stages (stage
+// st + 1 loads while stage st computes) with half the workgroup barriers.
+// Activation rows hold 128 bytes per stage (eight 16-byte parts, swizzled by
+// row / 2); weights keep their packed order, four 64-k slabs per column group.
+// The copies into LDS are issued from inline asm (`lds_copy16`): the
+// compiler then adds no wait for them before the fragment reads, which with
+// two buffers would stall each stage on the loads just issued for the next;
+// the wait for a stage's own copies is explicit (vmcnt before the barrier).
+__device__ __forceinline__ int a_slot256(int row, int p) { return p ^ ((row >> 1) & 7); }
+
+// 16 bytes per lane from a buffer resource into LDS at `lds` + 16 * lane.
+__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, const uint8_t* lds, uint32_t voff, int soff) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m), "v"(voff), "s"(r), "s"(soff)
+               : "memory", "m0");
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_gemm_lds256(
+    const uint8_t* __restrict__ A, const float* __restrict__ sx, int64_t M, int64_t K,
+    const uint8_t* __restrict__ Wp, const float* __restrict__ beta, int64_t N, float* __restrict__ y,
+    void* __restrict__ acc_dbg, int MT, int NT) {
+  static_assert(MODE != MODE_INT8, "4-bit codes only");
+  constexpr int AROW = 128;           // bytes per activation row per stage (256 codes)
+  constexpr int AStage = BM * AROW;   // 16 KB
+  constexpr int BStage = BN * 64;     // 16 KB: [group 16][slab 4][column 16] x 16 B
+  __shared__ __attribute__((aligned(1024))) uint8_t A0[AStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t A1[AStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t B0[BStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t B1[BStage];
+  __shared__ float sxs[BM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  const int li = lane & 31;
+  const int lh = lane >> 5;
+
+  const int T = MT * NT;
+  const int b = blockIdx.x;
+  const int t = (T % 8 == 0) ? (b % 8) * (T / 8) + b / 8 : b;
+  const int64_t m0 = static_cast<int64_t>(t % MT) * BM;
+  const int64_t n0 = static_cast<int64_t>(t / MT) * BN;
+  const int64_t kblocks = K >> 6;
+  const int64_t nst = K >> 8;
+  const int64_t a_row = K >> 1;
+
+  // A: copy j of wave w fills rows 8 (2w + j) .. + 7; lane i -> row + i / 8, LDS
+  // slot i % 8, which holds the row's part a_slot256(row, i % 8) (an involution).
+  const int64_t m_last = (M - 1 - m0 < BM - 1) ? M - 1 - m0 : BM - 1;
+  uint32_t aoff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = 8 * (2 * wave + j) + lane / 8;
+    const int part = a_slot256(row, lane % 8);
+    aoff[j] = static_cast<uint32_t>((row < m_last ? row : m_last) * a_row + part * 16);
+  }
+  // B: copy j of wave w fills column group 2w + j, all four slabs: lane i ->
+  // slab i / 16, column i % 16.
+  const int64_t ng = N >> 4;
+  const int64_t g_first = n0 >> 4;
+  uint32_t boff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t g0 = 2 * wave + j;
+    const int64_t gl = (g_first + g0 < ng) ? g0 : ng - 1 - g_first;
+    boff[j] = static_cast<uint32_t>((gl * kblocks + (lane >> 4)) * 256 + (lane & 15) * 16);
+  }
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(A + m0 * a_row), 0, static_cast<int>((M - m0) * a_row), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t brsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(Wp + g_first * kblocks * 256), 0, static_cast<int>((ng - g_first) * kblocks * 256),
+      kRsrcWord3);
+  const int64_t rot = ((t % MT) % 4) * (nst / 4);  // as in k_gemm_lds
+  auto issue = [&](int64_t st_req, uint8_t* As, uint8_t* Bs) {
+    int64_t sp = st_req + rot;
+    if (sp >= nst) sp -= nst;
+    const int st = static_cast<int>(sp);
+    const int sa = st * AROW;
+    const int sb = st * 1024;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) lds_copy16(arsrc, As + (2 * wave + j) * 1024, aoff[j], sa);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) lds_copy16(brsrc, Bs + (2 * wave + j) * 1024, boff[j], sb);
+  };
+
+  using acc_t = typename std::conditional<MODE == MODE_FP4, v16f, v16i>::type;
+  acc_t acc[2][2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[r][c][e] = 0;
+
+  auto compute = [&](const uint8_t* As, const uint8_t* Bs) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int col = wn * 64 + li;
+      int o0 = ((col >> 4) * 4 + s) * 256 + (col & 15) * 16 + 8 * lh;
+      int o1 = o0 + 2048;
+      asm volatile("" : "+v"(o0), "+v"(o1));
+      const uint2 w0 = *reinterpret_cast<const uint2*>(Bs + o0);
+      const uint2 w1 = *reinterpret_cast<const uint2*>(Bs + o1);
+      if constexpr (MODE == MODE_FP4) {
+        const v8i b0 = fp4_weights(w0.x, w0.y);
+        const v8i b1 = fp4_weights(w1.x, w1.y);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int row = wm * 64 + r * 32 + li;
+          const uint4 x = *reinterpret_cast<const uint4*>(As + row * AROW + 16 * a_slot256(row, 2 * s + lh));
+          const v8i a = fp4_operand(x.x, x.y, x.z, x.w);
+          acc[r][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b0, a, acc[r][0], 4, 4, 0, 127, 0, 127);
+          acc[r][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b1, a, acc[r][1], 4, 4, 0, 127, 0, 127);
+        }
+      } else {
+        const v4i b00 = widen_w_a4(w0.x), b01 = widen_w_a4(w0.y);
+        const v4i b10 = widen_w_a4(w1.x), b11 = widen_w_a4(w1.y);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int row = wm * 64 + r * 32 + li;
+          const uint4 x = *reinterpret_cast<const uint4*>(As + row * AROW + 16 * a_slot256(row, 2 * s + lh));
+          const v4i a0 = widen_int4(x.x, x.y);
+          const v4i a1 = widen_int4(x.z, x.w);
+          acc[r][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b00, a0, acc[r][0], 0, 0, 0);
+          acc[r][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b10, a0, acc[r][1], 0, 0, 0);
+          acc[r][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b01, a1, acc[r][0], 0, 0, 0);
+          acc[r][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b11, a1, acc[r][1], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  if (tid < BM) sxs[tid] = sx[(m0 + tid < M) ? m0 + tid : M - 1];
+
+  // Stage st: wait for this wave's copies of stage st (none other is in
+  // flight), barrier (stage st is complete in LDS and everyone is done with
+  // the other buffer), copy stage st + 1 into it, compute stage st.
+  issue(0, A0, B0);
+  auto step = [&](int64_t st, uint8_t* Ac, uint8_t* Bc, uint8_t* An, uint8_t* Bn) {
+    wait_vm<0>();
+    block_barrier();
+    if (st + 1 < nst) issue(st + 1, An, Bn);
+    compute(Ac, Bc);
+  };
+  for (int64_t st = 0; st < nst; st += 2) {
+    step(st, A0, B0, A1, B1);
+    if (st + 1 < nst) step(st + 1, A1, B1, A0, B0);
+  }
+  wait_vm<0>();  // (every copy was waited for at its stage)
+  __syncthreads();
+
+  // Epilogue as in k_gemm_lds (accumulator tile = y^T).
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int mt = wm * 64 + r * 32 + li;
+    const int64_t gm = m0 + mt;
+    const float sm = sxs[mt];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t gn = n0 + wn * 64 + c * 32 + 8 * g + 4 * lh;
+        if (gn >= N || gm >= M) continue;
+        const float4 bq = *reinterpret_cast<const float4*>(beta + gn);
+        const float bv[4] = {bq.x, bq.y, bq.z, bq.w};
+        float o[4];
+        if constexpr (MODE == MODE_FP4) {
+          if (acc_dbg)
+            *reinterpret_cast<float4*>(static_cast<float*>(acc_dbg) + gm * N + gn) =
+                make_float4(acc[r][c][4 * g], acc[r][c][4 * g + 1], acc[r][c][4 * g + 2], acc[r][c][4 * g + 3]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] = dequant(acc[r][c][4 * g + j], sm, bv[j]);
+        } else {
+          int32_t q[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) q[j] = acc[r][c][4 * g + j] >> acc_shift<MODE>();
+          if (acc_dbg)
+            *reinterpret_cast<int4*>(static_cast<int32_t*>(acc_dbg) + gm * N + gn) = make_int4(q[0], q[1], q[2], q[3]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] = dequant(static_cast<float>(q[j]), sm, bv[j]);
+        }
+        *reinterpret_cast<float4*>(y + gm * N + gn) = make_float4(o[0], o[1], o[2], o[3]);
+      }
+    }
+  }
+}
+
 }  // namespace
 
 bool gemm_lds_supported(int mode, int64_t M, int64_t K, int64_t N) {
@@ -294,12 +486,21 @@ hipError_t launch_gemm_lds(int mode, const void* codes, const float* sx, int64_t
   const int NT = static_cast<int>((N + BN - 1) / BN);
   const dim3 grid(static_cast<unsigned>(MT * NT)), block(kThreads);
   const uint8_t* A = static_cast<const uint8_t*>(codes);
+  const bool k256 = K % 256 == 0;
   switch (mode) {
     case MODE_INT4:
-      hipLaunchKernelGGL(k_gemm_lds<MODE_INT4>, grid, block, 0, s, A, sx, M, K, w_packed, beta, N, y, acc_dbg, MT, NT);
+      if (k256)
+        hipLaunchKernelGGL(k_gemm_lds256<MODE_INT4>, grid, block, 0, s, A, sx, M, K, w_packed, beta, N, y, acc_dbg, MT,
+                           NT);
+      else
+        hipLaunchKernelGGL(k_gemm_lds<MODE_INT4>, grid, block, 0, s, A, sx, M, K, w_packed, beta, N, y, acc_dbg, MT, NT);
       break;
     case MODE_FP4:
-      hipLaunchKernelGGL(k_gemm_lds<MODE_FP4>, grid, block, 0, s, A, sx, M, K, w_packed, beta, N, y, acc_dbg, MT, NT);
+      if (k256)
+        hipLaunchKernelGGL(k_gemm_lds256<MODE_FP4>, grid, block, 0, s, A, sx, M, K, w_packed, beta, N, y, acc_dbg, MT,
+                           NT);
+      else
+        hipLaunchKernelGGL(k_gemm_lds<MODE_FP4>, grid, block, 0, s, A, sx, M, K, w_packed, beta, N, y, acc_dbg, MT, NT);
       break;
     default:
       hipLaunchKernelGGL(k_gemm_lds<MODE_INT8>, grid, block, 0, s, A, sx, M, K, w_packed, beta, N, y, acc_dbg, MT, NT);

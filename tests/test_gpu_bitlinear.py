@@ -52,8 +52,11 @@ def test_small_bitlinear_m16_k256_n256(fmt):
 
 @pytest.mark.parametrize("fmt", [bw.BW_ACT_INT4, bw.BW_ACT_FP4_E2M1])
 @pytest.mark.parametrize("M,K,N", [(1, 64, 16), (37, 320, 208), (130, 1024, 144), (200, 256, 400), (8, 4096, 512),
-                                   (9, 320, 48), (16, 1088, 32), (17, 512, 64), (3, 11008, 64), (300, 11008, 272)])
+                                   (9, 320, 48), (16, 1088, 32), (17, 512, 64), (3, 11008, 64), (300, 11008, 272),
+                                   (40, 384, 96), (33, 1152, 272)])
 def test_ragged_shapes(fmt, M, K, N):
+    """K = 320 takes the register-staged kernel, K = 384 and 1152 the 128-k LDS kernel,
+    other multiples of 256 the 256-k one (an odd stage count at K = 11008); M <= 16 the GEMV."""
     x = synth.to_bf16(synth.normal(M + 3 * K + N, (M, K)))
     w = synth.to_bf16(synth.normal(N + 5 * K, (N, K), 0.02))
     y, acc = run_a4(bf16_dev(x), bf16_dev(w), fmt)
