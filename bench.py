@@ -19,7 +19,8 @@ that are resident in HBM before timing starts:
                                      K-major weights (reads only the rows of nonzero codes),
                                      32 layers each
   KV cache, one layer (8x4096x32x128): 3-bit pack of K and V, unpack of both to bf16,
-                                     single-token attention over the packed K and V
+                                     single-token attention over the packed K and V (one
+                                     launch after a cache eviction, and over 32 layers' caches)
   decoder layer, one new token for each of 8 sequences over that cache: the whole
                                      chain (bw_block_decode) over 32 layers of weights
   weights:                           absmean ternary pack of one 4096x4096 fp32 tensor
@@ -146,7 +147,12 @@ class Bench:
         self.sf = t.empty_like(self.s4)
         self.y_11008 = t.empty((M_PREFILL, FFN), dtype=t.float32, device=dev)
         self.y_4096 = t.empty((M_PREFILL, HIDDEN), dtype=t.float32, device=dev)
+        # cache eviction between rows: a read of 384 MB (more than the 256 MB Infinity Cache)
+        # through the library's streaming read; reading leaves the cache lines clean, so the
+        # next timed kernel does not pay for writing back the evicting bytes, as it would
+        # after a write fill
         self.evict = t.empty(384 * 1024 * 1024 // 4, dtype=t.float32, device=dev)
+        self.evict_sink = t.empty(4 * ((384 * 1024 * 1024 + 16383) // 16384), dtype=t.int32, device=dev)
         self.c8_pre = t.empty((M_PREFILL, HIDDEN), dtype=t.int8, device=dev)
         self.s8_pre = t.empty(M_PREFILL, dtype=t.float32, device=dev)
         # ---------------- sparse path
@@ -243,6 +249,7 @@ class Bench:
         # single-token attention over that layer's packed K (kvp[0]) and V (kvp[1])
         self.q_att = f32(synth.normal(S + 6, (B_, H_, D_)))
         self.att_out = t.empty((B_, H_, D_), dtype=t.float32, device=dev)
+        self.att_ws = t.empty(bw.bw_attn_decode_kv3_workspace_bytes(B_, S_, H_, D_), dtype=t.uint8, device=dev)
         # ---------------- one decoder layer per new token (8 sequences, 4096 cached positions):
         # 32 layers of weights (copies of one layer's packed bytes) and of the KV cache
         HD = H_ * D_
@@ -310,9 +317,9 @@ class Bench:
         # the W1.58A4 prefill hot path as one stream sequence (one event pair around
         # the three launches): the basis of `value`
         R.append(("a0_prefill_int4_sequence", "TOPS", gemm_ops(M, FFN, K) + gemm_ops(M, HIDDEN, K), [prefill_int4]))
-        # untimed: overwrite more than the 256 MB Infinity Cache, so the rows below
-        # see the prefill weights cold again, as a0 did
-        R.append(("_evict_cache", None, 0, [lambda: self.evict.fill_(1.0)]))
+        # untimed: read more than the 256 MB Infinity Cache, so the rows below see the
+        # prefill weights cold again, as a0 did
+        R.append(("_evict_cache", None, 0, [self.evict_cache]))
 
         def prefill_b158():
             bw.bw_quantize_sparse_a8(self.x_pre, None, K, self.c8_pre, self.s8_pre)
@@ -322,7 +329,7 @@ class Bench:
         # the same two projections on BitNet b1.58's activation path (INT8 absmax of
         # every entry, no top-k, W1.58A8 GEMMs): the baseline the pages compare against
         R.append(("b0_prefill_b158_int8_sequence", "TOPS", gemm_ops(M, FFN, K) + gemm_ops(M, HIDDEN, K), [prefill_b158]))
-        R.append(("_evict_cache_2", None, 0, [lambda: self.evict.fill_(2.0)]))
+        R.append(("_evict_cache_2", None, 0, [self.evict_cache]))
         R.append(("a1_quantize_int4", "GB/s", M * K * 2 + M * K / 2 + 4 * M,
                   [lambda: bw.bw_quantize(self.x_pre, bw.BW_ACT_INT4, self.c4, self.s4)]))
         R.append(("a4_gemm_int4_n11008", "TOPS", gemm_ops(M, FFN, K),
@@ -406,11 +413,11 @@ class Bench:
             # tiled W1.58A8 GEMV: every weight byte; gather: only the rows of nonzero codes.
             # Each row starts behind an untimed cache fill: the gather's rows of all 32 layers
             # (~108 MB for down_proj) would otherwise stay in the 256 MB Infinity Cache.
-            R.append((f"_evict_cache_{name}_t", None, 0, [lambda: self.evict.fill_(3.0)]))
+            R.append((f"_evict_cache_{name}_t", None, 0, [self.evict_cache]))
             R.append((f"a9_gemv_a8_{name}_m1", "GB/s", N1 * K1 / 4 + 4 * N1 + K1 + 4 + 4 * N1,
                       [lambda o=o, wt=wt: bw.bw_bitlinear_sparse_a8(o["codes"], o["scales"], wt, o["beta"], o["yt"])
                        for wt, _ in o["layers"]]))
-            R.append((f"_evict_cache_{name}_g", None, 0, [lambda: self.evict.fill_(4.0)]))
+            R.append((f"_evict_cache_{name}_g", None, 0, [self.evict_cache]))
             R.append((f"k10_gather_a8_{name}_m1", "GB/s", o["nnz"] * N1 / 4 + 4 * N1 + K1 + 4 + 4 * N1,
                       [lambda o=o, wk=wk: bw.bw_bitlinear_sparse_a8_gather(o["codes"], o["scales"], wk, o["beta"],
                                                                            o["ws"], o["yg"])
@@ -427,14 +434,21 @@ class Bench:
         # planes and scales of K and V, slot ids, both side slabs, q and out
         att_bytes = (2 * nvec * (3 * D_ // 8 + 4) + 4 * B_ * S_ + 2 * self.n_special * H_ * (D_ // 2 + 4)
                      + 2 * 4 * B_ * H_ * D_)
-        R.append(("_evict_cache_attn", None, 0, [lambda: self.evict.fill_(5.0)]))
+        R.append(("_evict_cache_attn", None, 0, [self.evict_cache]))
         R.append(("k11_attn_decode_kv3", "GB/s", att_bytes,
                   [lambda: bw.bw_attn_decode_kv3(self.q_att, self.kvp[0], self.kvp[1], self.slot_of, self.n_special,
                                                  self.att_out)]))
+        # the same attention over each of the 32 layers' caches in turn (each read cold, as a
+        # decode step reads them), averaged per layer
+        R.append(("_evict_cache_attn_l", None, 0, [self.evict_cache]))
+        R.append(("k11l_attn_decode_kv3_layers", "GB/s", att_bytes,
+                  [lambda kc=kc, vc=vc: bw.bw_attn_decode_kv3(self.q_att, kc, vc, self.slot_of, self.n_special,
+                                                              self.att_out, workspace=self.att_ws)
+                   for _, kc, vc in self.blk_layers]))
         # one decoder layer per new token: algorithmic bytes = the layer's packed weights and
         # beta + the attended cache (as the attention row) + small activations
         blk_bytes = self.blk_weight_bytes + att_bytes
-        R.append(("_evict_cache_blk", None, 0, [lambda: self.evict.fill_(6.0)]))
+        R.append(("_evict_cache_blk", None, 0, [self.evict_cache]))
         R.append(("k12_block_decode_b8", "GB/s", blk_bytes,
                   [lambda lw=lw, kc=kc, vc=vc: bw.bw_block_decode(self.blk_x, lw, kc, vc, self.slot_of, self.n_special,
                                                                   self.blk_pos, H_, x_out=self.blk_out,
@@ -443,6 +457,9 @@ class Bench:
         R.append(("a3_pack_ternary_4096x4096", "GB/s", HIDDEN * HIDDEN * 4 + HIDDEN * HIDDEN / 4 + 4 * HIDDEN,
                   [lambda: bw.bw_pack_ternary(self.w_q, bw.BW_ROLE_A4, self.pk, self.pk_b, self.pk_ws)]))
         return R
+
+    def evict_cache(self):
+        self.bw.bw_stream_read(self.evict, self.evict_sink)
 
     def capture(self):
         """Record each multi-launch row (the decode loops) once into a HIP graph (no
@@ -688,6 +705,13 @@ def main():
                  "basis": "one decoder layer for one new token of each of 8 sequences with 4096 cached positions "
                           "(INT4 q/k/v, 3-bit KV append and attention, top-k INT8 out_proj, INT4 gate/up, "
                           "ReLU^2 top-k INT8 down_proj, residuals), averaged over 32 layers of weights and caches"}
+    attn = None
+    if "k11_attn_decode_kv3" in table and "k11l_attn_decode_kv3_layers" in table:
+        attn = {"single_launch_after_eviction_us": table["k11_attn_decode_kv3"]["avg_us"],
+                "per_layer_us": table["k11l_attn_decode_kv3_layers"]["avg_us"],
+                "basis": "one new query per (batch, head) over 8 x 4096 cached positions, 32 heads of 128: one "
+                         "launch right after a 384 MB cache eviction (row k11), and the average over 32 layers' "
+                         "caches launched in turn, each read cold from HBM (row k11l)"}
     gather = {}
     for name, o in b.one.items():
         rt, rg = f"a9_gemv_a8_{name}_m1", f"k10_gather_a8_{name}_m1"
@@ -736,6 +760,7 @@ def main():
             "basis": "same ops / time of INT8 absmax (all entries, no top-k) + both W1.58A8 GEMMs, back to back (row b0)",
             "a48_over_b158": None if value is None else round(value / b158, 3)},
         "gather_decode_m1": gather or None,
+        "attn_decode_kv3": attn,
         "block_decode": block,
         "decode_gbs": None if decode_gbs is None else round(decode_gbs, 1),
         "decode_frac_hbm": None if decode_gbs is None else round(decode_gbs / HBM_PEAK_GBS, 4),
