@@ -69,7 +69,7 @@ M_PREFILL, HIDDEN, FFN = 2048, 4096, 11008
 # 256 MiB copy in the same runs; summary in profiles/gemm_int4_m2048_k4096_n11008_hbm_bytes.md).
 # It is reported only while the kernel sources still hash to the digest they were taken at.
 GEMM_TRAFFIC = {
-    "bytes": 218_486_596,
+    "bytes": 220_745_476,
     "sources": ("gemm_lds.hip", "bw_widen.h", "bw_device.h"),
     "sha256": "8fe941d945ce34b74765fdc1ddeac4c797a684b3838aea5edb6682c1f5a48e79",
 }
@@ -654,7 +654,10 @@ def main():
         rate = amount / (avg_ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
         peak = HBM_PEAK_GBS if unit == "GB/s" else (FP4_PEAK_TOPS if "fp4" in name else INT8_PEAK_TOPS)
         table[name] = {"avg_us": round(avg_ms * 1e3, 3), "launches_per_step": len(fns), "rate": round(rate, 2),
-                       "unit": unit, "frac_of_peak": round(rate / peak, 4), "amount_per_launch": amount}
+                       "unit": unit, "frac_of_peak": round(rate / peak, 4), "amount_per_launch": amount,
+                       # spread over the timed steps (per launch), to show steps that ran slow
+                       "min_us": round(min(row_ms) * 1e3 / len(fns), 3),
+                       "max_us": round(max(row_ms) * 1e3 / len(fns), 3)}
 
     def row_ms(names):
         return sum(table[n]["avg_us"] * table[n]["launches_per_step"] for n in names) / 1e3
@@ -783,7 +786,7 @@ def main():
     if args.rows:
         for n, r in table.items():
             print(f"{n:34s} {r['avg_us']:10.2f} us x{r['launches_per_step']:4d}  {r['rate']:9.1f} {r['unit']:5s} "
-                  f"{100 * r['frac_of_peak']:6.1f}%", file=sys.stderr)
+                  f"{100 * r['frac_of_peak']:6.1f}%  [{r['min_us']:.2f} .. {r['max_us']:.2f} us]", file=sys.stderr)
     print(json.dumps(out))
     return 0
 
