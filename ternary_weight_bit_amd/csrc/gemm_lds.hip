@@ -292,10 +292,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
 __device__ __forceinline__ int a_slot256(int row, int p) { return p ^ ((row >> 1) & 7); }
 
 // 16 bytes per lane from a buffer resource into LDS at `lds` + 16 * lane.
-__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, const uint8_t* lds, uint32_t voff, int soff) {
-  const uint32_t m = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m), "v"(voff), "s"(r), "s"(soff)
+__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, uint32_t voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds_addr), "v"(voff), "s"(r),
+               "s"(soff)
                : "memory", "m0");
+}
+
+// LDS byte address of a __shared__ pointer (the low half of its generic address).
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
 template <int MODE>
@@ -357,16 +362,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
       const_cast<uint8_t*>(Wp + g_first * kblocks * 256), 0, static_cast<int>((ng - g_first) * kblocks * 256),
       kRsrcWord3);
   const int64_t rot = ((t % MT) % 4) * (nst / 4);  // as in k_gemm_lds
+  // this wave's 2 KB of each stage buffer, as a wave-uniform (scalar) offset
+  const uint32_t wbase = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(2 * wave * 1024));
   auto issue = [&](int64_t st_req, uint8_t* As, uint8_t* Bs) {
     int64_t sp = st_req + rot;
     if (sp >= nst) sp -= nst;
     const int st = static_cast<int>(sp);
     const int sa = st * AROW;
     const int sb = st * 1024;
+    const uint32_t la = lds_addr(As) + wbase;
+    const uint32_t lb = lds_addr(Bs) + wbase;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) lds_copy16(arsrc, As + (2 * wave + j) * 1024, aoff[j], sa);
+    for (int j = 0; j < 2; ++j) lds_copy16(arsrc, la + 1024 * j, aoff[j], sa);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) lds_copy16(brsrc, Bs + (2 * wave + j) * 1024, boff[j], sb);
+    for (int j = 0; j < 2; ++j) lds_copy16(brsrc, lb + 1024 * j, boff[j], sb);
   };
 
   using acc_t = typename std::conditional<MODE == MODE_FP4, v16f, v16i>::type;
@@ -378,41 +387,66 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[r][c][e] = 0;
 
+  // Fragments of one 64-k block s of a stage: the weight words of columns
+  // wn*64 + li and + 32, and the activation parts of rows wm*64 + li and + 32.
+  struct Frag {
+    uint2 w0, w1;
+    uint4 x0, x1;
+  };
+  auto load_frag = [&](const uint8_t* As, const uint8_t* Bs, int s) {
+    Frag f;
+    const int col = wn * 64 + li;
+    int o0 = ((col >> 4) * 4 + s) * 256 + (col & 15) * 16 + 8 * lh;
+    int o1 = o0 + 2048;
+    asm volatile("" : "+v"(o0), "+v"(o1));
+    f.w0 = *reinterpret_cast<const uint2*>(Bs + o0);
+    f.w1 = *reinterpret_cast<const uint2*>(Bs + o1);
+    const int row0 = wm * 64 + li;
+    const int row1 = row0 + 32;
+    f.x0 = *reinterpret_cast<const uint4*>(As + row0 * AROW + 16 * a_slot256(row0, 2 * s + lh));
+    f.x1 = *reinterpret_cast<const uint4*>(As + row1 * AROW + 16 * a_slot256(row1, 2 * s + lh));
+    return f;
+  };
+  auto mma_frag = [&](const Frag& f) {
+    if constexpr (MODE == MODE_FP4) {
+      const v8i b0 = fp4_weights(f.w0.x, f.w0.y);
+      const v8i b1 = fp4_weights(f.w1.x, f.w1.y);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const uint4 x = r ? f.x1 : f.x0;
+        const v8i a = fp4_operand(x.x, x.y, x.z, x.w);
+        acc[r][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b0, a, acc[r][0], 4, 4, 0, 127, 0, 127);
+        acc[r][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b1, a, acc[r][1], 4, 4, 0, 127, 0, 127);
+      }
+    } else {
+      const v4i b00 = widen_w_a4(f.w0.x), b01 = widen_w_a4(f.w0.y);
+      const v4i b10 = widen_w_a4(f.w1.x), b11 = widen_w_a4(f.w1.y);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const uint4 x = r ? f.x1 : f.x0;
+        const v4i a0 = widen_int4(x.x, x.y);
+        const v4i a1 = widen_int4(x.z, x.w);
+        acc[r][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b00, a0, acc[r][0], 0, 0, 0);
+        acc[r][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b10, a0, acc[r][1], 0, 0, 0);
+        acc[r][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b01, a1, acc[r][0], 0, 0, 0);
+        acc[r][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b11, a1, acc[r][1], 0, 0, 0);
+      }
+    }
+  };
+  // The four 64-k blocks of a stage, each block's LDS reads issued before the
+  // previous block's products (the scheduling barriers keep that order; left to
+  // itself the compiler sinks each read next to its first use, which exposes the
+  // LDS latency once per block).
   auto compute = [&](const uint8_t* As, const uint8_t* Bs) {
+    Frag f = load_frag(As, Bs, 0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int col = wn * 64 + li;
-      int o0 = ((col >> 4) * 4 + s) * 256 + (col & 15) * 16 + 8 * lh;
-      int o1 = o0 + 2048;
-      asm volatile("" : "+v"(o0), "+v"(o1));
-      const uint2 w0 = *reinterpret_cast<const uint2*>(Bs + o0);
-      const uint2 w1 = *reinterpret_cast<const uint2*>(Bs + o1);
-      if constexpr (MODE == MODE_FP4) {
-        const v8i b0 = fp4_weights(w0.x, w0.y);
-        const v8i b1 = fp4_weights(w1.x, w1.y);
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const int row = wm * 64 + r * 32 + li;
-          const uint4 x = *reinterpret_cast<const uint4*>(As + row * AROW + 16 * a_slot256(row, 2 * s + lh));
-          const v8i a = fp4_operand(x.x, x.y, x.z, x.w);
-          acc[r][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b0, a, acc[r][0], 4, 4, 0, 127, 0, 127);
-          acc[r][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b1, a, acc[r][1], 4, 4, 0, 127, 0, 127);
-        }
-      } else {
-        const v4i b00 = widen_w_a4(w0.x), b01 = widen_w_a4(w0.y);
-        const v4i b10 = widen_w_a4(w1.x), b11 = widen_w_a4(w1.y);
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const int row = wm * 64 + r * 32 + li;
-          const uint4 x = *reinterpret_cast<const uint4*>(As + row * AROW + 16 * a_slot256(row, 2 * s + lh));
-          const v4i a0 = widen_int4(x.x, x.y);
-          const v4i a1 = widen_int4(x.z, x.w);
-          acc[r][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b00, a0, acc[r][0], 0, 0, 0);
-          acc[r][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b10, a0, acc[r][1], 0, 0, 0);
-          acc[r][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b01, a1, acc[r][0], 0, 0, 0);
-          acc[r][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b11, a1, acc[r][1], 0, 0, 0);
-        }
-      }
+      Frag g;
+      if (s < 3) g = load_frag(As, Bs, s + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_frag(f);
+      __builtin_amdgcn_sched_barrier(0);
+      f = g;
     }
   };
 
