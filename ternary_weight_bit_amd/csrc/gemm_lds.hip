@@ -469,38 +469,63 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
   wait_vm<0>();  // (every copy was waited for at its stage)
   __syncthreads();
 
-  // Epilogue as in k_gemm_lds (accumulator tile = y^T).
+  // Epilogue, y = fl(fl(q * sx) * beta), in two halves of the wave's 64 x 64
+  // block (32 rows each) staged through this wave's own 8 KB of the operand
+  // buffers (free after the barrier above; no other wave touches it), so that
+  // each store instruction writes 4 rows x 256 contiguous bytes instead of
+  // 16-byte pieces of 32 rows. A lane holds row li, 16-byte units c*8 + 2g + lh
+  // of the block's 64 columns; units are XOR-swizzled by the row in LDS.
+  using stage_t = typename std::conditional<MODE == MODE_FP4, float4, int4>::type;
+  uint8_t* const stage = (wave < 2 ? A0 : wave < 4 ? A1 : wave < 6 ? B0 : B1) + (wave & 1) * 8192;
+  int lane_e = lane;
+  asm volatile("" : "+v"(lane_e));  // derive the epilogue's indices here, not before the loop
+  const int u = lane_e & 15;
+  const int64_t gn = n0 + wn * 64 + 4 * u;
+  float bv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (gn < N) {
+    const float4 bq = *reinterpret_cast<const float4*>(beta + gn);
+    bv[0] = bq.x;
+    bv[1] = bq.y;
+    bv[2] = bq.z;
+    bv[3] = bq.w;
+  }
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    const int mt = wm * 64 + r * 32 + li;
-    const int64_t gm = m0 + mt;
-    const float sm = sxs[mt];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int64_t gn = n0 + wn * 64 + c * 32 + 8 * g + 4 * lh;
-        if (gn >= N || gm >= M) continue;
-        const float4 bq = *reinterpret_cast<const float4*>(beta + gn);
-        const float bv[4] = {bq.x, bq.y, bq.z, bq.w};
-        float o[4];
-        if constexpr (MODE == MODE_FP4) {
-          if (acc_dbg)
-            *reinterpret_cast<float4*>(static_cast<float*>(acc_dbg) + gm * N + gn) =
-                make_float4(acc[r][c][4 * g], acc[r][c][4 * g + 1], acc[r][c][4 * g + 2], acc[r][c][4 * g + 3]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) o[j] = dequant(acc[r][c][4 * g + j], sm, bv[j]);
-        } else {
-          int32_t q[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) q[j] = acc[r][c][4 * g + j] >> acc_shift<MODE>();
-          if (acc_dbg)
-            *reinterpret_cast<int4*>(static_cast<int32_t*>(acc_dbg) + gm * N + gn) = make_int4(q[0], q[1], q[2], q[3]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) o[j] = dequant(static_cast<float>(q[j]), sm, bv[j]);
-        }
-        *reinterpret_cast<float4*>(y + gm * N + gn) = make_float4(o[0], o[1], o[2], o[3]);
+        const int unit = c * 8 + 2 * g + lh;
+        stage_t v;
+        v.x = acc[r][c][4 * g];
+        v.y = acc[r][c][4 * g + 1];
+        v.z = acc[r][c][4 * g + 2];
+        v.w = acc[r][c][4 * g + 3];
+        *reinterpret_cast<stage_t*>(stage + li * 256 + ((unit ^ (li & 15)) << 4)) = v;
       }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int m = 4 * k + (lane_e >> 4);
+      const stage_t v = *reinterpret_cast<const stage_t*>(stage + m * 256 + ((u ^ (m & 15)) << 4));
+      const int mt = wm * 64 + r * 32 + m;
+      const int64_t gm = m0 + mt;
+      const float sm = sxs[mt];
+      float o[4];
+      if constexpr (MODE == MODE_FP4) {
+        if (acc_dbg && gm < M && gn < N) *reinterpret_cast<float4*>(static_cast<float*>(acc_dbg) + gm * N + gn) = v;
+        o[0] = dequant(v.x, sm, bv[0]);
+        o[1] = dequant(v.y, sm, bv[1]);
+        o[2] = dequant(v.z, sm, bv[2]);
+        o[3] = dequant(v.w, sm, bv[3]);
+      } else {
+        const int32_t q[4] = {v.x >> acc_shift<MODE>(), v.y >> acc_shift<MODE>(), v.z >> acc_shift<MODE>(),
+                              v.w >> acc_shift<MODE>()};
+        if (acc_dbg && gm < M && gn < N)
+          *reinterpret_cast<int4*>(static_cast<int32_t*>(acc_dbg) + gm * N + gn) = make_int4(q[0], q[1], q[2], q[3]);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) o[jj] = dequant(static_cast<float>(q[jj]), sm, bv[jj]);
+      }
+      if (gm < M && gn < N) *reinterpret_cast<float4*>(y + gm * N + gn) = make_float4(o[0], o[1], o[2], o[3]);
     }
   }
 }
