@@ -78,6 +78,88 @@ __device__ __forceinline__ int a_slot(int row, int p) {
   else return p ^ ((row >> 2) & 3);
 }
 
+// Epilogue of one wave's 64 x 64 accumulator block, y = fl(fl(q * sx) * beta).
+// The accumulator tile is y^T: lane l holds token l % 32 and channels
+// 8*(e/4) + 4*(l/32) + (e%4) of each 32 x 32 product, so elements 4g..4g+3 are
+// four consecutive channels of one token. Stores of that layout write 16-byte
+// pieces of 32 rows; instead the block goes through `stage`, LDS that only this
+// wave uses, and each store writes whole rows: WIDE = true stages 32 tokens x
+// 64 channels (8 KB) per round and stores 4 rows x 256 bytes; WIDE = false
+// stages 32 tokens x 32 channels (4 KB) and stores 8 rows x 128 bytes. Every
+// lane takes part in every LDS access (no divergent branch around them); the
+// 16-byte units of a staged row are XOR-swizzled by the row. LDS accesses of
+// one wave complete in issue order.
+template <int MODE, bool WIDE, typename AccT>
+__device__ __forceinline__ void epilogue_staged(const AccT (&acc)[2][2], uint8_t* stage, int lane, int wm, int wn,
+                                                int64_t m0, int64_t n0, int64_t M, int64_t N, const float* sxs,
+                                                const float* __restrict__ beta, float* __restrict__ y,
+                                                void* __restrict__ acc_dbg) {
+  using stage_t = typename std::conditional<MODE == MODE_FP4, float4, int4>::type;
+  constexpr int ROWB = WIDE ? 256 : 128;   // staged bytes per token
+  constexpr int UNITS = ROWB / 16;         // 16-byte units per staged token
+  constexpr int LPR = UNITS;               // lanes reading one token
+  constexpr int RPI = 64 / LPR;            // tokens per read instruction
+  constexpr int NC = WIDE ? 1 : 2;         // rounds over the two 32-channel halves
+  const int li = lane & 31;
+  const int lh = lane >> 5;
+  const int u = lane % LPR;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+#pragma unroll
+    for (int cr = 0; cr < NC; ++cr) {
+      // write: token li, units of channel halves c (all of them when WIDE)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        if (!WIDE && c != cr) continue;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int unit = (WIDE ? c * 8 : 0) + 2 * g + lh;
+          stage_t v;
+          v.x = acc[r][c][4 * g];
+          v.y = acc[r][c][4 * g + 1];
+          v.z = acc[r][c][4 * g + 2];
+          v.w = acc[r][c][4 * g + 3];
+          *reinterpret_cast<stage_t*>(stage + li * ROWB + ((unit ^ (li % UNITS)) << 4)) = v;
+        }
+      }
+      const int64_t gn = n0 + wn * 64 + (WIDE ? 0 : cr * 32) + 4 * u;
+      float bv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (gn < N) {
+        const float4 bq = *reinterpret_cast<const float4*>(beta + gn);
+        bv[0] = bq.x;
+        bv[1] = bq.y;
+        bv[2] = bq.z;
+        bv[3] = bq.w;
+      }
+      // read: token m, unit u; store 16 bytes of y
+#pragma unroll
+      for (int k = 0; k < 32 / RPI; ++k) {
+        const int m = RPI * k + lane / LPR;
+        const stage_t v = *reinterpret_cast<const stage_t*>(stage + m * ROWB + ((u ^ (m % UNITS)) << 4));
+        const int mt = wm * 64 + r * 32 + m;
+        const int64_t gm = m0 + mt;
+        const float sm = sxs[mt];
+        float o[4];
+        if constexpr (MODE == MODE_FP4) {
+          if (acc_dbg && gm < M && gn < N) *reinterpret_cast<float4*>(static_cast<float*>(acc_dbg) + gm * N + gn) = v;
+          o[0] = dequant(v.x, sm, bv[0]);
+          o[1] = dequant(v.y, sm, bv[1]);
+          o[2] = dequant(v.z, sm, bv[2]);
+          o[3] = dequant(v.w, sm, bv[3]);
+        } else {
+          const int32_t q[4] = {v.x >> acc_shift<MODE>(), v.y >> acc_shift<MODE>(), v.z >> acc_shift<MODE>(),
+                                v.w >> acc_shift<MODE>()};
+          if (acc_dbg && gm < M && gn < N)
+            *reinterpret_cast<int4*>(static_cast<int32_t*>(acc_dbg) + gm * N + gn) = make_int4(q[0], q[1], q[2], q[3]);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) o[jj] = dequant(static_cast<float>(q[jj]), sm, bv[jj]);
+        }
+        if (gm < M && gn < N) *reinterpret_cast<float4*>(y + gm * N + gn) = make_float4(o[0], o[1], o[2], o[3]);
+      }
+    }
+  }
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_gemm_lds(
     const uint8_t* __restrict__ A, const float* __restrict__ sx, int64_t M, int64_t K,
@@ -240,42 +322,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     if (st + 2 < nst) step(st + 2, A2, B2, A1, B1);
   }
   wait_vm<0>();  // no load into LDS outlives the workgroup
+  __syncthreads();  // every wave is done with the operand buffers
 
-  // Epilogue.  Accumulator tile = y^T: lane l holds token (l % 32) and channels
-  // 8*(e/4) + 4*(l/32) + (e%4), so elements 4g..4g+3 are four consecutive
-  // channels of one token.
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int mt = wm * 64 + r * 32 + li;
-    const int64_t gm = m0 + mt;
-    const float sm = sxs[mt];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t gn = n0 + wn * 64 + c * 32 + 8 * g + 4 * lh;
-        if (gn >= N || gm >= M) continue;
-        const float4 bq = *reinterpret_cast<const float4*>(beta + gn);
-        const float bv[4] = {bq.x, bq.y, bq.z, bq.w};
-        float o[4];
-        if constexpr (MODE == MODE_FP4) {
-          if (acc_dbg)
-            *reinterpret_cast<float4*>(static_cast<float*>(acc_dbg) + gm * N + gn) =
-                make_float4(acc[r][c][4 * g], acc[r][c][4 * g + 1], acc[r][c][4 * g + 2], acc[r][c][4 * g + 3]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) o[j] = dequant(acc[r][c][4 * g + j], sm, bv[j]);
-        } else {
-          int32_t q[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) q[j] = acc[r][c][4 * g + j] >> acc_shift<MODE>();
-          if (acc_dbg)
-            *reinterpret_cast<int4*>(static_cast<int32_t*>(acc_dbg) + gm * N + gn) = make_int4(q[0], q[1], q[2], q[3]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) o[j] = dequant(static_cast<float>(q[j]), sm, bv[j]);
-        }
-        *reinterpret_cast<float4*>(y + gm * N + gn) = make_float4(o[0], o[1], o[2], o[3]);
-      }
-    }
+  int lane_e = lane;
+  asm volatile("" : "+v"(lane_e));  // derive the epilogue's indices here, not before the loop
+  static_assert(MODE == MODE_INT8 ? (C::AStage >= 16384 && kBStage >= 8192) : (C::AStage >= 8192 && kBStage >= 4096),
+                "epilogue staging regions");
+  if constexpr (MODE == MODE_INT8) {
+    // 8 KB of LDS per wave: waves 2i, 2i+1 take A_i (16 KB each), waves 6, 7 take B0, B1
+    uint8_t* const stage = wave < 6 ? (wave < 2 ? A0 : wave < 4 ? A1 : A2) + (wave & 1) * 8192 : (wave == 6 ? B0 : B1);
+    epilogue_staged<MODE, true>(acc, stage, lane_e, wm, wn, m0, n0, M, N, sxs, beta, y, acc_dbg);
+  } else {
+    // 4 KB of LDS per wave: waves 2i, 2i+1 take A_i (8 KB each), waves 6, 7 take B0
+    uint8_t* const stage = (wave < 2 ? A0 : wave < 4 ? A1 : wave < 6 ? A2 : B0) + (wave & 1) * 4096;
+    epilogue_staged<MODE, false>(acc, stage, lane_e, wm, wn, m0, n0, M, N, sxs, beta, y, acc_dbg);
   }
 }
 
@@ -469,65 +529,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
   wait_vm<0>();  // (every copy was waited for at its stage)
   __syncthreads();
 
-  // Epilogue, y = fl(fl(q * sx) * beta), in two halves of the wave's 64 x 64
-  // block (32 rows each) staged through this wave's own 8 KB of the operand
-  // buffers (free after the barrier above; no other wave touches it), so that
-  // each store instruction writes 4 rows x 256 contiguous bytes instead of
-  // 16-byte pieces of 32 rows. A lane holds row li, 16-byte units c*8 + 2g + lh
-  // of the block's 64 columns; units are XOR-swizzled by the row in LDS.
-  using stage_t = typename std::conditional<MODE == MODE_FP4, float4, int4>::type;
+  // 8 KB of LDS per wave for the epilogue: waves 2i, 2i+1 take A0, A1, B0, B1.
+  static_assert(AStage >= 16384 && BStage >= 16384, "epilogue staging regions");
   uint8_t* const stage = (wave < 2 ? A0 : wave < 4 ? A1 : wave < 6 ? B0 : B1) + (wave & 1) * 8192;
   int lane_e = lane;
   asm volatile("" : "+v"(lane_e));  // derive the epilogue's indices here, not before the loop
-  const int u = lane_e & 15;
-  const int64_t gn = n0 + wn * 64 + 4 * u;
-  float bv[4] = {0.f, 0.f, 0.f, 0.f};
-  if (gn < N) {
-    const float4 bq = *reinterpret_cast<const float4*>(beta + gn);
-    bv[0] = bq.x;
-    bv[1] = bq.y;
-    bv[2] = bq.z;
-    bv[3] = bq.w;
-  }
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int unit = c * 8 + 2 * g + lh;
-        stage_t v;
-        v.x = acc[r][c][4 * g];
-        v.y = acc[r][c][4 * g + 1];
-        v.z = acc[r][c][4 * g + 2];
-        v.w = acc[r][c][4 * g + 3];
-        *reinterpret_cast<stage_t*>(stage + li * 256 + ((unit ^ (li & 15)) << 4)) = v;
-      }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int m = 4 * k + (lane_e >> 4);
-      const stage_t v = *reinterpret_cast<const stage_t*>(stage + m * 256 + ((u ^ (m & 15)) << 4));
-      const int mt = wm * 64 + r * 32 + m;
-      const int64_t gm = m0 + mt;
-      const float sm = sxs[mt];
-      float o[4];
-      if constexpr (MODE == MODE_FP4) {
-        if (acc_dbg && gm < M && gn < N) *reinterpret_cast<float4*>(static_cast<float*>(acc_dbg) + gm * N + gn) = v;
-        o[0] = dequant(v.x, sm, bv[0]);
-        o[1] = dequant(v.y, sm, bv[1]);
-        o[2] = dequant(v.z, sm, bv[2]);
-        o[3] = dequant(v.w, sm, bv[3]);
-      } else {
-        const int32_t q[4] = {v.x >> acc_shift<MODE>(), v.y >> acc_shift<MODE>(), v.z >> acc_shift<MODE>(),
-                              v.w >> acc_shift<MODE>()};
-        if (acc_dbg && gm < M && gn < N)
-          *reinterpret_cast<int4*>(static_cast<int32_t*>(acc_dbg) + gm * N + gn) = make_int4(q[0], q[1], q[2], q[3]);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) o[jj] = dequant(static_cast<float>(q[jj]), sm, bv[jj]);
-      }
-      if (gm < M && gn < N) *reinterpret_cast<float4*>(y + gm * N + gn) = make_float4(o[0], o[1], o[2], o[3]);
-    }
-  }
+  epilogue_staged<MODE, true>(acc, stage, lane_e, wm, wn, m0, n0, M, N, sxs, beta, y, acc_dbg);
 }
 
 }  // namespace
