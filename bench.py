@@ -35,13 +35,14 @@ clock only after tens of milliseconds of sustained load (a W1.58A4 GEMM at
 N=11008 runs ~115 us in the first milliseconds and ~81 us at the sustained
 clock), and the timed steps are meant to see the sustained operating point.
 The printed line's `value` is the W1.58A4 prefill throughput: int ops of the
-two GEMMs over the time of the INT4 quantizer and both GEMMs launched back to
-back (row a0, one event pair around the three launches);
-`value_from_separate_rows` divides the same ops by the sum of the individually
-bracketed rows a1 + a4 (each of which also pays its own launch latency).
+two products over the time of the INT4 quantizer followed by both products,
+which share its codes and run as one grouped launch (row a0, one event pair
+around the two launches); `value_from_separate_rows` divides the same ops by
+the sum of the individually bracketed rows a1 + a4 (one launch per product,
+each also paying its own launch latency and its own tail).
 `b158_baseline` runs the same two projections on BitNet b1.58's activation
-path (INT8 absmax of every entry, no top-k, W1.58A8 GEMMs; row b0) and gives
-the ratio of the two.  `decode_gbs` is the decode GEMV rate in algorithmic
+path (INT8 absmax of every entry, no top-k, W1.58A8 products grouped the same
+way; row b0) and gives the ratio of the two.  `decode_gbs` is the decode GEMV rate in algorithmic
 bytes (`decode_quant_gemv_gbs` with the quantizer in the same call);
 `decode_read_ceiling` sets each GEMV beside the bare read of its weight bytes;
 `decode_b158` compares the decode projections on the two activation paths;
@@ -311,11 +312,13 @@ class Bench:
 
         def prefill_int4():
             bw.bw_quantize(self.x_pre, bw.BW_ACT_INT4, self.c4, self.s4)
-            bw.bw_bitlinear_a4(self.c4, self.s4, bw.BW_ACT_INT4, self.wp_11008, self.b_11008, self.y_11008)
-            bw.bw_bitlinear_a4(self.c4, self.s4, bw.BW_ACT_INT4, self.wp_4096, self.b_4096, self.y_4096)
+            bw.bw_bitlinear_a4_grouped(self.c4, self.s4, bw.BW_ACT_INT4,
+                                       [(self.wp_11008, self.b_11008), (self.wp_4096, self.b_4096)],
+                                       ys=[self.y_11008, self.y_4096])
 
         # the W1.58A4 prefill hot path as one stream sequence (one event pair around
-        # the three launches): the basis of `value`
+        # the quantizer and the two products, which share its codes and run as one
+        # grouped launch): the basis of `value`
         R.append(("a0_prefill_int4_sequence", "TOPS", gemm_ops(M, FFN, K) + gemm_ops(M, HIDDEN, K), [prefill_int4]))
         # untimed: read more than the 256 MB Infinity Cache, so the rows below see the
         # prefill weights cold again, as a0 did
@@ -323,11 +326,13 @@ class Bench:
 
         def prefill_b158():
             bw.bw_quantize_sparse_a8(self.x_pre, None, K, self.c8_pre, self.s8_pre)
-            bw.bw_bitlinear_sparse_a8(self.c8_pre, self.s8_pre, self.wp8_11008, self.b8_11008, self.y_11008)
-            bw.bw_bitlinear_sparse_a8(self.c8_pre, self.s8_pre, self.wp8_4096, self.b8_4096, self.y_4096)
+            bw.bw_bitlinear_sparse_a8_grouped(self.c8_pre, self.s8_pre,
+                                              [(self.wp8_11008, self.b8_11008), (self.wp8_4096, self.b8_4096)],
+                                              ys=[self.y_11008, self.y_4096])
 
         # the same two projections on BitNet b1.58's activation path (INT8 absmax of
-        # every entry, no top-k, W1.58A8 GEMMs): the baseline the pages compare against
+        # every entry, no top-k, W1.58A8 products, grouped the same way): the
+        # baseline the pages compare against
         R.append(("b0_prefill_b158_int8_sequence", "TOPS", gemm_ops(M, FFN, K) + gemm_ops(M, HIDDEN, K), [prefill_b158]))
         R.append(("_evict_cache_2", None, 0, [self.evict_cache]))
         R.append(("a1_quantize_int4", "GB/s", M * K * 2 + M * K / 2 + 4 * M,
@@ -755,12 +760,14 @@ def main():
                                "the 3-bit cache 8x4096x32x128 and one decoder layer for 8 sequences x 4096 cached "
                                "positions", "global_batch": M_PREFILL, "seq_len": KV_SHAPE[1],
                    "parallelism": "none (1 GPU)"},
-        "value_basis": "2*2048*4096*(11008+4096) int ops / time of the INT4 quantizer + both W1.58A4 GEMMs, "
-                       "launched back to back as one stream sequence (row a0)",
+        "value_basis": "2*2048*4096*(11008+4096) int ops / time of the INT4 quantizer + the W1.58A4 products "
+                       "N=11008 and N=4096 over its codes (one grouped launch), back to back as one stream "
+                       "sequence (row a0)",
         "value_from_separate_rows": value_rows,
         "b158_baseline": None if b158 is None else {
             "value": b158, "unit": "TOPS",
-            "basis": "same ops / time of INT8 absmax (all entries, no top-k) + both W1.58A8 GEMMs, back to back (row b0)",
+            "basis": "same ops / time of INT8 absmax (all entries, no top-k) + the two W1.58A8 products over its "
+                     "codes (one grouped launch), back to back (row b0)",
             "a48_over_b158": None if value is None else round(value / b158, 3)},
         "gather_decode_m1": gather or None,
         "attn_decode_kv3": attn,

@@ -154,6 +154,27 @@ bw_status bw_bitlinear_a4(const uint8_t* codes, const float* x_scales, int64_t M
                           int64_t N, float* y, void* acc_dbg, void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * Several W1.58A4 BitLinear products over the same 4-bit codes in one call.
+ * Source: as bw_bitlinear_a4 (BitNet a4.8 abstract: ternary layers on 4-bit
+ * activations); the projections that read one activation (q/k/v, or gate
+ * and up) share its codes.
+ * For g < n_groups, y[g] receives exactly bw_bitlinear_a4(codes, x_scales,
+ * M, K, fmt, w_packed[g], beta[g], N[g]) (bit for bit), and acc_dbg[g] its
+ * accumulators.  With M > 16 tokens and K % 128 == 0 all products run as one
+ * launch whose grid holds the tiles of every product, so one product's tiles
+ * fill the CUs another's leave idle; otherwise one launch per product.
+ * w_packed, beta, N, y: HOST arrays of n_groups entries (device pointers of
+ * the same kinds as bw_bitlinear_a4's, and sizes).  acc_dbg: NULL, or a host
+ * array of n_groups entries, each NULL or as bw_bitlinear_a4's.  The host
+ * arrays are read during the call only.
+ * Shapes: 1 <= n_groups <= 4; every product as bw_bitlinear_a4.
+ * ------------------------------------------------------------------------ */
+bw_status bw_bitlinear_a4_grouped(const uint8_t* codes, const float* x_scales, int64_t M, int64_t K,
+                                  bw_act4_fmt fmt, int n_groups, const uint8_t* const* w_packed,
+                                  const float* const* beta, const int64_t* N, float* const* y,
+                                  void* const* acc_dbg, void* stream);
+
+/* ------------------------------------------------------------------------ *
  * 4-bit quantizer and W1.58A4 BitLinear in one call.
  * Source: as bw_quantize and bw_bitlinear_a4 (BitNet a4.8 abstract: 4-bit
  * activations for the attention and FFN inputs, INT4/FP4 kernels).
@@ -204,6 +225,21 @@ bw_status bw_quantize_sparse_a8(const void* gate_or_x, const void* up, bw_dtype 
 bw_status bw_bitlinear_sparse_a8(const int8_t* codes, const float* x_scales, int64_t M, int64_t K,
                                  const uint8_t* w_packed, const float* beta, int64_t N, float* y,
                                  int32_t* acc_dbg, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Several W1.58A8 BitLinear products over the same INT8 codes in one call.
+ * Source: as bw_bitlinear_sparse_a8.  The b1.58 path (absmax INT8 of every
+ * entry, toshoseti review, opening lines) feeds q/k/v and gate/up from one
+ * set of codes the same way the 4-bit path does.
+ * For g < n_groups, y[g] receives exactly bw_bitlinear_sparse_a8(codes,
+ * x_scales, M, K, w_packed[g], beta[g], N[g]); launches as
+ * bw_bitlinear_a4_grouped.  Host arrays and acc_dbg as there (int32 [M][N]).
+ * Shapes: 1 <= n_groups <= 4; every product as bw_bitlinear_sparse_a8.
+ * ------------------------------------------------------------------------ */
+bw_status bw_bitlinear_sparse_a8_grouped(const int8_t* codes, const float* x_scales, int64_t M, int64_t K,
+                                         int n_groups, const uint8_t* const* w_packed,
+                                         const float* const* beta, const int64_t* N, float* const* y,
+                                         int32_t* const* acc_dbg, void* stream);
 
 /* ------------------------------------------------------------------------ *
  * W1.58A8 product that reads only the weight rows of nonzero codes.

@@ -57,9 +57,11 @@ def _load() -> ctypes.CDLL:
         "bw_pack_ternary": ([P, I, I64, I64, I, P, P, P, SZ, P], I),
         "bw_quantize": ([P, I, I64, I64, I, P, P, P], I),
         "bw_bitlinear_a4": ([P, P, I64, I64, I, P, P, I64, P, P, P], I),
+        "bw_bitlinear_a4_grouped": ([P, P, I64, I64, I, I, P, P, P, P, P, P], I),
         "bw_quantize_bitlinear_a4": ([P, I, I64, I64, I, P, P, I64, P, P, P, P, P], I),
         "bw_quantize_sparse_a8": ([P, P, I, I64, I64, I64, P, P, P, P], I),
         "bw_bitlinear_sparse_a8": ([P, P, I64, I64, P, P, I64, P, P, P], I),
+        "bw_bitlinear_sparse_a8_grouped": ([P, P, I64, I64, I, P, P, P, P, P, P], I),
         "bw_bitlinear_sparse_a8_gather_workspace_bytes": ([I64, I64, I64], SZ),
         "bw_bitlinear_sparse_a8_gather": ([P, P, I64, I64, P, P, I64, P, P, P, SZ, P], I),
         "bw_kv_pack3": ([P, I, I64, I64, I64, I64, P, I64, P, P, P, P, P], I),
@@ -190,6 +192,40 @@ def bw_bitlinear_a4(codes: torch.Tensor, x_scales: torch.Tensor, fmt: int, w_pac
     return y
 
 
+def _grouped_args(weights, M, K, ys, accs, acc_dt):
+    """Host arrays (ctypes) of the grouped calls: device pointers and sizes per product."""
+    n = len(weights)
+    if not 1 <= n <= 4:
+        raise ValueError("1 to 4 products per grouped call")
+    Ns = [beta.shape[0] for _, beta in weights]
+    if ys is None:
+        ys = [None] * n
+    ys = [torch.empty((M, N), dtype=torch.float32, device=weights[0][1].device) if yv is None else yv
+          for yv, N in zip(ys, Ns)]
+    P = ctypes.c_void_p
+    w_arr = (P * n)(*[_dev(w, "w_packed", (torch.uint8,), (N * K // 4,)) for (w, _), N in zip(weights, Ns)])
+    b_arr = (P * n)(*[_dev(b, "beta", (torch.float32,), (N,)) for (_, b), N in zip(weights, Ns)])
+    n_arr = (ctypes.c_int64 * n)(*Ns)
+    y_arr = (P * n)(*[_dev(yv, "y", (torch.float32,), (M, N)) for yv, N in zip(ys, Ns)])
+    a_arr = None
+    if accs is not None:
+        a_arr = (P * n)(*[_opt(a, "acc_dbg", acc_dt, (M, N)) for a, N in zip(accs, Ns)])
+    return n, w_arr, b_arr, n_arr, y_arr, a_arr, ys
+
+
+def bw_bitlinear_a4_grouped(codes: torch.Tensor, x_scales: torch.Tensor, fmt: int, weights, ys=None, accs=None):
+    """bw_bitlinear_a4 for each (w_packed, beta) of `weights` over the same codes, in one launch
+    at prefill sizes; returns the list of y [M][N_g]."""
+    M, Kh = codes.shape
+    K = 2 * Kh
+    acc_dt = (torch.int32,) if fmt == BW_ACT_INT4 else (torch.float32,)
+    n, w_arr, b_arr, n_arr, y_arr, a_arr, ys = _grouped_args(weights, M, K, ys, accs, acc_dt)
+    _check(_lib.bw_bitlinear_a4_grouped(
+        _dev(codes, "codes", (torch.uint8,)), _dev(x_scales, "x_scales", (torch.float32,), (M,)), M, K, fmt, n,
+        w_arr, b_arr, n_arr, y_arr, a_arr, _stream(codes)))
+    return ys
+
+
 def bw_quantize_bitlinear_a4(x: torch.Tensor, fmt: int, w_packed: torch.Tensor, beta: torch.Tensor, y=None,
                              codes=None, scales=None, acc_dbg=None):
     """bw_quantize followed by bw_bitlinear_a4 in one call (one launch for M <= 2);
@@ -245,6 +281,17 @@ def bw_bitlinear_sparse_a8(codes: torch.Tensor, x_scales: torch.Tensor, w_packed
         _dev(y, "y", (torch.float32,), (M, N)), _opt(acc_dbg, "acc_dbg", (torch.int32,), (M, N)),
         _stream(codes)))
     return y
+
+
+def bw_bitlinear_sparse_a8_grouped(codes: torch.Tensor, x_scales: torch.Tensor, weights, ys=None, accs=None):
+    """bw_bitlinear_sparse_a8 for each (w_packed, beta) of `weights` over the same INT8 codes,
+    in one launch at prefill sizes; returns the list of y [M][N_g]."""
+    M, K = codes.shape
+    n, w_arr, b_arr, n_arr, y_arr, a_arr, ys = _grouped_args(weights, M, K, ys, accs, (torch.int32,))
+    _check(_lib.bw_bitlinear_sparse_a8_grouped(
+        _dev(codes, "codes", (torch.int8,)), _dev(x_scales, "x_scales", (torch.float32,), (M,)), M, K, n,
+        w_arr, b_arr, n_arr, y_arr, a_arr, _stream(codes)))
+    return ys
 
 
 def bw_bitlinear_sparse_a8_gather_workspace_bytes(M: int, K: int, N: int) -> int:

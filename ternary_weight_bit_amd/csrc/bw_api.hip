@@ -117,6 +117,51 @@ bw_status bw_bitlinear_a4(const uint8_t* codes, const float* x_scales, int64_t M
                     "bw_bitlinear_a4");
 }
 
+// Products over one set of codes: a single grouped launch of the LDS GEMM
+// when every product takes it at this M, else one launch per product.
+static bw_status bitlinear_grouped(const char* who, int mode, const void* codes, const float* x_scales, int64_t M,
+                                   int64_t K, int n, const uint8_t* const* w, const float* const* beta,
+                                   const int64_t* N, float* const* y, void* const* acc, hipStream_t s) {
+  BW_REQUIRE(n >= 1 && n <= bw::kMaxGroups, BW_ERR_ARG, "%s: need 1 <= n_groups <= %d (n_groups=%d)", who,
+             bw::kMaxGroups, n);
+  BW_REQUIRE(w && beta && N && y, BW_ERR_NULL, "%s: NULL host array", who);
+  for (int g = 0; g < n; ++g) {
+    bw_status st = check_gemm(who, codes, x_scales, M, K, w[g], beta[g], N[g], y[g], acc ? acc[g] : nullptr);
+    if (st != BW_OK) return st;
+  }
+  if (M == 0) return ok();
+  bool grouped = M > bw::kGemvMaxM;
+  for (int g = 0; g < n && grouped; ++g) grouped = bw::gemm_lds_supported(mode, M, K, N[g]);
+  if (grouped) {
+    bw::GemmGroups G{};
+    G.n = n;
+    for (int g = 0; g < n; ++g) {
+      G.w[g] = w[g];
+      G.beta[g] = beta[g];
+      G.y[g] = y[g];
+      G.acc_dbg[g] = acc ? acc[g] : nullptr;
+      G.N[g] = N[g];
+    }
+    return hip_status(bw::launch_gemm_lds_grouped(mode, codes, x_scales, M, K, G, s), who);
+  }
+  for (int g = 0; g < n; ++g) {
+    bw_status st = hip_status(
+        bw::launch_bitlinear(mode, codes, x_scales, M, K, w[g], beta[g], N[g], y[g], acc ? acc[g] : nullptr, s), who);
+    if (st != BW_OK) return st;
+  }
+  return ok();
+}
+
+bw_status bw_bitlinear_a4_grouped(const uint8_t* codes, const float* x_scales, int64_t M, int64_t K,
+                                  bw_act4_fmt fmt, int n_groups, const uint8_t* const* w_packed,
+                                  const float* const* beta, const int64_t* N, float* const* y,
+                                  void* const* acc_dbg, void* stream) {
+  BW_REQUIRE(fmt == BW_ACT_INT4 || fmt == BW_ACT_FP4_E2M1, BW_ERR_DTYPE, "bw_bitlinear_a4_grouped: bad format %d",
+             (int)fmt);
+  return bitlinear_grouped("bw_bitlinear_a4_grouped", fmt == BW_ACT_INT4 ? 0 : 1, codes, x_scales, M, K, n_groups,
+                           w_packed, beta, N, y, acc_dbg, static_cast<hipStream_t>(stream));
+}
+
 bw_status bw_quantize_bitlinear_a4(const void* x, bw_dtype x_dtype, int64_t M, int64_t K, bw_act4_fmt fmt,
                                    const uint8_t* w_packed, const float* beta, int64_t N, uint8_t* codes,
                                    float* scales, float* y, void* acc_dbg, void* stream) {
@@ -168,6 +213,17 @@ bw_status bw_bitlinear_sparse_a8(const int8_t* codes, const float* x_scales, int
   return hip_status(bw::launch_bitlinear(2, codes, x_scales, M, K, w_packed, beta, N, y, acc_dbg,
                                          static_cast<hipStream_t>(stream)),
                     "bw_bitlinear_sparse_a8");
+}
+
+bw_status bw_bitlinear_sparse_a8_grouped(const int8_t* codes, const float* x_scales, int64_t M, int64_t K,
+                                         int n_groups, const uint8_t* const* w_packed,
+                                         const float* const* beta, const int64_t* N, float* const* y,
+                                         int32_t* const* acc_dbg, void* stream) {
+  void* acc[bw::kMaxGroups] = {};
+  if (acc_dbg && n_groups >= 1 && n_groups <= bw::kMaxGroups)
+    for (int g = 0; g < n_groups; ++g) acc[g] = acc_dbg[g];
+  return bitlinear_grouped("bw_bitlinear_sparse_a8_grouped", 2, codes, x_scales, M, K, n_groups, w_packed, beta, N,
+                           y, acc_dbg ? acc : nullptr, static_cast<hipStream_t>(stream));
 }
 
 size_t bw_bitlinear_sparse_a8_gather_workspace_bytes(int64_t M, int64_t K, int64_t N) {

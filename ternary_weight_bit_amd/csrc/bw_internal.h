@@ -46,6 +46,23 @@ bool gemm_lds_supported(int mode, int64_t M, int64_t K, int64_t N);
 hipError_t launch_gemm_lds(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
                            const uint8_t* w_packed, const float* beta, int64_t N, float* y, void* acc_dbg,
                            hipStream_t s);
+// Several products over the same activation codes in one launch: product g
+// takes tiles [tile_end[g-1], tile_end[g]) of one grid, with its own weights,
+// beta, N and y, so the tiles of all of them share the CUs in one schedule.
+constexpr int kMaxGroups = 4;
+struct GemmGroups {
+  const uint8_t* w[kMaxGroups];
+  const float* beta[kMaxGroups];
+  float* y[kMaxGroups];
+  void* acc_dbg[kMaxGroups];
+  int64_t N[kMaxGroups];
+  int tile_end[kMaxGroups];
+  int n;
+};
+// Every product of `g` must satisfy gemm_lds_supported; the caller fills w,
+// beta, y, acc_dbg, N and n (tile_end is filled here).
+hipError_t launch_gemm_lds_grouped(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
+                                   GemmGroups g, hipStream_t s);
 hipError_t launch_bitlinear(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
                             const uint8_t* w_packed, const float* beta, int64_t N, float* y,
                             void* acc_dbg, hipStream_t s);

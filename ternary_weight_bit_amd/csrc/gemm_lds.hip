@@ -78,6 +78,24 @@ __device__ __forceinline__ int a_slot(int row, int p) {
   else return p ^ ((row >> 2) & 3);
 }
 
+// Field of group g (g < kMaxGroups) without indexing the kernel argument
+// array by a variable (which would copy it to scratch).
+template <typename T>
+__device__ __forceinline__ T pick(const T (&a)[kMaxGroups], int g) {
+  static_assert(kMaxGroups == 4, "pick covers four groups");
+  return g == 0 ? a[0] : g == 1 ? a[1] : g == 2 ? a[2] : a[3];
+}
+
+// Group of grid tile tg (tiles in group order), and tg's index inside it.
+__device__ __forceinline__ int group_of(const GemmGroups& G, int tg, int& t_local) {
+  int gi = 0;
+  if (G.n > 1 && tg >= G.tile_end[0]) gi = 1;
+  if (G.n > 2 && tg >= G.tile_end[1]) gi = 2;
+  if (G.n > 3 && tg >= G.tile_end[2]) gi = 3;
+  t_local = tg - (gi == 0 ? 0 : pick(G.tile_end, gi - 1));
+  return gi;
+}
+
 // Epilogue of one wave's 64 x 64 accumulator block, y = fl(fl(q * sx) * beta).
 // The accumulator tile is y^T: lane l holds token l % 32 and channels
 // 8*(e/4) + 4*(l/32) + (e%4) of each 32 x 32 product, so elements 4g..4g+3 are
@@ -162,9 +180,8 @@ __device__ __forceinline__ void epilogue_staged(const AccT (&acc)[2][2], uint8_t
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_gemm_lds(
-    const uint8_t* __restrict__ A, const float* __restrict__ sx, int64_t M, int64_t K,
-    const uint8_t* __restrict__ Wp, const float* __restrict__ beta, int64_t N, float* __restrict__ y,
-    void* __restrict__ acc_dbg, int MT, int NT) {
+    const uint8_t* __restrict__ A, const float* __restrict__ sx, int64_t M, int64_t K, const GemmGroups G,
+    int MT) {
   using C = LdsCfg<MODE>;
   __shared__ __attribute__((aligned(1024))) uint8_t A0[C::AStage];
   __shared__ __attribute__((aligned(1024))) uint8_t A1[C::AStage];
@@ -182,10 +199,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
   const int li = lane & 31;
   const int lh = lane >> 5;
 
-  // XCD-aware tile order: workgroups b, b+8, b+16, ... share an XCD
-  const int T = MT * NT;
+  // XCD-aware tile order over all groups: workgroups b, b+8, b+16, ... share an XCD
+  const int T = pick(G.tile_end, G.n - 1);
   const int b = blockIdx.x;
-  const int t = (T % 8 == 0) ? (b % 8) * (T / 8) + b / 8 : b;
+  const int tg = (T % 8 == 0) ? (b % 8) * (T / 8) + b / 8 : b;
+  int t;
+  const int gi = group_of(G, tg, t);
+  const uint8_t* __restrict__ const Wp = pick(G.w, gi);
+  const float* __restrict__ const beta = pick(G.beta, gi);
+  float* __restrict__ const y = pick(G.y, gi);
+  void* __restrict__ const acc_dbg = pick(G.acc_dbg, gi);
+  const int64_t N = pick(G.N, gi);
   const int64_t m0 = static_cast<int64_t>(t % MT) * BM;
   const int64_t n0 = static_cast<int64_t>(t / MT) * BN;
 
@@ -365,9 +389,8 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_gemm_lds256(
-    const uint8_t* __restrict__ A, const float* __restrict__ sx, int64_t M, int64_t K,
-    const uint8_t* __restrict__ Wp, const float* __restrict__ beta, int64_t N, float* __restrict__ y,
-    void* __restrict__ acc_dbg, int MT, int NT) {
+    const uint8_t* __restrict__ A, const float* __restrict__ sx, int64_t M, int64_t K, const GemmGroups G,
+    int MT) {
   static_assert(MODE != MODE_INT8, "4-bit codes only");
   constexpr int AROW = 128;           // bytes per activation row per stage (256 codes)
   constexpr int AStage = BM * AROW;   // 16 KB
@@ -386,9 +409,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
   const int li = lane & 31;
   const int lh = lane >> 5;
 
-  const int T = MT * NT;
+  // XCD-aware tile order over all groups, as in k_gemm_lds
+  const int T = pick(G.tile_end, G.n - 1);
   const int b = blockIdx.x;
-  const int t = (T % 8 == 0) ? (b % 8) * (T / 8) + b / 8 : b;
+  const int tg = (T % 8 == 0) ? (b % 8) * (T / 8) + b / 8 : b;
+  int t;
+  const int gi = group_of(G, tg, t);
+  const uint8_t* __restrict__ const Wp = pick(G.w, gi);
+  const float* __restrict__ const beta = pick(G.beta, gi);
+  float* __restrict__ const y = pick(G.y, gi);
+  void* __restrict__ const acc_dbg = pick(G.acc_dbg, gi);
+  const int64_t N = pick(G.N, gi);
   const int64_t m0 = static_cast<int64_t>(t % MT) * BM;
   const int64_t n0 = static_cast<int64_t>(t / MT) * BN;
   const int64_t kblocks = K >> 6;
@@ -545,34 +576,56 @@ bool gemm_lds_supported(int mode, int64_t M, int64_t K, int64_t N) {
   return K % 128 == 0 && a_bytes < (int64_t{1} << 31) && w_bytes < (int64_t{1} << 31);
 }
 
-hipError_t launch_gemm_lds(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
-                           const uint8_t* w_packed, const float* beta, int64_t N, float* y, void* acc_dbg,
-                           hipStream_t s) {
+hipError_t launch_gemm_lds_grouped(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
+                                   GemmGroups G, hipStream_t s) {
   const int MT = static_cast<int>((M + BM - 1) / BM);
-  const int NT = static_cast<int>((N + BN - 1) / BN);
-  const dim3 grid(static_cast<unsigned>(MT * NT)), block(kThreads);
+  int T = 0;
+  for (int g = 0; g < kMaxGroups; ++g) {
+    if (g < G.n) {
+      T += MT * static_cast<int>((G.N[g] + BN - 1) / BN);
+    } else {  // unused slots: valid values, never selected
+      G.w[g] = G.w[0];
+      G.beta[g] = G.beta[0];
+      G.y[g] = G.y[0];
+      G.acc_dbg[g] = G.acc_dbg[0];
+      G.N[g] = G.N[0];
+    }
+    G.tile_end[g] = T;
+  }
+  const dim3 grid(static_cast<unsigned>(T)), block(kThreads);
   const uint8_t* A = static_cast<const uint8_t*>(codes);
   const bool k256 = K % 256 == 0;
   switch (mode) {
     case MODE_INT4:
       if (k256)
-        hipLaunchKernelGGL(k_gemm_lds256<MODE_INT4>, grid, block, 0, s, A, sx, M, K, w_packed, beta, N, y, acc_dbg, MT,
-                           NT);
+        hipLaunchKernelGGL(k_gemm_lds256<MODE_INT4>, grid, block, 0, s, A, sx, M, K, G, MT);
       else
-        hipLaunchKernelGGL(k_gemm_lds<MODE_INT4>, grid, block, 0, s, A, sx, M, K, w_packed, beta, N, y, acc_dbg, MT, NT);
+        hipLaunchKernelGGL(k_gemm_lds<MODE_INT4>, grid, block, 0, s, A, sx, M, K, G, MT);
       break;
     case MODE_FP4:
       if (k256)
-        hipLaunchKernelGGL(k_gemm_lds256<MODE_FP4>, grid, block, 0, s, A, sx, M, K, w_packed, beta, N, y, acc_dbg, MT,
-                           NT);
+        hipLaunchKernelGGL(k_gemm_lds256<MODE_FP4>, grid, block, 0, s, A, sx, M, K, G, MT);
       else
-        hipLaunchKernelGGL(k_gemm_lds<MODE_FP4>, grid, block, 0, s, A, sx, M, K, w_packed, beta, N, y, acc_dbg, MT, NT);
+        hipLaunchKernelGGL(k_gemm_lds<MODE_FP4>, grid, block, 0, s, A, sx, M, K, G, MT);
       break;
     default:
-      hipLaunchKernelGGL(k_gemm_lds<MODE_INT8>, grid, block, 0, s, A, sx, M, K, w_packed, beta, N, y, acc_dbg, MT, NT);
+      hipLaunchKernelGGL(k_gemm_lds<MODE_INT8>, grid, block, 0, s, A, sx, M, K, G, MT);
       break;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_lds(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
+                           const uint8_t* w_packed, const float* beta, int64_t N, float* y, void* acc_dbg,
+                           hipStream_t s) {
+  GemmGroups G{};
+  G.n = 1;
+  G.w[0] = w_packed;
+  G.beta[0] = beta;
+  G.y[0] = y;
+  G.acc_dbg[0] = acc_dbg;
+  G.N[0] = N;
+  return launch_gemm_lds_grouped(mode, codes, sx, M, K, G, s);
 }
 
 }  // namespace bw

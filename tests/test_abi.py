@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -68,6 +68,28 @@ def test_bitlinear_validation():
     g = lib.bw_bitlinear_sparse_a8
     assert g(A, A, 8, 11008, A, A, 4095, A, None, None) == 2
     assert g(A, None, 8, 11008, A, A, 4096, A, None, None) == 1
+
+
+def test_grouped_validation():
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    w = (P * 2)(A, A)
+    b = (P * 2)(A, A)
+    y = (P * 2)(A, A)
+    n_ok = (I64 * 2)(128, 4096)
+    n_bad = (I64 * 2)(128, 100)
+    f = lib.bw_bitlinear_a4_grouped
+    assert f(A, A, 64, 4096, 0, 0, w, b, n_ok, y, None, None) == 5  # n_groups
+    assert f(A, A, 64, 4096, 0, 5, w, b, n_ok, y, None, None) == 5
+    assert f(A, A, 64, 4096, 0, 2, w, b, n_bad, y, None, None) == 2  # second product's N % 16
+    assert f(A, A, 64, 4096, 3, 2, w, b, n_ok, y, None, None) == 4  # fmt
+    assert f(A, A, 64, 4096, 0, 2, None, b, n_ok, y, None, None) == 1  # host array
+    y_mis = (P * 2)(A, MIS)
+    assert f(A, A, 64, 4096, 0, 2, w, b, n_ok, y_mis, None, None) == 3
+    assert f(None, None, 0, 4096, 0, 2, w, b, n_ok, y, None, None) == 0  # no tokens
+    g = lib.bw_bitlinear_sparse_a8_grouped
+    assert g(A, A, 64, 11008, 0, w, b, n_ok, y, None, None) == 5
+    assert g(A, A, 64, 11008, 2, w, b, n_bad, y, None, None) == 2
+    assert g(A, None, 64, 11008, 2, w, b, n_ok, y, None, None) == 1
 
 
 def test_gather_validation():
