@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_chunk(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar loop bounds)
   const int phase = wave >> 1;                  // positions phase, phase + 4, ...
   const int g = lane % G;                       // 32-dim group
   const int hl = (wave & 1) * HW + lane / G;    // head within the head block
@@ -268,13 +268,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_chunk(
         ds[j] = bload_f32(ksr, os + 4 * j * sstride);
       }
     };
-    load_k(phase, pl, sc);
-    for (int j0 = phase; j0 < np; j0 += 4 * kUnroll) {
-      load_k(j0 + 4 * kUnroll, nl, ns);
+    auto score = [&](int j0, const uint32_t (&kl)[kUnroll][3], const float (&ks)[kUnroll]) {
 #pragma unroll
       for (int j = 0; j < kUnroll; ++j) {
         uint32_t u[8];
-        unpack_group(pl[j][0], pl[j][1], pl[j][2], u);
+        unpack_group(kl[j][0], kl[j][1], kl[j][2], u);
         int dg[4] = {0, 0, 0, 0};
 #pragma unroll
         for (int k = 0; k < 8; ++k)
@@ -288,15 +286,21 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_chunk(
         const float tf = fmaf(static_cast<float>(hi), 16777216.0f, static_cast<float>(lo));
         const float dot = groups_sum_last<G>(tf);
         const int p = j0 + 4 * j;
-        if (g == G - 1 && hok && p < np) s_z[p * HP + h] = dot * qunit * sc[j] * inv_sqrt_d;
+        if (g == G - 1 && hok && p < np) s_z[p * HP + h] = dot * qunit * ks[j] * inv_sqrt_d;
       }
-#pragma unroll
-      for (int j = 0; j < kUnroll; ++j) {
-        pl[j][0] = nl[j][0];
-        pl[j][1] = nl[j][1];
-        pl[j][2] = nl[j][2];
-        sc[j] = ns[j];
-      }
+    };
+    // two register buffers in alternation (no copy from one to the other, which
+    // would wait for the batch just issued): batch i + 1 loads while batch i
+    // is scored
+    load_k(phase, pl, sc);
+    for (int j0 = phase; j0 < np;) {
+      load_k(j0 + 4 * kUnroll, nl, ns);
+      score(j0, pl, sc);
+      j0 += 4 * kUnroll;
+      if (j0 >= np) break;
+      load_k(j0 + 4 * kUnroll, pl, sc);
+      score(j0, nl, ns);
+      j0 += 4 * kUnroll;
     }
     if (hb == 0) scan_specials();  // uniform: every thread takes the barriers
     // special positions: rescored from their 4-bit codes by the lanes of the
@@ -363,18 +367,16 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_chunk(
         ds[j] = bload_f32(vsr, os + 4 * j * sstride);
       }
     };
-    load_v(phase, pl, sc);
-    for (int j0 = phase; j0 < np; j0 += 4 * kUnroll) {
-      load_v(j0 + 4 * kUnroll, nl, ns);
+    auto accumulate = [&](int j0, const uint32_t (&vl)[kUnroll][3], const float (&vsc)[kUnroll]) {
 #pragma unroll
       for (int j = 0; j < kUnroll; ++j) {
         const int p = j0 + 4 * j;
         const int pc = p < np ? p : 0;
         const bool live = p < np && !((s_spec[pc >> 5] >> (pc & 31)) & 1u);
-        const float w = live ? s_z[pc * HP + hc] * sc[j] : 0.0f;
+        const float w = live ? s_z[pc * HP + hc] * vsc[j] : 0.0f;
         const float wu = w * inv_unit;  // exact: power-of-two scaling
         uint32_t u[8];
-        unpack_group(pl[j][0], pl[j][1], pl[j][2], u);
+        unpack_group(vl[j][0], vl[j][1], vl[j][2], u);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const float2 lo2 = byte_pair_fp8<false>(u[k]);  // codes k, k + 8
@@ -386,13 +388,16 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_chunk(
         }
         wsum += w;
       }
-#pragma unroll
-      for (int j = 0; j < kUnroll; ++j) {
-        pl[j][0] = nl[j][0];
-        pl[j][1] = nl[j][1];
-        pl[j][2] = nl[j][2];
-        sc[j] = ns[j];
-      }
+    };
+    load_v(phase, pl, sc);
+    for (int j0 = phase; j0 < np;) {
+      load_v(j0 + 4 * kUnroll, nl, ns);
+      accumulate(j0, pl, sc);
+      j0 += 4 * kUnroll;
+      if (j0 >= np) break;
+      load_v(j0 + 4 * kUnroll, pl, sc);
+      accumulate(j0, nl, ns);
+      j0 += 4 * kUnroll;
     }
     // remove the +4 of the codes, add the special positions' 4-bit terms
 #pragma unroll
