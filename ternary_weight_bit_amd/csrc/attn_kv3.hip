@@ -211,6 +211,24 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_chunk(
     const int64_t h = hb + hl;
     const bool hok = h < H;
     const int64_t hc = hok ? h : H - 1;
+    // A batch's loads are issued together; positions past the chunk read
+    // zeros and are not stored.  The next batch's loads are issued before this
+    // batch is computed (two register buffers); the first batch is issued
+    // before the query is converted, which hides its latency.
+    const uint32_t t3 = static_cast<uint32_t>(hc) * VB + 12 * g;  // this lane's words at position 0
+    const uint32_t ts = static_cast<uint32_t>(hc) * 4;
+    uint32_t pl[kUnroll][3], nl[kUnroll][3];
+    float sc[kUnroll], ns[kUnroll];
+    auto load_k = [&](int j0, uint32_t (&dl)[kUnroll][3], float (&ds)[kUnroll]) {
+      const uint32_t o3 = t3 + static_cast<uint32_t>(j0) * pstride;
+      const uint32_t os = ts + static_cast<uint32_t>(j0) * sstride;
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j) {
+        bload12(kr, o3 + 4 * j * pstride, dl[j]);
+        ds[j] = bload_f32(ksr, os + 4 * j * sstride);
+      }
+    };
+    load_k(phase, pl, sc);
     const float* __restrict__ qv = q + b * q_stride + hc * D + 32 * g;
     // fixed-point query: Q_i = rne(q_i * 2^30 / max|q|) (fp64 product), four
     // balanced base-256 digits; its deviation from q is at most 2^-31 max|q|
@@ -252,22 +270,6 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_chunk(
     const int q4lo = T & 0xFFFFFF;
     const int q4hi = ((T - q4lo) >> 24) + 4 * dsum[3];
 
-    // A batch's loads are issued together; positions past the chunk read
-    // zeros and are not stored.  The next batch's loads are issued before this
-    // batch is computed (two register buffers).
-    const uint32_t t3 = static_cast<uint32_t>(hc) * VB + 12 * g;  // this lane's words at position 0
-    const uint32_t ts = static_cast<uint32_t>(hc) * 4;
-    uint32_t pl[kUnroll][3], nl[kUnroll][3];
-    float sc[kUnroll], ns[kUnroll];
-    auto load_k = [&](int j0, uint32_t (&dl)[kUnroll][3], float (&ds)[kUnroll]) {
-      const uint32_t o3 = t3 + static_cast<uint32_t>(j0) * pstride;
-      const uint32_t os = ts + static_cast<uint32_t>(j0) * sstride;
-#pragma unroll
-      for (int j = 0; j < kUnroll; ++j) {
-        bload12(kr, o3 + 4 * j * pstride, dl[j]);
-        ds[j] = bload_f32(ksr, os + 4 * j * sstride);
-      }
-    };
     auto score = [&](int j0, const uint32_t (&kl)[kUnroll][3], const float (&ks)[kUnroll]) {
 #pragma unroll
       for (int j = 0; j < kUnroll; ++j) {
@@ -292,7 +294,6 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_chunk(
     // two register buffers in alternation (no copy from one to the other, which
     // would wait for the batch just issued): batch i + 1 loads while batch i
     // is scored
-    load_k(phase, pl, sc);
     for (int j0 = phase; j0 < np;) {
       load_k(j0 + 4 * kUnroll, nl, ns);
       score(j0, pl, sc);
@@ -323,6 +324,20 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_chunk(
     }
   }
   __syncthreads();
+
+  // the first batch of pass 2's values (head block 0) loads during the softmax
+  uint32_t v0l[kUnroll][3];
+  float v0s[kUnroll];
+  {
+    const int64_t hc0 = hl < H ? hl : H - 1;
+    const uint32_t o3 = static_cast<uint32_t>(hc0) * VB + 12 * g + static_cast<uint32_t>(phase) * pstride;
+    const uint32_t os = static_cast<uint32_t>(hc0) * 4 + static_cast<uint32_t>(phase) * sstride;
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      bload12(vr, o3 + 4 * j * pstride, v0l[j]);
+      v0s[j] = bload_f32(vsr, os + 4 * j * sstride);
+    }
+  }
 
   // ---- per head over the chunk: m = max z, e = exp(z - m), l = sum e
   for (int64_t h = wave; h < H; h += kAttnThreads / 64) {
@@ -389,7 +404,17 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_chunk(
         wsum += w;
       }
     };
-    load_v(phase, pl, sc);
+    if (hb == 0) {
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j) {
+        pl[j][0] = v0l[j][0];
+        pl[j][1] = v0l[j][1];
+        pl[j][2] = v0l[j][2];
+        sc[j] = v0s[j];
+      }
+    } else {
+      load_v(phase, pl, sc);
+    }
     for (int j0 = phase; j0 < np;) {
       load_v(j0 + 4 * kUnroll, nl, ns);
       accumulate(j0, pl, sc);
