@@ -131,7 +131,12 @@ static bw_status bitlinear_grouped(const char* who, int mode, const void* codes,
   }
   if (M == 0) return ok();
   bool grouped = M > bw::kGemvMaxM;
-  for (int g = 0; g < n && grouped; ++g) grouped = bw::gemm_lds_supported(mode, M, K, N[g]);
+  int64_t tiles = 0;
+  for (int g = 0; g < n && grouped; ++g) {
+    grouped = bw::gemm_lds_supported(mode, M, K, N[g]);
+    tiles += grouped ? bw::gemm_lds_tiles(M, N[g]) : 0;
+  }
+  grouped = grouped && tiles < (int64_t{1} << 31);
   if (grouped) {
     bw::GemmGroups G{};
     G.n = n;

@@ -42,7 +42,8 @@ hipError_t launch_gemm(int mode, const void* codes, const float* sx, int64_t M, 
                        hipStream_t s);
 // Prefill GEMM with operands loaded straight into LDS; launch_gemm uses it
 // whenever gemm_lds_supported holds (K % 128 == 0, operands below 2 GiB).
-bool gemm_lds_supported(int mode, int64_t M, int64_t K, int64_t N);
+bool gemm_lds_supported(int mode, int64_t M, int64_t K, int64_t N);  // includes tiles < 2^30
+int64_t gemm_lds_tiles(int64_t M, int64_t N);                          // grid tiles of one product
 hipError_t launch_gemm_lds(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
                            const uint8_t* w_packed, const float* beta, int64_t N, float* y, void* acc_dbg,
                            hipStream_t s);
@@ -59,8 +60,9 @@ struct GemmGroups {
   int tile_end[kMaxGroups];
   int n;
 };
-// Every product of `g` must satisfy gemm_lds_supported; the caller fills w,
-// beta, y, acc_dbg, N and n (tile_end is filled here).
+// Every product of `g` must satisfy gemm_lds_supported and their tiles must
+// sum below 2^31; the caller fills w, beta, y, acc_dbg, N and n (tile_end is
+// filled here).
 hipError_t launch_gemm_lds_grouped(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
                                    GemmGroups g, hipStream_t s);
 hipError_t launch_bitlinear(int mode, const void* codes, const float* sx, int64_t M, int64_t K,

@@ -570,10 +570,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
 
 }  // namespace
 
+int64_t gemm_lds_tiles(int64_t M, int64_t N) { return ((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
+
 bool gemm_lds_supported(int mode, int64_t M, int64_t K, int64_t N) {
   const int64_t a_bytes = M * ((mode == 2) ? K : K / 2);
   const int64_t w_bytes = N * K / 4;
-  return K % 128 == 0 && a_bytes < (int64_t{1} << 31) && w_bytes < (int64_t{1} << 31);
+  return K % 128 == 0 && a_bytes < (int64_t{1} << 31) && w_bytes < (int64_t{1} << 31) &&
+         gemm_lds_tiles(M, N) < (int64_t{1} << 30);
 }
 
 hipError_t launch_gemm_lds_grouped(int mode, const void* codes, const float* sx, int64_t M, int64_t K,
