@@ -7,7 +7,10 @@
 //   * ternary codes -> int8 bytes of 64*t (code moved to bits 7..6:
 //     00 -> 0, 01 -> 64, 11 -> -64);
 //   * INT8 codes are used as they are;
-//   * e2m1 codes are used as they are; ternary codes become e2m1 +-1.0.
+//   * e2m1 codes are used as they are; ternary codes become e2m1 +-2.0 (the
+//     code moved to bits 3..2 of a nibble: sign and high exponent bit), and the
+//     MFMA's block scale for the weight operand is 2^-1, so the products are
+//     exactly v * t.
 #pragma once
 
 #include "bw_device.h"
@@ -58,11 +61,14 @@ __device__ __forceinline__ v4i widen_w_a8(uint32_t w) {
 }
 
 // Ternary word in A4 slot order -> two words of e2m1 nibbles: `lo` holds k
-// offsets 0..7, `hi` 8..15 (nibble j of each = offset j of its half).
-// Code 01 (+1) -> 0b0010 (+1.0), 11 (-1) -> 0b1010 (-1.0), 00 -> 0.
+// offsets 0..7, `hi` 8..15 (nibble j of each = offset j of its half).  The
+// code already sits in two bits of a nibble; moved to bits 3..2 it reads as
+// e2m1: 01 (+1) -> 0b0100 (+2.0), 11 (-1) -> 0b1100 (-2.0), 00 -> 0.
+// The weight operand's MFMA scale kE2m1WeightScale halves it back.
+constexpr int kE2m1WeightScale = 126;  // E8M0 block scale 2^(126 - 127)
 __device__ __forceinline__ void widen_w_e2m1(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  lo = ((w << 1) & 0x22222222u) | ((w << 2) & 0x88888888u);
-  hi = ((w >> 1) & 0x22222222u) | (w & 0x88888888u);
+  lo = (w << 2) & 0xCCCCCCCCu;
+  hi = w & 0xCCCCCCCCu;
 }
 
 __device__ __forceinline__ v4i as_v4i(uint4 x) {

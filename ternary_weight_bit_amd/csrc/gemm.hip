@@ -16,7 +16,8 @@
 // 128 k of packed activations and weights into LDS
 // through registers, double-buffered with one barrier per stage; operands are
 // widened in registers right before v_mfma_i32_32x32x32_i8 (INT4/INT8 codes)
-// or v_mfma_scale_f32_32x32x64_f8f6f4 (e2m1 codes, block scales 2^0).
+// or v_mfma_scale_f32_32x32x64_f8f6f4 (e2m1 codes; block scales 2^0 for the
+// activations, 2^-1 for the weights, which enter as +-2.0).
 // LDS rows are padded (A by 16 bytes, B by 8) so the 32 lanes of a fragment
 // read hit distinct banks.  Tiles are numbered so that each of the 8 XCDs
 // (workgroup id mod 8) works through a contiguous range of tiles.
@@ -185,8 +186,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
           const int row = wm * 64 + r * 32 + li;
           const uint4 x = *reinterpret_cast<const uint4*>(&As[cur][row * C::ASTR + s * 32 + 16 * lh]);
           const v8i a = fp4_operand(x.x, x.y, x.z, x.w);
-          acc[r][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b0, acc[r][0], 4, 4, 0, 127, 0, 127);
-          acc[r][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b1, acc[r][1], 4, 4, 0, 127, 0, 127);
+          acc[r][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b0, acc[r][0], 4, 4, 0, 127, 0, kE2m1WeightScale);
+          acc[r][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b1, acc[r][1], 4, 4, 0, 127, 0, kE2m1WeightScale);
         }
       }
     }

@@ -292,8 +292,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
           const int row = wm * 64 + r * 32 + li;
           const uint4 x = *reinterpret_cast<const uint4*>(As + row * 64 + 16 * a_slot<MODE>(row, 2 * s + lh));
           const v8i a = fp4_operand(x.x, x.y, x.z, x.w);
-          acc[r][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b0, a, acc[r][0], 4, 4, 0, 127, 0, 127);
-          acc[r][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b1, a, acc[r][1], 4, 4, 0, 127, 0, 127);
+          acc[r][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b0, a, acc[r][0], 4, 4, 0, kE2m1WeightScale, 0, 127);
+          acc[r][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b1, a, acc[r][1], 4, 4, 0, kE2m1WeightScale, 0, 127);
         }
       } else {
         v4i b00, b01, b10, b11;
@@ -506,8 +506,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
       for (int r = 0; r < 2; ++r) {
         const uint4 x = r ? f.x1 : f.x0;
         const v8i a = fp4_operand(x.x, x.y, x.z, x.w);
-        acc[r][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b0, a, acc[r][0], 4, 4, 0, 127, 0, 127);
-        acc[r][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b1, a, acc[r][1], 4, 4, 0, 127, 0, 127);
+        acc[r][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b0, a, acc[r][0], 4, 4, 0, kE2m1WeightScale, 0, 127);
+        acc[r][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b1, a, acc[r][1], 4, 4, 0, kE2m1WeightScale, 0, 127);
       }
     } else {
       const v4i b00 = widen_w_a4(f.w0.x), b01 = widen_w_a4(f.w0.y);

@@ -60,9 +60,11 @@ __device__ __forceinline__ void mfma_tile(typename TileOps<MODE>::acc_t& acc, co
     acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_v4i(a[3]), widen_w_a8(wv.w), acc, 0, 0, 0);
   } else {
     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fp4_operand(a[0].x, a[0].y, a[0].z, a[0].w),
-                                                           fp4_weights(wv.x, wv.y), acc, 4, 4, 0, 127, 0, 127);
+                                                           fp4_weights(wv.x, wv.y), acc, 4, 4, 0, 127, 0,
+                                                           kE2m1WeightScale);
     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fp4_operand(a[1].x, a[1].y, a[1].z, a[1].w),
-                                                           fp4_weights(wv.z, wv.w), acc, 4, 4, 0, 127, 0, 127);
+                                                           fp4_weights(wv.z, wv.w), acc, 4, 4, 0, 127, 0,
+                                                           kE2m1WeightScale);
   }
 }
 
