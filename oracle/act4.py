@@ -15,6 +15,13 @@ Readings (the pages give no formula):
   magnitude, ties to the even code (mantissa bit 0), saturating at 6, sign bit
   copied from t;
 * packed storage: two codes per byte, the even k in the low nibble.
+* a second storage of the same INT4 values (not from the pages: the operand
+  format of the fp6 matrix instructions): each value q as a 6-bit e2m3 field
+  (sign bit, then |q| in five bits, which the OCP Microscaling e2m3 format -
+  1 sign, 2 exponent bits with bias 1, 3 mantissa bits, subnormals - reads as
+  q/8); per 64 values, the 24-byte little-endian bit streams S0 (values 0..31)
+  and S1 (values 32..63) are stored as S0[0:16], S1[0:16], S0[16:24],
+  S1[16:24].
 """
 from __future__ import annotations
 
@@ -104,3 +111,56 @@ def unpack_nibbles(packed: np.ndarray, signed: bool) -> np.ndarray:
     if signed:
         out = np.where(out >= 8, out - 16, out)
     return out.astype(np.int8) if signed else out.astype(np.uint8)
+
+
+def e2m3_fields(q: np.ndarray) -> np.ndarray:
+    """6-bit field of each INT4 value: (q < 0) << 5 | |q| (uint8)."""
+    q = np.asarray(q).astype(np.int16)
+    assert q.min(initial=0) >= -15 and q.max(initial=0) <= 15
+    return (((q < 0).astype(np.int16) << 5) | np.abs(q)).astype(np.uint8)
+
+
+def pack_int4_e2m3(q: np.ndarray) -> np.ndarray:
+    """[M][K] INT4 values (K % 64 == 0) -> uint8 [M][3K/4] in the e2m3 storage.
+
+    Four fields f0..f3 make 24 bits f0 | f1 << 6 | f2 << 12 | f3 << 18, three
+    little-endian bytes; eight such runs form the 24-byte stream of 32 values."""
+    q = np.asarray(q)
+    M, K = q.shape
+    assert K % 64 == 0
+    f = e2m3_fields(q).astype(np.uint32).reshape(M, K // 64, 2, 8, 4)
+    run = f[..., 0] | (f[..., 1] << 6) | (f[..., 2] << 12) | (f[..., 3] << 18)
+    stream = np.stack([run & 0xFF, (run >> 8) & 0xFF, run >> 16], axis=-1).astype(np.uint8)
+    stream = stream.reshape(M, K // 64, 2, 24)  # [row][group][S0/S1][byte]
+    group = np.concatenate([stream[:, :, 0, :16], stream[:, :, 1, :16], stream[:, :, 0, 16:], stream[:, :, 1, 16:]],
+                           axis=-1)
+    return np.ascontiguousarray(group.reshape(M, K // 64 * 48))
+
+
+def e2m3_value(f: np.ndarray) -> np.ndarray:
+    """Value of each 6-bit e2m3 field (float64): sign bit 5, exponent bits 4..3
+    (bias 1), mantissa bits 2..0; exponent 0 is subnormal (mantissa / 8)."""
+    f = np.asarray(f).astype(np.int64)
+    sign = np.where((f >> 5) & 1, -1.0, 1.0)
+    e = (f >> 3) & 3
+    m = (f & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0, np.exp2(e - 1.0) * (1.0 + m / 8.0))
+    return sign * mag
+
+
+def unpack_int4_e2m3(packed: np.ndarray, K: int) -> np.ndarray:
+    """Inverse of pack_int4_e2m3 by another route: the group's bytes back into
+    the two streams, the streams into bits (numpy's little-endian bit order),
+    six bits per field, and each field's e2m3 value times 8."""
+    p = np.asarray(packed, dtype=np.uint8)
+    M = p.shape[0]
+    g = p.reshape(M, K // 64, 48)
+    s0 = np.concatenate([g[:, :, 0:16], g[:, :, 32:40]], axis=-1)
+    s1 = np.concatenate([g[:, :, 16:32], g[:, :, 40:48]], axis=-1)
+    streams = np.stack([s0, s1], axis=2)  # [M][groups][2][24]
+    bits = np.unpackbits(streams, axis=-1, bitorder="little").reshape(M, K // 64, 2, 32, 6)
+    fields = (bits.astype(np.int64) << np.arange(6)).sum(axis=-1)
+    v = e2m3_value(fields) * 8.0
+    q = np.rint(v)
+    assert np.array_equal(q, v), "field is not an integer multiple of 1/8"
+    return q.reshape(M, K).astype(np.int8)

@@ -129,3 +129,61 @@ def test_fp4_decode_and_error_bound():
     t = (x * (np.float32(6) / np.abs(x).max(axis=1))[:, None]).astype(np.float64)
     gap = np.where(np.abs(t) < 2, 0.5, np.where(np.abs(t) < 4, 1.0, 2.0))
     assert np.all(np.abs(t - v) <= gap / 2 + 1e-12)
+
+
+# ---- INT4 values stored as e2m3 fields (operand of the fp6 matrix instructions)
+
+def test_e2m3_worked_group():
+    g = _load("int4_e2m3_worked.json")
+    q = np.zeros((1, 64), dtype=np.int8)
+    for k, v in g["q_nonzero"].items():
+        q[0, int(k)] = v
+    want = np.zeros(48, dtype=np.uint8)
+    for k, v in g["bytes_nonzero"].items():
+        want[int(k)] = v
+    assert act4.pack_int4_e2m3(q)[0].tolist() == want.tolist()
+    assert np.array_equal(act4.unpack_int4_e2m3(act4.pack_int4_e2m3(q), 64), q)
+
+
+def test_e2m3_value_table():
+    """The 32 magnitudes of e2m3 (OCP Microscaling): 0 .. 7/8 in steps of 1/8
+    (subnormal), then 1 .. 15/8, 2 .. 3.75 by 1/4, 4 .. 7.5 by 1/2."""
+    want = [m / 8 for m in range(8)] + [1 + m / 8 for m in range(8)] + [2 + m / 4 for m in range(8)] + \
+        [4 + m / 2 for m in range(8)]
+    assert act4.e2m3_value(np.arange(32)).tolist() == want
+    assert act4.e2m3_value(np.arange(32, 64)).tolist() == [-w for w in want]
+    # |q| <= 15 written as the 5-bit magnitude reads as q / 8: the subnormals and
+    # the first normal binade are spaced by 1/8
+    q = np.arange(-15, 16)
+    assert np.array_equal(act4.e2m3_value(act4.e2m3_fields(q)) * 8, q.astype(np.float64))
+
+
+def _pack_e2m3_by_ints(q):
+    """Independent packer: each 32-value stream as one Python integer."""
+    M, K = q.shape
+    out = bytearray()
+    for m in range(M):
+        for g in range(K // 64):
+            streams = []
+            for h in range(2):
+                v = 0
+                for j in range(32):
+                    x = int(q[m, 64 * g + 32 * h + j])
+                    v |= ((32 if x < 0 else 0) | abs(x)) << (6 * j)
+                streams.append(v.to_bytes(24, "little"))
+            out += streams[0][:16] + streams[1][:16] + streams[0][16:] + streams[1][16:]
+    return np.frombuffer(bytes(out), dtype=np.uint8).reshape(M, K // 64 * 48)
+
+
+def test_e2m3_pack_matches_integer_streams_and_round_trips():
+    rs = np.random.default_rng(7)
+    q = rs.integers(-8, 8, size=(5, 192)).astype(np.int8)
+    q[0, :16] = np.arange(-8, 8)
+    p = act4.pack_int4_e2m3(q)
+    assert p.shape == (5, 144)
+    assert np.array_equal(p, _pack_e2m3_by_ints(q))
+    assert np.array_equal(act4.unpack_int4_e2m3(p, 192), q)
+    # a quantized row: the storage holds exactly the INT4 codes
+    x = rs.standard_normal((3, 256)).astype(np.float32)
+    qi, _ = act4.quantize_int4(x)
+    assert np.array_equal(act4.unpack_int4_e2m3(act4.pack_int4_e2m3(qi), 256), qi)
