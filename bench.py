@@ -61,7 +61,7 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0  # dense int8 MFMA, MI355X
-FP4_PEAK_TOPS = 10100.0  # dense fp4/fp6 MFMA, MI355X
+FP4_PEAK_TOPS = 10100.0  # dense fp4/fp6 MFMA, MI355X (the e2m3 x e2m1 products run at this rate)
 
 M_PREFILL, HIDDEN, FFN = 2048, 4096, 11008
 
@@ -144,6 +144,8 @@ class Bench:
         del self.w_up
         self.c4 = t.empty((M_PREFILL, HIDDEN // 2), dtype=t.uint8, device=dev)
         self.s4 = t.empty(M_PREFILL, dtype=t.float32, device=dev)
+        self.c6 = t.empty((M_PREFILL, HIDDEN // 4 * 3), dtype=t.uint8, device=dev)  # INT4 values as e2m3 fields
+        self.s6 = t.empty(M_PREFILL, dtype=t.float32, device=dev)
         self.cf = t.empty_like(self.c4)
         self.sf = t.empty_like(self.s4)
         self.y_11008 = t.empty((M_PREFILL, FFN), dtype=t.float32, device=dev)
@@ -311,18 +313,30 @@ class Bench:
         M, K = M_PREFILL, HIDDEN
 
         def prefill_int4():
+            bw.bw_quantize(self.x_pre, bw.BW_ACT_INT4_E2M3, self.c6, self.s6)
+            bw.bw_bitlinear_a4_grouped(self.c6, self.s6, bw.BW_ACT_INT4_E2M3,
+                                       [(self.wp_11008, self.b_11008), (self.wp_4096, self.b_4096)],
+                                       ys=[self.y_11008, self.y_4096])
+
+        def prefill_int4_nibbles():
             bw.bw_quantize(self.x_pre, bw.BW_ACT_INT4, self.c4, self.s4)
             bw.bw_bitlinear_a4_grouped(self.c4, self.s4, bw.BW_ACT_INT4,
                                        [(self.wp_11008, self.b_11008), (self.wp_4096, self.b_4096)],
                                        ys=[self.y_11008, self.y_4096])
 
         # the W1.58A4 prefill hot path as one stream sequence (one event pair around
-        # the quantizer and the two products, which share its codes and run as one
-        # grouped launch): the basis of `value`
+        # the INT4 quantizer and the two products, which share its codes and run as
+        # one grouped launch): the basis of `value`.  The INT4 values are stored as
+        # e2m3 fields and multiplied on the fp6 x fp4 matrix instruction (the same
+        # accumulators and y as the nibble path, bit for bit).
         R.append(("a0_prefill_int4_sequence", "TOPS", gemm_ops(M, FFN, K) + gemm_ops(M, HIDDEN, K), [prefill_int4]))
         # untimed: read more than the 256 MB Infinity Cache, so the rows below see the
         # prefill weights cold again, as a0 did
         R.append(("_evict_cache", None, 0, [self.evict_cache]))
+        # the same sequence with INT4 nibble codes on the int8 matrix instruction
+        R.append(("a0n_prefill_int4_nibbles_sequence", "TOPS", gemm_ops(M, FFN, K) + gemm_ops(M, HIDDEN, K),
+                  [prefill_int4_nibbles]))
+        R.append(("_evict_cache_0", None, 0, [self.evict_cache]))
 
         def prefill_b158():
             bw.bw_quantize_sparse_a8(self.x_pre, None, K, self.c8_pre, self.s8_pre)
@@ -335,6 +349,14 @@ class Bench:
         # baseline the pages compare against
         R.append(("b0_prefill_b158_int8_sequence", "TOPS", gemm_ops(M, FFN, K) + gemm_ops(M, HIDDEN, K), [prefill_b158]))
         R.append(("_evict_cache_2", None, 0, [self.evict_cache]))
+        R.append(("a1e_quantize_int4_e2m3", "GB/s", M * K * 2 + M * K * 3 / 4 + 4 * M,
+                  [lambda: bw.bw_quantize(self.x_pre, bw.BW_ACT_INT4_E2M3, self.c6, self.s6)]))
+        R.append(("a4e_gemm_int4_e2m3_n11008", "TOPS", gemm_ops(M, FFN, K),
+                  [lambda: bw.bw_bitlinear_a4(self.c6, self.s6, bw.BW_ACT_INT4_E2M3, self.wp_11008, self.b_11008,
+                                              self.y_11008)]))
+        R.append(("a4e_gemm_int4_e2m3_n4096", "TOPS", gemm_ops(M, HIDDEN, K),
+                  [lambda: bw.bw_bitlinear_a4(self.c6, self.s6, bw.BW_ACT_INT4_E2M3, self.wp_4096, self.b_4096,
+                                              self.y_4096)]))
         R.append(("a1_quantize_int4", "GB/s", M * K * 2 + M * K / 2 + 4 * M,
                   [lambda: bw.bw_quantize(self.x_pre, bw.BW_ACT_INT4, self.c4, self.s4)]))
         R.append(("a4_gemm_int4_n11008", "TOPS", gemm_ops(M, FFN, K),
@@ -657,7 +679,8 @@ def main():
         row_ms = [evs[s_][2 * i].elapsed_time(evs[s_][2 * i + 1]) for s_ in range(args.steps)]
         avg_ms = float(np.mean(row_ms)) / len(fns)
         rate = amount / (avg_ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
-        peak = HBM_PEAK_GBS if unit == "GB/s" else (FP4_PEAK_TOPS if "fp4" in name else INT8_PEAK_TOPS)
+        peak = HBM_PEAK_GBS if unit == "GB/s" else (
+            FP4_PEAK_TOPS if ("fp4" in name or "e2m3" in name or name.startswith("a0_")) else INT8_PEAK_TOPS)
         table[name] = {"avg_us": round(avg_ms * 1e3, 3), "launches_per_step": len(fns), "rate": round(rate, 2),
                        "unit": unit, "frac_of_peak": round(rate / peak, 4), "amount_per_launch": amount,
                        # spread over the timed steps (per launch), to show steps that ran slow
@@ -668,12 +691,15 @@ def main():
         return sum(table[n]["avg_us"] * table[n]["launches_per_step"] for n in names) / 1e3
 
     prefill_ops = 2.0 * M_PREFILL * HIDDEN * (FFN + HIDDEN)
-    prefill_rows = ("a1_quantize_int4", "a4_gemm_int4_n11008", "a4_gemm_int4_n4096")
+    prefill_rows = ("a1e_quantize_int4_e2m3", "a4e_gemm_int4_e2m3_n11008", "a4e_gemm_int4_e2m3_n4096")
     value = value_rows = None
     if "a0_prefill_int4_sequence" in table:
         value = round(prefill_ops / (row_ms(("a0_prefill_int4_sequence",)) * 1e-3) / 1e12, 2)
     if all(n in table for n in prefill_rows):
         value_rows = round(prefill_ops / (row_ms(prefill_rows) * 1e-3) / 1e12, 2)
+    nibbles = None
+    if "a0n_prefill_int4_nibbles_sequence" in table:
+        nibbles = round(prefill_ops / (row_ms(("a0n_prefill_int4_nibbles_sequence",)) * 1e-3) / 1e12, 2)
     b158 = None
     if "b0_prefill_b158_int8_sequence" in table:
         b158 = round(prefill_ops / (row_ms(("b0_prefill_b158_int8_sequence",)) * 1e-3) / 1e12, 2)
@@ -730,15 +756,22 @@ def main():
                 "tiled_us": table[rt]["avg_us"], "gather_us": table[rg]["avg_us"],
                 "tiled_over_gather_time": round(table[rt]["avg_us"] / table[rg]["avg_us"], 3)}
     roof = None
-    if "a4_gemm_int4_n11008" in table:
-        dom = table["a4_gemm_int4_n11008"]
+    if "a4e_gemm_int4_e2m3_n11008" in table:
+        dom = table["a4e_gemm_int4_e2m3_n11008"]
         roof = {
-            "bound": "mfma", "kernel": "k_gemm_lds256<INT4> (W1.58A4 GEMM, M=2048 K=4096 N=11008)",
-            "achieved": dom["rate"], "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
-            "frac": round(dom["rate"] / INT8_PEAK_TOPS, 4), "traffic": gemm_traffic_bytes(),
-            "note": "int8 MFMA int-ops (2*M*N*K per launch) / average launch duration from HIP events; "
-                    "traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE (copy-calibrated)",
+            "bound": "mfma", "kernel": "k_gemm_lds256<E2M3> (W1.58A4 GEMM, INT4 values as e2m3 fields, "
+                                       "M=2048 K=4096 N=11008)",
+            "achieved": dom["rate"], "peak": FP4_PEAK_TOPS, "unit": "TFLOP/s",
+            "frac": round(dom["rate"] / FP4_PEAK_TOPS, 4), "traffic": gemm_traffic_bytes(),
+            "note": "ops (2*M*N*K per launch) on the fp6 x fp4 MFMA (dense peak 10.1 POPS) / average launch "
+                    "duration from HIP events; traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE "
+                    "(copy-calibrated)",
         }
+        if "a4_gemm_int4_n11008" in table:
+            nb = table["a4_gemm_int4_n11008"]
+            roof["int4_nibble_path"] = {
+                "kernel": "k_gemm_lds256<INT4> (same product, INT4 nibbles widened to int8)", "avg_us": nb["avg_us"],
+                "achieved": nb["rate"], "peak": INT8_PEAK_TOPS, "frac": nb["frac_of_peak"]}
     out = {
         "metric": "BitLinear W1.58A4 prefill TOPS + decode GEMV HBM GB/s at 7B shapes, 1 GPU",
         "value": value,
@@ -751,7 +784,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4xternary->int32 (prefill); e2m1 fp4, int8 on the other rows",
+        "dtype": "int4 (as e2m3 fp6 fields) x ternary (as e2m1) -> exact fp32 sums (prefill); e2m1 fp4, int8 on "
+                 "the other rows",
         "data": "synthetic (seeded N(0,1)/Student-t activations, N(0,0.02) weights; 7B Llama-like shapes)",
         "config": {"workload": "a4.8 BitLinear hot path at 7B shapes: prefill M=2048 K=4096 N=11008/4096 "
                                "(INT4+FP4), sparse A8 down/out_proj M=2048, decode GEMV M=1,2,4,8 over 32 layers "
@@ -760,10 +794,14 @@ def main():
                                "the 3-bit cache 8x4096x32x128 and one decoder layer for 8 sequences x 4096 cached "
                                "positions", "global_batch": M_PREFILL, "seq_len": KV_SHAPE[1],
                    "parallelism": "none (1 GPU)"},
-        "value_basis": "2*2048*4096*(11008+4096) int ops / time of the INT4 quantizer + the W1.58A4 products "
-                       "N=11008 and N=4096 over its codes (one grouped launch), back to back as one stream "
-                       "sequence (row a0)",
+        "value_basis": "2*2048*4096*(11008+4096) ops / time of the INT4 quantizer (values stored as e2m3 fields) "
+                       "+ the W1.58A4 products N=11008 and N=4096 over its codes (one grouped launch on the fp6 x "
+                       "fp4 MFMA; accumulators and y equal to the INT4 nibble path bit for bit), back to back as "
+                       "one stream sequence (row a0)",
         "value_from_separate_rows": value_rows,
+        "int4_nibble_sequence": None if nibbles is None else {
+            "value": nibbles, "unit": "TOPS",
+            "basis": "the same sequence with INT4 nibble codes widened to int8 for the int8 MFMA (row a0n)"},
         "b158_baseline": None if b158 is None else {
             "value": b158, "unit": "TOPS",
             "basis": "same ops / time of INT8 absmax (all entries, no top-k) + the two W1.58A8 products over its "

@@ -62,8 +62,10 @@ typedef enum {
 typedef enum { BW_F32 = 0, BW_BF16 = 1 } bw_dtype;
 
 typedef enum {
-  BW_ACT_INT4 = 0,     /* two's-complement 4-bit integers, absmax scale a'/7 */
-  BW_ACT_FP4_E2M1 = 1  /* e2m1 floats (magnitudes 0,.5,1,1.5,2,3,4,6), scale a'/6 */
+  BW_ACT_INT4 = 0,      /* two's-complement 4-bit integers, absmax scale a'/7 */
+  BW_ACT_FP4_E2M1 = 1,  /* e2m1 floats (magnitudes 0,.5,1,1.5,2,3,4,6), scale a'/6 */
+  BW_ACT_INT4_E2M3 = 2  /* the values and scales of BW_ACT_INT4, each value stored as a
+                           6-bit e2m3 field (the operand of the fp6 matrix cores) */
 } bw_act4_fmt;
 
 /* Which activations a packed weight meets; selects the within-word order of
@@ -129,6 +131,13 @@ bw_status bw_pack_ternary(const void* W, bw_dtype w_dtype, int64_t N, int64_t K,
  *                    nearest e2m1 magnitude (ties to the even code, saturate
  *                    at 6), sign bit copied from t.
  * codes[M][K/2] (uint8): two codes per byte, even k in the low nibble.
+ * BW_ACT_INT4_E2M3: the same q and s as BW_ACT_INT4; codes[M][3K/4] (uint8)
+ *   hold per value the field f = (q < 0) << 5 | |q| (e2m3: sign bit, 2-bit
+ *   exponent, 3-bit mantissa with bias 1, so f reads as q/8 exactly for
+ *   |q| <= 15).  Per 64 values (48 bytes): let S0, S1 be the 24-byte
+ *   little-endian bit streams of the fields of values 0..31 and 32..63
+ *   (value j at bits 6j..6j+5); the bytes are S0[0:16], S1[0:16], S0[16:24],
+ *   S1[16:24].
  * scales[M] (fp32): s.
  * Shapes: K % 64 == 0, K <= 131072.  x dtype BW_F32 or BW_BF16.
  * ------------------------------------------------------------------------ */
@@ -145,8 +154,11 @@ bw_status bw_quantize(const void* x, bw_dtype x_dtype, int64_t M, int64_t K, bw_
  *   y[m][n]   = fl( fl(acc * x_scales[m]) * beta[n] )
  * codes/x_scales: as written by bw_quantize with the same fmt.  w_packed:
  * BW_ROLE_A4 layout of t[N][K].  y: fp32 [M][N] row-major.
- * acc_dbg: NULL, or [M][N] receiving acc (int32 for BW_ACT_INT4, fp32 for
- * BW_ACT_FP4_E2M1), for exactness checks.
+ * acc_dbg: NULL, or [M][N] receiving acc (int32 for BW_ACT_INT4 and
+ * BW_ACT_INT4_E2M3, fp32 for BW_ACT_FP4_E2M1), for exactness checks.
+ * BW_ACT_INT4_E2M3 gives the same acc and y as BW_ACT_INT4 on the same
+ * values (bit for bit) from the fp6 x fp4 matrix instruction, at any M; it
+ * returns BW_ERR_UNSUPPORTED when M*3K/4 or N*K/4 reaches 2^31 bytes.
  * Shapes: K % 64 == 0, K <= 131072, N % 16 == 0.
  * ------------------------------------------------------------------------ */
 bw_status bw_bitlinear_a4(const uint8_t* codes, const float* x_scales, int64_t M, int64_t K,
@@ -179,10 +191,11 @@ bw_status bw_bitlinear_a4_grouped(const uint8_t* codes, const float* x_scales, i
  * Source: as bw_quantize and bw_bitlinear_a4 (BitNet a4.8 abstract: 4-bit
  * activations for the attention and FFN inputs, INT4/FP4 kernels).
  * Computes exactly bw_quantize(x) followed by bw_bitlinear_a4 on its codes:
- * writes codes[M][K/2] and scales[M] (bw_quantize's bytes) and y[M][N]
- * (bw_bitlinear_a4's values).  For one or two tokens (M <= 2, K <= 8192) it
- * is one launch in which every workgroup quantizes the tokens itself;
- * otherwise the two launches of the separate calls.
+ * writes codes and scales[M] (bw_quantize's bytes) and y[M][N]
+ * (bw_bitlinear_a4's values).  For one or two tokens (M <= 2, K <= 8192) and
+ * BW_ACT_INT4 or BW_ACT_FP4_E2M1 it is one launch in which every workgroup
+ * quantizes the tokens itself; otherwise the two launches of the separate
+ * calls.
  * acc_dbg: as bw_bitlinear_a4.
  * Shapes: K % 64 == 0, K <= 131072, N % 16 == 0.  x dtype BW_F32 or BW_BF16.
  * ------------------------------------------------------------------------ */

@@ -14,11 +14,11 @@ import os
 import torch
 
 __all__ = [
-    "BW_OK", "BW_F32", "BW_BF16", "BW_ACT_INT4", "BW_ACT_FP4_E2M1", "BW_ROLE_A4", "BW_ROLE_A8",
+    "BW_OK", "BW_F32", "BW_BF16", "BW_ACT_INT4", "BW_ACT_FP4_E2M1", "BW_ACT_INT4_E2M3", "BW_ROLE_A4", "BW_ROLE_A8",
     "BW_ROLE_A8_KMAJOR", "bw_bitlinear_sparse_a8_gather_workspace_bytes", "bw_bitlinear_sparse_a8_gather",
     "BwError", "lib_path", "bw_abi_version", "bw_pack_layout_version", "bw_last_error",
     "bw_ternary_packed_bytes", "bw_pack_ternary_workspace_bytes", "bw_pack_ternary", "bw_quantize",
-    "bw_bitlinear_a4", "bw_quantize_bitlinear_a4", "bw_quantize_sparse_a8", "bw_bitlinear_sparse_a8", "bw_kv_pack3", "bw_kv_unpack3",
+    "bw_bitlinear_a4", "code_bytes", "bw_quantize_bitlinear_a4", "bw_quantize_sparse_a8", "bw_bitlinear_sparse_a8", "bw_kv_pack3", "bw_kv_unpack3",
     "bw_attn_decode_kv3_workspace_bytes", "bw_attn_decode_kv3", "bw_block_decode_workspace_bytes",
     "bw_block_decode", "bw_block_decode_noalloc_max_bytes", "bw_block_decode_noalloc", "bw_stream_read",
 ]
@@ -29,7 +29,7 @@ STATUS_NAMES = {
     5: "BW_ERR_ARG", 6: "BW_ERR_HIP", 7: "BW_ERR_UNSUPPORTED",
 }
 BW_F32, BW_BF16 = 0, 1
-BW_ACT_INT4, BW_ACT_FP4_E2M1 = 0, 1
+BW_ACT_INT4, BW_ACT_FP4_E2M1, BW_ACT_INT4_E2M3 = 0, 1, 2
 BW_ROLE_A4, BW_ROLE_A8, BW_ROLE_A8_KMAJOR = 0, 1, 2
 
 lib_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbw.so")
@@ -160,16 +160,30 @@ def bw_pack_ternary(W: torch.Tensor, role: int, w_packed=None, beta=None, worksp
     return w_packed, beta
 
 
+def code_bytes(K: int, fmt: int) -> int:
+    """Bytes of one token's 4-bit codes: K/2 (nibbles), 3K/4 (BW_ACT_INT4_E2M3 fields)."""
+    return K // 4 * 3 if fmt == BW_ACT_INT4_E2M3 else K // 2
+
+
+def _k_of_codes(row_bytes: int, fmt: int) -> int:
+    return row_bytes // 3 * 4 if fmt == BW_ACT_INT4_E2M3 else 2 * row_bytes
+
+
+def _acc_dtype(fmt: int):
+    return (torch.float32,) if fmt == BW_ACT_FP4_E2M1 else (torch.int32,)
+
+
 def bw_quantize(x: torch.Tensor, fmt: int, codes=None, scales=None):
-    """Per-token 4-bit quantizer; returns (codes uint8 [M][K/2], scales fp32 [M])."""
+    """Per-token 4-bit quantizer; returns (codes uint8 [M][code_bytes(K, fmt)], scales fp32 [M])."""
     M, K = x.shape
+    cb = code_bytes(K, fmt)
     if codes is None:
-        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+        codes = torch.empty((M, cb), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty(M, dtype=torch.float32, device=x.device)
     _check(_lib.bw_quantize(
         _dev(x, "x", _FLOATS), _fdtype(x), M, K, fmt,
-        _dev(codes, "codes", (torch.uint8,), (M, K // 2)),
+        _dev(codes, "codes", (torch.uint8,), (M, cb)),
         _dev(scales, "scales", (torch.float32,), (M,)), _stream(x)))
     return codes, scales
 
@@ -178,11 +192,11 @@ def bw_bitlinear_a4(codes: torch.Tensor, x_scales: torch.Tensor, fmt: int, w_pac
                     beta: torch.Tensor, y=None, acc_dbg=None):
     """y [M][N] fp32 = ternary(W) applied to 4-bit activations (codes from bw_quantize)."""
     M, Kh = codes.shape
-    K = 2 * Kh
+    K = _k_of_codes(Kh, fmt)
     N = beta.shape[0]
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=codes.device)
-    acc_dt = (torch.int32,) if fmt == BW_ACT_INT4 else (torch.float32,)
+    acc_dt = _acc_dtype(fmt)
     _check(_lib.bw_bitlinear_a4(
         _dev(codes, "codes", (torch.uint8,)), _dev(x_scales, "x_scales", (torch.float32,), (M,)), M, K, fmt,
         _dev(w_packed, "w_packed", (torch.uint8,), (N * K // 4,)),
@@ -217,8 +231,8 @@ def bw_bitlinear_a4_grouped(codes: torch.Tensor, x_scales: torch.Tensor, fmt: in
     """bw_bitlinear_a4 for each (w_packed, beta) of `weights` over the same codes, in one launch
     at prefill sizes; returns the list of y [M][N_g]."""
     M, Kh = codes.shape
-    K = 2 * Kh
-    acc_dt = (torch.int32,) if fmt == BW_ACT_INT4 else (torch.float32,)
+    K = _k_of_codes(Kh, fmt)
+    acc_dt = _acc_dtype(fmt)
     n, w_arr, b_arr, n_arr, y_arr, a_arr, ys = _grouped_args(weights, M, K, ys, accs, acc_dt)
     _check(_lib.bw_bitlinear_a4_grouped(
         _dev(codes, "codes", (torch.uint8,)), _dev(x_scales, "x_scales", (torch.float32,), (M,)), M, K, fmt, n,
@@ -229,21 +243,22 @@ def bw_bitlinear_a4_grouped(codes: torch.Tensor, x_scales: torch.Tensor, fmt: in
 def bw_quantize_bitlinear_a4(x: torch.Tensor, fmt: int, w_packed: torch.Tensor, beta: torch.Tensor, y=None,
                              codes=None, scales=None, acc_dbg=None):
     """bw_quantize followed by bw_bitlinear_a4 in one call (one launch for M <= 2);
-    returns (y fp32 [M][N], codes uint8 [M][K/2], scales fp32 [M])."""
+    returns (y fp32 [M][N], codes uint8 [M][code_bytes(K, fmt)], scales fp32 [M])."""
     M, K = x.shape
     N = beta.shape[0]
     dev = x.device
+    cb = code_bytes(K, fmt)
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
     if codes is None:
-        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        codes = torch.empty((M, cb), dtype=torch.uint8, device=dev)
     if scales is None:
         scales = torch.empty(M, dtype=torch.float32, device=dev)
-    acc_dt = (torch.int32,) if fmt == BW_ACT_INT4 else (torch.float32,)
+    acc_dt = _acc_dtype(fmt)
     _check(_lib.bw_quantize_bitlinear_a4(
         _dev(x, "x", _FLOATS), _fdtype(x), M, K, fmt,
         _dev(w_packed, "w_packed", (torch.uint8,), (N * K // 4,)), _dev(beta, "beta", (torch.float32,), (N,)), N,
-        _dev(codes, "codes", (torch.uint8,), (M, K // 2)), _dev(scales, "scales", (torch.float32,), (M,)),
+        _dev(codes, "codes", (torch.uint8,), (M, cb)), _dev(scales, "scales", (torch.float32,), (M,)),
         _dev(y, "y", (torch.float32,), (M, N)), _opt(acc_dbg, "acc_dbg", acc_dt, (M, N)), _stream(x)))
     return y, codes, scales
 

@@ -39,6 +39,11 @@ bw_status hip_status(hipError_t e, const char* where) {
 constexpr int64_t kMaxK = 131072;
 constexpr int64_t kMaxKSparse = 16384;
 
+bool valid_fmt(bw_act4_fmt f) { return f == BW_ACT_INT4 || f == BW_ACT_FP4_E2M1 || f == BW_ACT_INT4_E2M3; }
+
+// Kernel mode of a 4-bit format: 0 = INT4 nibbles, 1 = e2m1, 3 = INT4 as e2m3 fields.
+int mode_of(bw_act4_fmt f) { return f == BW_ACT_INT4 ? 0 : f == BW_ACT_FP4_E2M1 ? 1 : 3; }
+
 }  // namespace
 
 extern "C" {
@@ -80,7 +85,7 @@ bw_status bw_pack_ternary(const void* W, bw_dtype w_dtype, int64_t N, int64_t K,
 bw_status bw_quantize(const void* x, bw_dtype x_dtype, int64_t M, int64_t K, bw_act4_fmt fmt, uint8_t* codes,
                       float* scales, void* stream) {
   BW_REQUIRE(x_dtype == BW_F32 || x_dtype == BW_BF16, BW_ERR_DTYPE, "bw_quantize: bad dtype %d", (int)x_dtype);
-  BW_REQUIRE(fmt == BW_ACT_INT4 || fmt == BW_ACT_FP4_E2M1, BW_ERR_DTYPE, "bw_quantize: bad format %d", (int)fmt);
+  BW_REQUIRE(valid_fmt(fmt), BW_ERR_DTYPE, "bw_quantize: bad format %d", (int)fmt);
   BW_REQUIRE(M >= 0 && K >= 64 && K % 64 == 0 && K <= kMaxK, BW_ERR_SHAPE,
              "bw_quantize: need M >= 0, K %% 64 == 0, 64 <= K <= %lld (M=%lld K=%lld)", (long long)kMaxK,
              (long long)M, (long long)K);
@@ -106,14 +111,31 @@ static bw_status check_gemm(const char* who, const void* codes, const float* sx,
   return ok();
 }
 
+// e2m3 fields are read by the LDS GEMM only (any M); it must take the shape.
+static bw_status check_e2m3(const char* who, int64_t M, int64_t K, int64_t N) {
+  BW_REQUIRE(bw::gemm_lds_supported(3, M, K, N), BW_ERR_UNSUPPORTED,
+             "%s: BW_ACT_INT4_E2M3 needs M*3K/4 and N*K/4 below 2^31 bytes (M=%lld K=%lld N=%lld)", who,
+             (long long)M, (long long)K, (long long)N);
+  return ok();
+}
+
+// One product: e2m3 fields go to the LDS GEMM, the other formats through the
+// GEMV / GEMM dispatch.
+static hipError_t launch_a4(int mode, const void* codes, const float* sx, int64_t M, int64_t K, const uint8_t* w,
+                            const float* beta, int64_t N, float* y, void* acc, hipStream_t s) {
+  if (mode == 3) return bw::launch_gemm_lds(mode, codes, sx, M, K, w, beta, N, y, acc, s);
+  return bw::launch_bitlinear(mode, codes, sx, M, K, w, beta, N, y, acc, s);
+}
+
 bw_status bw_bitlinear_a4(const uint8_t* codes, const float* x_scales, int64_t M, int64_t K, bw_act4_fmt fmt,
                           const uint8_t* w_packed, const float* beta, int64_t N, float* y, void* acc_dbg,
                           void* stream) {
-  BW_REQUIRE(fmt == BW_ACT_INT4 || fmt == BW_ACT_FP4_E2M1, BW_ERR_DTYPE, "bw_bitlinear_a4: bad format %d", (int)fmt);
+  BW_REQUIRE(valid_fmt(fmt), BW_ERR_DTYPE, "bw_bitlinear_a4: bad format %d", (int)fmt);
   bw_status st = check_gemm("bw_bitlinear_a4", codes, x_scales, M, K, w_packed, beta, N, y, acc_dbg);
   if (st != BW_OK || M == 0) return st;
-  return hip_status(bw::launch_bitlinear(fmt == BW_ACT_INT4 ? 0 : 1, codes, x_scales, M, K, w_packed, beta, N, y,
-                                         acc_dbg, static_cast<hipStream_t>(stream)),
+  if (fmt == BW_ACT_INT4_E2M3 && (st = check_e2m3("bw_bitlinear_a4", M, K, N)) != BW_OK) return st;
+  return hip_status(launch_a4(mode_of(fmt), codes, x_scales, M, K, w_packed, beta, N, y, acc_dbg,
+                              static_cast<hipStream_t>(stream)),
                     "bw_bitlinear_a4");
 }
 
@@ -130,7 +152,16 @@ static bw_status bitlinear_grouped(const char* who, int mode, const void* codes,
     if (st != BW_OK) return st;
   }
   if (M == 0) return ok();
-  bool grouped = M > bw::kGemvMaxM;
+  if (mode == 3) {
+    int64_t tiles = 0;
+    for (int g = 0; g < n; ++g) {
+      bw_status st = check_e2m3(who, M, K, N[g]);
+      if (st != BW_OK) return st;
+      tiles += bw::gemm_lds_tiles(M, N[g]);
+    }
+    BW_REQUIRE(tiles < (int64_t{1} << 31), BW_ERR_UNSUPPORTED, "%s: %lld tiles in one launch", who, (long long)tiles);
+  }
+  bool grouped = M > bw::kGemvMaxM || mode == 3;
   int64_t tiles = 0;
   for (int g = 0; g < n && grouped; ++g) {
     grouped = bw::gemm_lds_supported(mode, M, K, N[g]);
@@ -161,10 +192,9 @@ bw_status bw_bitlinear_a4_grouped(const uint8_t* codes, const float* x_scales, i
                                   bw_act4_fmt fmt, int n_groups, const uint8_t* const* w_packed,
                                   const float* const* beta, const int64_t* N, float* const* y,
                                   void* const* acc_dbg, void* stream) {
-  BW_REQUIRE(fmt == BW_ACT_INT4 || fmt == BW_ACT_FP4_E2M1, BW_ERR_DTYPE, "bw_bitlinear_a4_grouped: bad format %d",
-             (int)fmt);
-  return bitlinear_grouped("bw_bitlinear_a4_grouped", fmt == BW_ACT_INT4 ? 0 : 1, codes, x_scales, M, K, n_groups,
-                           w_packed, beta, N, y, acc_dbg, static_cast<hipStream_t>(stream));
+  BW_REQUIRE(valid_fmt(fmt), BW_ERR_DTYPE, "bw_bitlinear_a4_grouped: bad format %d", (int)fmt);
+  return bitlinear_grouped("bw_bitlinear_a4_grouped", mode_of(fmt), codes, x_scales, M, K, n_groups, w_packed, beta,
+                           N, y, acc_dbg, static_cast<hipStream_t>(stream));
 }
 
 bw_status bw_quantize_bitlinear_a4(const void* x, bw_dtype x_dtype, int64_t M, int64_t K, bw_act4_fmt fmt,
@@ -172,23 +202,23 @@ bw_status bw_quantize_bitlinear_a4(const void* x, bw_dtype x_dtype, int64_t M, i
                                    float* scales, float* y, void* acc_dbg, void* stream) {
   BW_REQUIRE(x_dtype == BW_F32 || x_dtype == BW_BF16, BW_ERR_DTYPE, "bw_quantize_bitlinear_a4: bad dtype %d",
              (int)x_dtype);
-  BW_REQUIRE(fmt == BW_ACT_INT4 || fmt == BW_ACT_FP4_E2M1, BW_ERR_DTYPE, "bw_quantize_bitlinear_a4: bad format %d",
-             (int)fmt);
+  BW_REQUIRE(valid_fmt(fmt), BW_ERR_DTYPE, "bw_quantize_bitlinear_a4: bad format %d", (int)fmt);
   bw_status st = check_gemm("bw_quantize_bitlinear_a4", codes, scales, M, K, w_packed, beta, N, y, acc_dbg);
   if (st != BW_OK || M == 0) return st;
+  if (fmt == BW_ACT_INT4_E2M3 && (st = check_e2m3("bw_quantize_bitlinear_a4", M, K, N)) != BW_OK) return st;
   BW_REQUIRE(x, BW_ERR_NULL, "bw_quantize_bitlinear_a4: NULL pointer");
   BW_REQUIRE(!misaligned(x), BW_ERR_ALIGN, "bw_quantize_bitlinear_a4: device pointers must be 16-byte aligned");
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = x_dtype == BW_BF16;
-  const int f = fmt == BW_ACT_INT4 ? 0 : 1;
-  if (bw::gemv_quant_supported(M, K)) {
+  const int f = static_cast<int>(fmt);  // quantizer format
+  if (fmt != BW_ACT_INT4_E2M3 && bw::gemv_quant_supported(M, K)) {
     return hip_status(bw::launch_gemv_quant(x, bf16, f, M, K, w_packed, beta, N, y, codes, scales, acc_dbg, nullptr,
                                             N, s),
                       "bw_quantize_bitlinear_a4");
   }
   st = hip_status(bw::launch_quantize_act4(x, bf16, M, K, f, codes, scales, s), "bw_quantize_bitlinear_a4");
   if (st != BW_OK) return st;
-  return hip_status(bw::launch_bitlinear(f, codes, scales, M, K, w_packed, beta, N, y, acc_dbg, s),
+  return hip_status(launch_a4(mode_of(fmt), codes, scales, M, K, w_packed, beta, N, y, acc_dbg, s),
                     "bw_quantize_bitlinear_a4");
 }
 

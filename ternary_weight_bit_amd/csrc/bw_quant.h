@@ -1,5 +1,6 @@
 // 4-bit activation codes shared by the standalone quantizer and the fused
-// quantize + GEMV kernel, so both produce the same bytes.
+// quantize + GEMV kernel, so both produce the same bytes.  INT4 values can also
+// be stored as e2m3 (fp6) fields, the operand of the f8f6f4 matrix instruction.
 //
 // BitNet a4.8 abstract: 4-bit activations (INT4/FP4) at the inputs of attention
 // and FFN; toshoseti review «Метод»: FP4 as the wider-range alternative.
@@ -29,16 +30,25 @@ __device__ __forceinline__ uint32_t e2m1_code(float t) {
   return c | ((__float_as_uint(t) >> 31) << 3);
 }
 
-// FMT 0 = INT4, 1 = e2m1: the code of one element given inv = fl(qmax / a').
+// The INT4 value rne(t) of int4_code_absmax as a 6-bit e2m3 field: bit 5 the
+// sign (clear for 0), bits 4..0 the magnitude (e2m3 reads them as |q| / 8).
+__device__ __forceinline__ uint32_t e2m3_field_absmax(float t) {
+  const uint32_t mag = __float_as_uint(fabsf(t) + 12582912.0f) & 0xFu;
+  const uint32_t neg = (__float_as_uint(t) >> 31) & static_cast<uint32_t>(mag != 0u);
+  return mag | (neg << 5);
+}
+
+// FMT 0 = INT4, 1 = e2m1, 2 = INT4 as an e2m3 field: the code of one element
+// given inv = fl(qmax / a').
 template <int FMT>
 __device__ __forceinline__ uint32_t act4_code(float x, float inv) {
   const float t = mul_rn(x, inv);
-  return FMT == 0 ? int4_code_absmax(t) : e2m1_code(t);
+  return FMT == 0 ? int4_code_absmax(t) : FMT == 1 ? e2m1_code(t) : e2m3_field_absmax(t);
 }
 
 template <int FMT>
 constexpr float act4_qmax() {
-  return FMT == 0 ? 7.0f : 6.0f;
+  return FMT == 1 ? 6.0f : 7.0f;
 }
 
 }  // namespace bw

@@ -11,6 +11,11 @@
 //     code moved to bits 3..2 of a nibble: sign and high exponent bit), and the
 //     MFMA's block scale for the weight operand is 2^-1, so the products are
 //     exactly v * t.
+//   * INT4 values stored as e2m3 (fp6) fields are used as they are against the
+//     same e2m1 weights: a field holds sign and |q| as a 5-bit magnitude, which
+//     e2m3 reads as |q| / 8 (the subnormal and first normal binade are evenly
+//     spaced by 1/8); the activation operand's block scale 2^3 restores q, so
+//     the products are exactly q * t and the fp32 sums are exact integers.
 #pragma once
 
 #include "bw_device.h"
@@ -20,7 +25,7 @@ namespace bw {
 constexpr uint32_t kHiNib = 0xF0F0F0F0u;
 constexpr uint32_t kTopBits = 0xC0C0C0C0u;
 
-enum { MODE_INT4 = 0, MODE_FP4 = 1, MODE_INT8 = 2 };
+enum { MODE_INT4 = 0, MODE_FP4 = 1, MODE_INT8 = 2, MODE_E2M3 = 3 };
 
 // Right shift that turns an int8-MFMA accumulator back into sum q*t:
 // INT4 operands carry 16*q and 64*t (x1024), INT8 operands carry q and 64*t (x64).
@@ -91,6 +96,16 @@ __device__ __forceinline__ v8i fp4_operand(uint32_t a, uint32_t b, uint32_t c, u
   r[5] = 0;
   r[6] = 0;
   r[7] = 0;
+  return r;
+}
+
+// e2m3 operand: 32 fields of 6 bits (value j at bits 6j..6j+5 of the six
+// words), given as the first 16 and the last 8 bytes; upper words unused.
+constexpr int kE2m3ActScale = 130;  // E8M0 block scale 2^(130 - 127): field |q| / 8 -> q
+__device__ __forceinline__ v8i fp6_operand(uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t e,
+                                           uint32_t f) {
+  const v8i r = {static_cast<int>(a), static_cast<int>(b), static_cast<int>(c), static_cast<int>(d),
+                 static_cast<int>(e), static_cast<int>(f), 0, 0};
   return r;
 }
 

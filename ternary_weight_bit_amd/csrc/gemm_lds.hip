@@ -112,7 +112,7 @@ __device__ __forceinline__ void epilogue_staged(const AccT (&acc)[2][2], uint8_t
                                                 int64_t m0, int64_t n0, int64_t M, int64_t N, const float* sxs,
                                                 const float* __restrict__ beta, float* __restrict__ y,
                                                 void* __restrict__ acc_dbg) {
-  using stage_t = typename std::conditional<MODE == MODE_FP4, float4, int4>::type;
+  using stage_t = typename std::conditional<MODE == MODE_FP4 || MODE == MODE_E2M3, float4, int4>::type;
   constexpr int ROWB = WIDE ? 256 : 128;   // staged bytes per token
   constexpr int UNITS = ROWB / 16;         // 16-byte units per staged token
   constexpr int LPR = UNITS;               // lanes reading one token
@@ -160,6 +160,15 @@ __device__ __forceinline__ void epilogue_staged(const AccT (&acc)[2][2], uint8_t
         float o[4];
         if constexpr (MODE == MODE_FP4) {
           if (acc_dbg && gm < M && gn < N) *reinterpret_cast<float4*>(static_cast<float*>(acc_dbg) + gm * N + gn) = v;
+          o[0] = dequant(v.x, sm, bv[0]);
+          o[1] = dequant(v.y, sm, bv[1]);
+          o[2] = dequant(v.z, sm, bv[2]);
+          o[3] = dequant(v.w, sm, bv[3]);
+        } else if constexpr (MODE == MODE_E2M3) {
+          // exact integers in fp32: the int32 accumulator and the same y as the INT4 path
+          if (acc_dbg && gm < M && gn < N)
+            *reinterpret_cast<int4*>(static_cast<int32_t*>(acc_dbg) + gm * N + gn) =
+                make_int4(static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z), static_cast<int>(v.w));
           o[0] = dequant(v.x, sm, bv[0]);
           o[1] = dequant(v.y, sm, bv[1]);
           o[2] = dequant(v.z, sm, bv[2]);
@@ -364,16 +373,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
 }
 
 
-// 4-bit codes with K a multiple of 256: stages of 256 k in two LDS buffers.
+// 4-bit codes with K a multiple of 256, and INT4 values stored as e2m3 fields
+// (any K % 64 == 0): stages of 256 k in two LDS buffers.
 // The same prefetch window as the three-buffer ring of 128-k stages (stage
 // st + 1 loads while stage st computes) with half the workgroup barriers.
-// Activation rows hold 128 bytes per stage (eight 16-byte parts, swizzled by
-// row / 2); weights keep their packed order, four 64-k slabs per column group.
+// Nibble activation rows hold 128 bytes per stage (eight 16-byte parts,
+// swizzled by row / 2).  e2m3 rows hold 192 bytes per stage (twelve 16-byte
+// parts) and are stored by bands of 16 rows, part-major: part c of row r at
+// (r / 16) * 3072 + c * 256 + (r % 16) * 16, so one wave's copy is 16 rows x
+// four parts and the fragment reads of 16 rows are 16 bytes apart (no bank
+// conflict).  Weights keep their packed order, four 64-k slabs per column
+// group.
 // The copies into LDS are issued from inline asm (`lds_copy16`): the
 // compiler then adds no wait for them before the fragment reads, which with
 // two buffers would stall each stage on the loads just issued for the next;
 // the wait for a stage's own copies is explicit (vmcnt before the barrier).
 __device__ __forceinline__ int a_slot256(int row, int p) { return p ^ ((row >> 1) & 7); }
+
+constexpr int kGroupRows = 4;  // row tiles per block of the e2m3 tile order
 
 // 16 bytes per lane from a buffer resource into LDS at `lds` + 16 * lane.
 __device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, uint32_t voff, int soff) {
@@ -387,19 +404,43 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
+// Fragments of one 64-k block: weight words of two columns and the activation
+// bits of two rows (16 bytes of nibbles, or 24 bytes of e2m3 fields, each).
+template <bool E6>
+struct Frag256 {
+  uint2 w0, w1;
+  uint4 x0, x1;
+};
+template <>
+struct Frag256<true> {
+  uint2 w0, w1;
+  v8i a0, a1;  // the two rows' e2m3 operands
+};
+
 template <int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_gemm_lds256(
     const uint8_t* __restrict__ A, const float* __restrict__ sx, int64_t M, int64_t K, const GemmGroups G,
     int MT) {
   static_assert(MODE != MODE_INT8, "4-bit codes only");
-  constexpr int AROW = 128;           // bytes per activation row per stage (256 codes)
-  constexpr int AStage = BM * AROW;   // 16 KB
-  constexpr int BStage = BN * 64;     // 16 KB: [group 16][slab 4][column 16] x 16 B
+  constexpr bool E6 = MODE == MODE_E2M3;
+  constexpr int AROW = E6 ? 192 : 128;   // bytes per activation row per stage (256 values)
+  constexpr int AStage = BM * AROW;      // 24 KB / 16 KB
+  constexpr int ACOPIES = AStage / 8192; // 1 KB copies per wave per stage
+  constexpr int BStage = BN * 64;        // 16 KB: [group 16][slab 4][column 16] x 16 B
   __shared__ __attribute__((aligned(1024))) uint8_t A0[AStage];
   __shared__ __attribute__((aligned(1024))) uint8_t A1[AStage];
   __shared__ __attribute__((aligned(1024))) uint8_t B0[BStage];
   __shared__ __attribute__((aligned(1024))) uint8_t B1[BStage];
-  __shared__ float sxs[BM];
+  // Token scales: their own 512 bytes, except for e2m3 rows, whose buffers
+  // fill exactly half of the CU's LDS (two workgroups per CU); there the
+  // scales go to B1 after the main loop.
+  float* sxs;
+  if constexpr (E6) {
+    sxs = reinterpret_cast<float*>(B1);
+  } else {
+    __shared__ float sxs_own[BM];
+    sxs = sxs_own;
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -420,56 +461,105 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
   float* __restrict__ const y = pick(G.y, gi);
   void* __restrict__ const acc_dbg = pick(G.acc_dbg, gi);
   const int64_t N = pick(G.N, gi);
-  const int64_t m0 = static_cast<int64_t>(t % MT) * BM;
-  const int64_t n0 = static_cast<int64_t>(t / MT) * BN;
-  const int64_t kblocks = K >> 6;
-  const int64_t nst = K >> 8;
-  const int64_t a_row = K >> 1;
-
-  // A: copy j of wave w fills rows 8 (2w + j) .. + 7; lane i -> row + i / 8, LDS
-  // slot i % 8, which holds the row's part a_slot256(row, i % 8) (an involution).
-  const int64_t m_last = (M - 1 - m0 < BM - 1) ? M - 1 - m0 : BM - 1;
-  uint32_t aoff[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = 8 * (2 * wave + j) + lane / 8;
-    const int part = a_slot256(row, lane % 8);
-    aoff[j] = static_cast<uint32_t>((row < m_last ? row : m_last) * a_row + part * 16);
+  // Tile -> (row tile, column tile).  e2m3 rows: blocks of kGroupRows row
+  // tiles, column by column inside a block, so the tiles an XCD holds at once
+  // share both their rows and their columns (its slice of consecutive tiles
+  // is about kGroupRows rows by a few columns, not every row).
+  int mt = t % MT, nt = t / MT;
+  if constexpr (E6 && kGroupRows > 0) {
+    const int NT = static_cast<int>((N + BN - 1) / BN);
+    const int bm = t / (kGroupRows * NT);
+    const int rows = MT - bm * kGroupRows < kGroupRows ? MT - bm * kGroupRows : kGroupRows;
+    const int rem = t - bm * kGroupRows * NT;
+    mt = bm * kGroupRows + rem % rows;
+    nt = rem / rows;
   }
-  // B: copy j of wave w fills column group 2w + j, all four slabs: lane i ->
-  // slab i / 16, column i % 16.
+  const int64_t m0 = static_cast<int64_t>(mt) * BM;
+  const int64_t n0 = static_cast<int64_t>(nt) * BN;
+  const int64_t kblocks = K >> 6;
+  const int nst = static_cast<int>((K + 255) >> 8);
+  // 64-k blocks in the last stage (K % 256 != 0 happens for e2m3 rows only)
+  const int nb_last = (kblocks & 3) ? static_cast<int>(kblocks & 3) : 4;
+  const int64_t a_row = E6 ? (K >> 2) * 3 : (K >> 1);
+
+  // A copies.  Nibble rows: copy j of wave w fills rows 8 (2w + j) .. + 7;
+  // lane i -> row + i / 8, LDS slot i % 8, which holds the row's part
+  // a_slot256(row, i % 8) (an involution).  e2m3 rows: copy j of wave w fills
+  // parts 4j .. 4j + 3 of rows 16w .. 16w + 15 (lane i -> row 16w + i % 16,
+  // part 4j + i / 16): one lane offset, the copies 64 bytes apart.
+  const int64_t m_last = (M - 1 - m0 < BM - 1) ? M - 1 - m0 : BM - 1;
+  uint32_t aoff[E6 ? 1 : ACOPIES];
+  if constexpr (E6) {
+    const int row = 16 * wave + (lane & 15);
+    aoff[0] = static_cast<uint32_t>((row < m_last ? row : m_last) * a_row + (lane >> 4) * 16);
+  } else {
+#pragma unroll
+    for (int j = 0; j < ACOPIES; ++j) {
+      const int row = 8 * (2 * wave + j) + lane / 8;
+      const int part = a_slot256(row, lane % 8);
+      aoff[j] = static_cast<uint32_t>((row < m_last ? row : m_last) * a_row + part * 16);
+    }
+  }
+  // B: copy j of wave w fills column group 2w + j (wave-uniform), all four
+  // slabs: lane i -> slab i / 16, column i % 16.
   const int64_t ng = N >> 4;
   const int64_t g_first = n0 >> 4;
-  uint32_t boff[2];
+  const uint32_t boff = static_cast<uint32_t>((lane >> 4) * 256 + (lane & 15) * 16);
+  int bgrp[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int64_t g0 = 2 * wave + j;
     const int64_t gl = (g_first + g0 < ng) ? g0 : ng - 1 - g_first;
-    boff[j] = static_cast<uint32_t>((gl * kblocks + (lane >> 4)) * 256 + (lane & 15) * 16);
+    bgrp[j] = __builtin_amdgcn_readfirstlane(static_cast<int>(gl * kblocks * 256));
   }
   const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(A + m0 * a_row), 0, static_cast<int>((M - m0) * a_row), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t brsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(Wp + g_first * kblocks * 256), 0, static_cast<int>((ng - g_first) * kblocks * 256),
       kRsrcWord3);
-  const int64_t rot = ((t % MT) % 4) * (nst / 4);  // as in k_gemm_lds
-  // this wave's 2 KB of each stage buffer, as a wave-uniform (scalar) offset
-  const uint32_t wbase = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(2 * wave * 1024));
-  auto issue = [&](int64_t st_req, uint8_t* As, uint8_t* Bs) {
-    int64_t sp = st_req + rot;
-    if (sp >= nst) sp -= nst;
-    const int st = static_cast<int>(sp);
+  const int rot = (mt % 4) * (nst / 4);  // as in k_gemm_lds
+  auto stage_of = [&](int st) {
+    const int sp = st + rot;
+    return sp >= nst ? sp - nst : sp;
+  };
+  // this wave's part of each stage buffer, as wave-uniform (scalar) offsets
+  const uint32_t wbase_a = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(ACOPIES * wave * 1024));
+  const uint32_t wbase_b = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(2 * wave * 1024));
+  // The last stage of a K that is not a multiple of 256 (e2m3 rows) holds
+  // nb_last < 4 blocks: the copies of the parts and slabs past K read the
+  // stage's first part and slab instead, so no copy leaves the row or the
+  // column group (the copies are not range-checked against the scalar
+  // offset); the blocks they fill are skipped.
+  auto issue = [&](int st_req, uint8_t* As, uint8_t* Bs) {
+    const int st = stage_of(st_req);
     const int sa = st * AROW;
     const int sb = st * 1024;
-    const uint32_t la = lds_addr(As) + wbase;
-    const uint32_t lb = lds_addr(Bs) + wbase;
+    const uint32_t la = lds_addr(As) + wbase_a;
+    const uint32_t lb = lds_addr(Bs) + wbase_b;
+    if (E6 && nb_last < 4 && st == nst - 1) {
+      // derived here (once per workgroup), not kept in registers across the loop
+      uint32_t a0 = aoff[0], b0 = boff, q = static_cast<uint32_t>(lane >> 4);
+      asm volatile("" : "+v"(a0), "+v"(b0), "+v"(q));
 #pragma unroll
-    for (int j = 0; j < 2; ++j) lds_copy16(arsrc, la + 1024 * j, aoff[j], sa);
+      for (int j = 0; j < ACOPIES; ++j) {
+        const bool in_k = static_cast<int>(4 * j + q) < 3 * nb_last;
+        lds_copy16(arsrc, la + 1024 * j, in_k ? a0 + 64 * j : a0 - 16 * q, sa);
+      }
+      const uint32_t bo = static_cast<int>(q) < nb_last ? b0 : b0 - 256 * q;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) lds_copy16(brsrc, lb + 1024 * j, boff[j], sb);
+      for (int j = 0; j < 2; ++j) lds_copy16(brsrc, lb + 1024 * j, bo, bgrp[j] + sb);
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < ACOPIES; ++j) {
+      if constexpr (E6) lds_copy16(arsrc, la + 1024 * j, aoff[0], sa + 64 * j);
+      else lds_copy16(arsrc, la + 1024 * j, aoff[j], sa);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) lds_copy16(brsrc, lb + 1024 * j, boff, bgrp[j] + sb);
   };
 
-  using acc_t = typename std::conditional<MODE == MODE_FP4, v16f, v16i>::type;
+  using acc_t = typename std::conditional<MODE == MODE_INT4, v16i, v16f>::type;
   acc_t acc[2][2];
 #pragma unroll
   for (int r = 0; r < 2; ++r)
@@ -478,36 +568,67 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[r][c][e] = 0;
 
+  // e2m3 rows: the 48 bytes of 64-k block s are parts 3s, 3s+1, 3s+2 (the
+  // first 16 bytes of the fields of values 0..31, the same of values 32..63,
+  // then the last 8 of each): this lane's 24 bytes are 16 at e6_x and 8 at
+  // e6_y, plus 768 s; row + 32 is two bands further on.
+  int e6_x = 0, e6_y = 0;
+  if constexpr (E6) {
+    const int base = (wm * 4 + (li >> 4)) * 3072 + (li & 15) * 16;
+    e6_x = base + 256 * lh;
+    e6_y = base + 512 + 8 * lh;
+  }
+
   // Fragments of one 64-k block s of a stage: the weight words of columns
-  // wn*64 + li and + 32, and the activation parts of rows wm*64 + li and + 32.
-  struct Frag {
-    uint2 w0, w1;
-    uint4 x0, x1;
-  };
+  // wn*64 + li and + 32, and the activation bits of rows wm*64 + li and + 32.
+  using Frag = Frag256<E6>;
   auto load_frag = [&](const uint8_t* As, const uint8_t* Bs, int s) {
     Frag f;
     const int col = wn * 64 + li;
     int o0 = ((col >> 4) * 4 + s) * 256 + (col & 15) * 16 + 8 * lh;
     int o1 = o0 + 2048;
-    asm volatile("" : "+v"(o0), "+v"(o1));
+    if constexpr (!E6) asm volatile("" : "+v"(o0), "+v"(o1));
     f.w0 = *reinterpret_cast<const uint2*>(Bs + o0);
     f.w1 = *reinterpret_cast<const uint2*>(Bs + o1);
-    const int row0 = wm * 64 + li;
-    const int row1 = row0 + 32;
-    f.x0 = *reinterpret_cast<const uint4*>(As + row0 * AROW + 16 * a_slot256(row0, 2 * s + lh));
-    f.x1 = *reinterpret_cast<const uint4*>(As + row1 * AROW + 16 * a_slot256(row1, 2 * s + lh));
+    if constexpr (E6) {
+      const uint8_t* p = As + 768 * s;
+      const uint4 x0 = *reinterpret_cast<const uint4*>(p + e6_x);
+      const uint2 x0t = *reinterpret_cast<const uint2*>(p + e6_y);
+      const uint4 x1 = *reinterpret_cast<const uint4*>(p + e6_x + 6144);
+      const uint2 x1t = *reinterpret_cast<const uint2*>(p + e6_y + 6144);
+      f.a0 = fp6_operand(x0.x, x0.y, x0.z, x0.w, x0t.x, x0t.y);
+      f.a1 = fp6_operand(x1.x, x1.y, x1.z, x1.w, x1t.x, x1t.y);
+    } else {
+      const int row0 = wm * 64 + li;
+      const int row1 = row0 + 32;
+      f.x0 = *reinterpret_cast<const uint4*>(As + row0 * AROW + 16 * a_slot256(row0, 2 * s + lh));
+      f.x1 = *reinterpret_cast<const uint4*>(As + row1 * AROW + 16 * a_slot256(row1, 2 * s + lh));
+    }
     return f;
   };
   auto mma_frag = [&](const Frag& f) {
-    if constexpr (MODE == MODE_FP4) {
+    if constexpr (MODE == MODE_FP4 || MODE == MODE_E2M3) {
       const v8i b0 = fp4_weights(f.w0.x, f.w0.y);
       const v8i b1 = fp4_weights(f.w1.x, f.w1.y);
+      if constexpr (E6) {
+        const v8i a0 = f.a0;
+        const v8i a1 = f.a1;
+        acc[0][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b0, a0, acc[0][0], 4, 2, 0, kE2m1WeightScale, 0,
+                                                                    kE2m3ActScale);
+        acc[0][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b1, a0, acc[0][1], 4, 2, 0, kE2m1WeightScale, 0,
+                                                                    kE2m3ActScale);
+        acc[1][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b0, a1, acc[1][0], 4, 2, 0, kE2m1WeightScale, 0,
+                                                                    kE2m3ActScale);
+        acc[1][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b1, a1, acc[1][1], 4, 2, 0, kE2m1WeightScale, 0,
+                                                                    kE2m3ActScale);
+      } else {
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const uint4 x = r ? f.x1 : f.x0;
-        const v8i a = fp4_operand(x.x, x.y, x.z, x.w);
-        acc[r][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b0, a, acc[r][0], 4, 4, 0, kE2m1WeightScale, 0, 127);
-        acc[r][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b1, a, acc[r][1], 4, 4, 0, kE2m1WeightScale, 0, 127);
+        for (int r = 0; r < 2; ++r) {
+          const uint4 x = r ? f.x1 : f.x0;
+          const v8i a = fp4_operand(x.x, x.y, x.z, x.w);
+          acc[r][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b0, a, acc[r][0], 4, 4, 0, kE2m1WeightScale, 0, 127);
+          acc[r][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b1, a, acc[r][1], 4, 4, 0, kE2m1WeightScale, 0, 127);
+        }
       }
     } else {
       const v4i b00 = widen_w_a4(f.w0.x), b01 = widen_w_a4(f.w0.y);
@@ -527,42 +648,74 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
   // The four 64-k blocks of a stage, each block's LDS reads issued before the
   // previous block's products (the scheduling barriers keep that order; left to
   // itself the compiler sinks each read next to its first use, which exposes the
-  // LDS latency once per block).
-  auto compute = [&](const uint8_t* As, const uint8_t* Bs) {
-    Frag f = load_frag(As, Bs, 0);
+  // LDS latency once per block).  nb < 4 only in the last stage of a K that is
+  // not a multiple of 256: the blocks past K hold other rows' bytes and are
+  // skipped (wave-uniform branch).
+  auto compute = [&](const uint8_t* As, const uint8_t* Bs, int nb) {
+    if constexpr (E6) {
+      const Frag f0 = load_frag(As, Bs, 0);
+      const Frag f1 = load_frag(As, Bs, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_frag(f0);
+      __builtin_amdgcn_sched_barrier(0);
+      const Frag f2 = load_frag(As, Bs, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (nb > 1) mma_frag(f1);
+      __builtin_amdgcn_sched_barrier(0);
+      const Frag f3 = load_frag(As, Bs, 3);
+      __builtin_amdgcn_sched_barrier(0);
+      if (nb > 2) mma_frag(f2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (nb > 3) mma_frag(f3);
+    } else {
+      Frag f = load_frag(As, Bs, 0);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      Frag g;
-      if (s < 3) g = load_frag(As, Bs, s + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      mma_frag(f);
-      __builtin_amdgcn_sched_barrier(0);
-      f = g;
+      for (int s = 0; s < 4; ++s) {
+        Frag g;
+        if (s < 3) g = load_frag(As, Bs, s + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_frag(f);
+        __builtin_amdgcn_sched_barrier(0);
+        f = g;
+      }
     }
   };
 
-  if (tid < BM) sxs[tid] = sx[(m0 + tid < M) ? m0 + tid : M - 1];
+  if constexpr (!E6) {
+    if (tid < BM) sxs[tid] = sx[(m0 + tid < M) ? m0 + tid : M - 1];
+  }
 
   // Stage st: wait for this wave's copies of stage st (none other is in
   // flight), barrier (stage st is complete in LDS and everyone is done with
   // the other buffer), copy stage st + 1 into it, compute stage st.
   issue(0, A0, B0);
-  auto step = [&](int64_t st, uint8_t* Ac, uint8_t* Bc, uint8_t* An, uint8_t* Bn) {
+  auto step = [&](int st, uint8_t* Ac, uint8_t* Bc, uint8_t* An, uint8_t* Bn) {
     wait_vm<0>();
     block_barrier();
     if (st + 1 < nst) issue(st + 1, An, Bn);
-    compute(Ac, Bc);
+    int nb = 4;
+    if constexpr (E6) nb = stage_of(st) == nst - 1 ? nb_last : 4;
+    compute(Ac, Bc, nb);
   };
-  for (int64_t st = 0; st < nst; st += 2) {
+  for (int st = 0; st < nst; st += 2) {
     step(st, A0, B0, A1, B1);
     if (st + 1 < nst) step(st + 1, A1, B1, A0, B0);
   }
   wait_vm<0>();  // (every copy was waited for at its stage)
   __syncthreads();
 
-  // 8 KB of LDS per wave for the epilogue: waves 2i, 2i+1 take A0, A1, B0, B1.
+  // 8 KB of LDS per wave for the epilogue: nibble rows: waves 2i, 2i+1 take
+  // A0, A1, B0, B1; e2m3 rows: waves 0-2 take A0, 3-5 A1, 6-7 B0 (the scales
+  // are in B1).
   static_assert(AStage >= 16384 && BStage >= 16384, "epilogue staging regions");
-  uint8_t* const stage = (wave < 2 ? A0 : wave < 4 ? A1 : wave < 6 ? B0 : B1) + (wave & 1) * 8192;
+  uint8_t* stage;
+  if constexpr (E6) {
+    if (tid < BM) sxs[tid] = sx[(m0 + tid < M) ? m0 + tid : M - 1];
+    __syncthreads();
+    stage = (wave < 3 ? A0 + wave * 8192 : wave < 6 ? A1 + (wave - 3) * 8192 : B0 + (wave - 6) * 8192);
+  } else {
+    stage = (wave < 2 ? A0 : wave < 4 ? A1 : wave < 6 ? B0 : B1) + (wave & 1) * 8192;
+  }
   int lane_e = lane;
   asm volatile("" : "+v"(lane_e));  // derive the epilogue's indices here, not before the loop
   epilogue_staged<MODE, true>(acc, stage, lane_e, wm, wn, m0, n0, M, N, sxs, beta, y, acc_dbg);
@@ -573,9 +726,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
 int64_t gemm_lds_tiles(int64_t M, int64_t N) { return ((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
 
 bool gemm_lds_supported(int mode, int64_t M, int64_t K, int64_t N) {
-  const int64_t a_bytes = M * ((mode == 2) ? K : K / 2);
+  const int64_t a_bytes = M * (mode == MODE_INT8 ? K : mode == MODE_E2M3 ? K / 4 * 3 : K / 2);
   const int64_t w_bytes = N * K / 4;
-  return K % 128 == 0 && a_bytes < (int64_t{1} << 31) && w_bytes < (int64_t{1} << 31) &&
+  return K % (mode == MODE_E2M3 ? 64 : 128) == 0 && a_bytes < (int64_t{1} << 31) && w_bytes < (int64_t{1} << 31) &&
          gemm_lds_tiles(M, N) < (int64_t{1} << 30);
 }
 
@@ -610,6 +763,9 @@ hipError_t launch_gemm_lds_grouped(int mode, const void* codes, const float* sx,
         hipLaunchKernelGGL(k_gemm_lds256<MODE_FP4>, grid, block, 0, s, A, sx, M, K, G, MT);
       else
         hipLaunchKernelGGL(k_gemm_lds<MODE_FP4>, grid, block, 0, s, A, sx, M, K, G, MT);
+      break;
+    case MODE_E2M3:
+      hipLaunchKernelGGL(k_gemm_lds256<MODE_E2M3>, grid, block, 0, s, A, sx, M, K, G, MT);
       break;
     default:
       hipLaunchKernelGGL(k_gemm_lds<MODE_INT8>, grid, block, 0, s, A, sx, M, K, G, MT);

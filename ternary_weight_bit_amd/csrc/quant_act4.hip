@@ -1,4 +1,5 @@
-// Per-token 4-bit activation quantizer (INT4 absmax or e2m1 FP4) for gfx950.
+// Per-token 4-bit activation quantizer (INT4 absmax or e2m1 FP4) for gfx950;
+// INT4 values are stored as nibbles or as e2m3 fields.
 //
 // BitNet a4.8 abstract: 4-bit activations at the inputs of attention and FFN
 // (INT4/FP4 kernels).  toshoseti review «Метод»: the q/k/v/gate/up inputs are
@@ -30,6 +31,48 @@ __device__ __forceinline__ uint32_t encode8(const float (&v)[8], float inv) {
   return w;
 }
 
+// Eight INT4 values as e2m3 fields, value i at bits 6i..6i+5 of 48 bits.
+__device__ __forceinline__ uint64_t encode8_e2m3(const float (&v)[8], float inv) {
+  uint64_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w |= static_cast<uint64_t>(act4_code<2>(v[i], inv)) << (6 * i);
+  return w;
+}
+
+// Row bytes of K values: two codes per byte, or e2m3 fields (3 bytes per 4).
+template <int FMT>
+__device__ __forceinline__ int64_t code_row_bytes(int64_t K) {
+  return FMT == 2 ? (K >> 2) * 3 : (K >> 1);
+}
+
+// Store the codes of chunk ch (values 8ch .. 8ch+7) of a row.  Nibbles: one
+// word.  e2m3 fields: 64 values form a group of 48 bytes, the 24-byte bit
+// streams of values 0..31 (S0) and 32..63 (S1) stored as S0[0:16], S1[0:16],
+// S0[16:24], S1[16:24]; chunk j of a half covers bytes 6j .. 6j+5 of its
+// stream.  The even lane of each lane pair (chunks 2p, 2p+1 of a half) writes
+// their 12 bytes; every lane of the wave must call this (a lane exchange).
+template <int FMT>
+__device__ __forceinline__ void store_chunk(uint8_t* __restrict__ row, int64_t ch, bool valid,
+                                            const float (&v)[8], float inv) {
+  if constexpr (FMT != 2) {
+    if (valid) reinterpret_cast<uint32_t*>(row)[ch] = encode8<FMT>(v, inv);
+  } else {
+    const uint64_t e = encode8_e2m3(v, inv);
+    const uint32_t lo = static_cast<uint32_t>(e), hi = static_cast<uint32_t>(e >> 32);
+    const uint32_t plo = __shfl_xor(lo, 1), phi = __shfl_xor(hi, 1);
+    if (valid && (ch & 1) == 0) {
+      const uint32_t d0 = lo, d1 = hi | (plo << 16), d2 = (plo >> 16) | (phi << 16);
+      uint8_t* g = row + 48 * (ch >> 3) + 16 * ((ch >> 2) & 1);  // this half's first 16 bytes
+      if ((ch & 2) == 0) {  // stream bytes 0..11
+        *reinterpret_cast<uint3*>(g) = make_uint3(d0, d1, d2);
+      } else {              // stream bytes 12..23: the last word of the first 16, then the last 8
+        reinterpret_cast<uint32_t*>(g)[3] = d0;
+        *reinterpret_cast<uint2*>(row + 48 * (ch >> 3) + 32 + 8 * ((ch >> 2) & 1)) = make_uint2(d1, d2);
+      }
+    }
+  }
+}
+
 // One wave per row (rows longer than 8192): the row is read twice, once for
 // the maximum and once to encode (the second read hits L2).
 template <bool BF16, int FMT>
@@ -41,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_act4(const void* __restri
   if (m >= M) return;  // whole wave leaves together
   const int64_t nchunk = K >> 3;
   const int64_t row = m * K;
-  uint32_t* __restrict__ out = reinterpret_cast<uint32_t*>(codes + m * (K >> 1));
+  uint8_t* __restrict__ out = codes + m * code_row_bytes<FMT>(K);
   float amax = 0.0f;
   for (int64_t ch = lane; ch < nchunk; ch += kWave) {
     float t[8];
@@ -51,12 +94,13 @@ __global__ __launch_bounds__(kThreads) void k_quantize_act4(const void* __restri
   }
   amax = wave_max(amax);
   const float a = fmaxf(amax, 1e-5f);
-  const float qmax = (FMT == 0) ? 7.0f : 6.0f;
+  const float qmax = act4_qmax<FMT>();
   const float inv = div_rn(qmax, a);
+  // nchunk is a multiple of 8: the lanes of a pair leave the loop together
   for (int64_t ch = lane; ch < nchunk; ch += kWave) {
     float t[8];
     load8<BF16>(x, row + ch * 8, t);
-    out[ch] = encode8<FMT>(t, inv);
+    store_chunk<FMT>(out, ch, true, t, inv);
   }
   if (lane == 0) scales[m] = div_rn(a, qmax);
 }
@@ -114,13 +158,13 @@ __global__ __launch_bounds__(kThreads) void k_quantize_act4_row(const void* __re
   __syncthreads();
   amax = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
   const float a = fmaxf(__uint_as_float(amax), 1e-5f);
-  const float qmax = (FMT == 0) ? 7.0f : 6.0f;
+  const float qmax = act4_qmax<FMT>();
   const float inv = div_rn(qmax, a);
-  uint32_t* __restrict__ out = reinterpret_cast<uint32_t*>(codes + m * (K >> 1));
+  uint8_t* __restrict__ out = codes + m * code_row_bytes<FMT>(K);
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int64_t ch = tid + c * kThreads;
-    if (ch < nchunk) out[ch] = encode8<FMT>(v[c], inv);
+    store_chunk<FMT>(out, ch, ch < nchunk, v[c], inv);
   }
   if (tid == 0) scales[m] = div_rn(a, qmax);
 }
@@ -147,10 +191,12 @@ hipError_t launch_quantize_act4(const void* x, bool bf16, int64_t M, int64_t K, 
                                 uint8_t* codes, float* scales, hipStream_t s) {
   if (bf16) {
     return fmt == 0 ? launch_t<true, 0>(x, M, K, codes, scales, s)
-                    : launch_t<true, 1>(x, M, K, codes, scales, s);
+           : fmt == 1 ? launch_t<true, 1>(x, M, K, codes, scales, s)
+                      : launch_t<true, 2>(x, M, K, codes, scales, s);
   }
   return fmt == 0 ? launch_t<false, 0>(x, M, K, codes, scales, s)
-                  : launch_t<false, 1>(x, M, K, codes, scales, s);
+         : fmt == 1 ? launch_t<false, 1>(x, M, K, codes, scales, s)
+                    : launch_t<false, 2>(x, M, K, codes, scales, s);
 }
 
 }  // namespace bw

@@ -92,6 +92,20 @@ def test_grouped_validation():
     assert g(A, None, 64, 11008, 2, w, b, n_ok, y, None, None) == 1
 
 
+def test_e2m3_validation():
+    """BW_ACT_INT4_E2M3 codes are read by the LDS GEMM only: shapes beyond its
+    32-bit offsets are refused before anything is launched."""
+    f = lib.bw_bitlinear_a4
+    assert f(A, A, 1 << 20, 4096, 2, A, A, 128, A, None, None) == 7  # 3 GB of codes
+    assert f(A, A, 64, 4096, 2, A, A, 100, A, None, None) == 2       # N % 16 still checked first
+    g = lib.bw_quantize_bitlinear_a4
+    assert g(A, 1, 1 << 20, 4096, 2, A, A, 128, A, A, A, None, None) == 7
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    w = (P * 2)(A, A)
+    n = (I64 * 2)(128, 4096)
+    assert lib.bw_bitlinear_a4_grouped(A, A, 1 << 20, 4096, 2, 2, w, w, n, w, None, None) == 7
+
+
 def test_gather_validation():
     ws = bw.bw_bitlinear_sparse_a8_gather_workspace_bytes(1, 11008, 4096)
     assert ws >= 4 * 4096 and ws % 256 == 0
