@@ -65,14 +65,14 @@ FP4_PEAK_TOPS = 10100.0  # dense fp4/fp6 MFMA, MI355X (the e2m3 x e2m1 products 
 
 M_PREFILL, HIDDEN, FFN = 2048, 4096, 11008
 
-# HBM traffic of the dominant kernel (W1.58A4 GEMM, M=2048 K=4096 N=11008) from two
+# HBM traffic of the dominant kernel (W1.58A4 GEMM on e2m3 fields, M=2048 K=4096 N=11008) from two
 # rocprofv3 counter passes (FETCH_SIZE x 1.9998 + WRITE_SIZE x 1.0000, scales from a plain
-# 256 MiB copy in the same runs; summary in profiles/gemm_int4_m2048_k4096_n11008_hbm_bytes.md).
+# 256 MiB copy in the same runs; summary in profiles/gemm_int4_e2m3_m2048_k4096_n11008_hbm_bytes.md).
 # It is reported only while the kernel sources still hash to the digest they were taken at.
 GEMM_TRAFFIC = {
-    "bytes": 204_309_059,
+    "bytes": 227_119_986,
     "sources": ("gemm_lds.hip", "bw_widen.h", "bw_device.h"),
-    "sha256": "262982c323e8ff71f0f75f982f00a729939dec2e7cec05f132b6ddc9b7c39157",
+    "sha256": "6e5afd6b06fd9f492e21d8c66438bf1f47f939c5d79e4c5646fbd5bc11506de9",
 }
 
 
