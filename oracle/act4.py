@@ -21,10 +21,7 @@ Readings (the pages give no formula):
   1 sign, 2 exponent bits with bias 1, 3 mantissa bits, subnormals - reads as
   q/8); per 64 values, the 24-byte little-endian bit streams S0 (values 0..31)
   and S1 (values 32..63) are stored as S0[0:16], S1[0:16], S0[16:24],
-  S1[16:24]; and these row bytes are tiled by 16 tokens and 256 values: the
-  192 bytes of token m for values 256s .. 256s+255 are twelve 16-byte units,
-  unit u at byte ((m // 16) * S + s) * 3072 + 256 u + 16 (m % 16), with
-  S = ceil(K / 256) (rows past M and values past K are padding).
+  S1[16:24].
 """
 from __future__ import annotations
 
@@ -167,25 +164,3 @@ def unpack_int4_e2m3(packed: np.ndarray, K: int) -> np.ndarray:
     q = np.rint(v)
     assert np.array_equal(q, v), "field is not an integer multiple of 1/8"
     return q.reshape(M, K).astype(np.int8)
-
-
-def e2m3_tiled_bytes(M: int, K: int) -> int:
-    """Bytes of the tiled e2m3 storage: ceil(M/16) * ceil(K/256) * 3072."""
-    return -(-M // 16) * -(-K // 256) * 3072
-
-
-def tile_int4_e2m3(rows: np.ndarray, K: int) -> tuple[np.ndarray, np.ndarray]:
-    """Row bytes of pack_int4_e2m3 ([M][3K/4]) -> (tiled uint8 [e2m3_tiled_bytes],
-    mask of the bytes that hold data; padding bytes are 0 and unmasked)."""
-    rows = np.asarray(rows, dtype=np.uint8)
-    M = rows.shape[0]
-    G, S = -(-M // 16), -(-K // 256)
-    padded = np.zeros((G * 16, S * 192), dtype=np.uint8)
-    valid = np.zeros_like(padded, dtype=bool)
-    padded[:M, : rows.shape[1]] = rows
-    valid[:M, : rows.shape[1]] = True
-    def tile(a):
-        # [G][16 rows][S][12 units][16 B] -> [G][S][12 units][16 rows][16 B]
-        t = a.reshape(G, 16, S, 12, 16).transpose(0, 2, 3, 1, 4)
-        return np.ascontiguousarray(t).reshape(-1)
-    return tile(padded), tile(valid)

@@ -187,26 +187,3 @@ def test_e2m3_pack_matches_integer_streams_and_round_trips():
     x = rs.standard_normal((3, 256)).astype(np.float32)
     qi, _ = act4.quantize_int4(x)
     assert np.array_equal(act4.unpack_int4_e2m3(act4.pack_int4_e2m3(qi), 256), qi)
-
-
-def test_e2m3_tiling_by_explicit_offsets():
-    """The tiled storage against the offset formula written out per unit."""
-    rs = np.random.default_rng(11)
-    for M, K in [(1, 64), (16, 256), (21, 448), (40, 1024)]:
-        q = rs.integers(-8, 8, size=(M, K)).astype(np.int8)
-        rows = act4.pack_int4_e2m3(q)
-        t, valid = act4.tile_int4_e2m3(rows, K)
-        S = -(-K // 256)
-        assert t.size == act4.e2m3_tiled_bytes(M, K) == -(-M // 16) * S * 3072
-        want = np.zeros(t.size, dtype=np.uint8)
-        mask = np.zeros(t.size, dtype=bool)
-        for m in range(M):
-            for s in range(S):
-                for u in range(12):
-                    src = 192 * s + 16 * u
-                    if src >= rows.shape[1]:
-                        continue
-                    off = ((m // 16) * S + s) * 3072 + 256 * u + 16 * (m % 16)
-                    want[off : off + 16] = rows[m, src : src + 16]
-                    mask[off : off + 16] = True
-        assert np.array_equal(t, want) and np.array_equal(valid, mask)
