@@ -12,7 +12,9 @@
 // waves per row, each wave holding 512-entry chunks in the same per-lane
 // arrangement; measured at 2048 rows of 11008 this is 43.5 us cold against
 // 65 us for a wave per row, while at 2048 rows of 4096 a wave per row stays
-// faster (18 vs 23 us warm).
+// faster (18 vs 23 us warm).  A third kernel takes the one-wave shapes when
+// the input is bf16 without a gate: it selects on the 15-bit bf16 magnitudes
+// themselves (two radix passes, described at the kernel).
 //
 // Lane l of a wave holds entries 512c + 8l + i (i < 8) of its 512-entry
 // chunks c in registers as the fp32 bits of h, read once with 16-byte loads
@@ -370,6 +372,195 @@ __device__ __forceinline__ void find_bin_wave(const int* hist, int per, int need
   cnt_bin = lane_value(cnt, J);
 }
 
+// ------------------------------------ one wave per row, bf16 input without a gate
+// When h is a bf16 input itself, |h| is the low 15 bits of its bf16 word and
+// the fp32 magnitudes order exactly as those bits.  The row then stays in
+// registers as loaded, two entries per word (32 registers for 4096 entries),
+// and tau comes from two radix passes over the 15-bit keys: bits 14..4 (2048
+// bins) over every entry, then bits 3..0 (16 bins) over the entries of the
+// chosen bin.  Zeros are counted like any other key, so tau = 0 falls out
+// when fewer than k_keep entries are nonzero; the lanes' entries past K read
+// as zero (buffer loads past the row) and are taken out of bin 0.  Ties at
+// tau, lowest index first: per 512-entry chunk one ballot per register slot
+// counts the entries equal to tau, and only the chunk where the cut falls
+// ranks them (ballot + mbcnt); the other chunks keep key >= tau or key > tau.
+template <int CH, bool MASK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void k_sparse_a8_wave_bf16(const uint16_t* __restrict__ x, int M, int K, int k_keep, int8_t* __restrict__ codes,
+                           float* __restrict__ scales, uint32_t* __restrict__ mask) {
+  __shared__ __attribute__((aligned(16))) int hist_all[kRowsPerBlock][kHist];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar: LDS and row bases in SGPRs
+  const int m = blockIdx.x * kRowsPerBlock + wave;
+  if (m >= M) return;  // whole wave leaves together
+  int* hist = hist_all[wave];
+  const int64_t row = static_cast<int64_t>(m) * K;
+
+  // w[c][j]: entry 512c + 8 lane + 2j in the low half, 2j + 1 in the high half
+  const auto rs = rsrc(x + row, 2 * static_cast<int64_t>(K));
+  uint32_t w[CH][4];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int e = c * 512 + 8 * lane;
+    const uint4 v = bload16(rs, e < K ? static_cast<uint32_t>(2 * e) : kOutOfRange);
+    w[c][0] = v.x;
+    w[c][1] = v.y;
+    w[c][2] = v.z;
+    w[c][3] = v.w;
+  }
+
+  // ---- row maximum on packed 16-bit magnitudes (exact, order-free)
+  typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+  us2 m2 = {0, 0};
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(us2, w[c][j] & 0x7FFF7FFFu));
+  const uint32_t kmax = lane_value(static_cast<int>(wave_incl_umax(m2.x > m2.y ? m2.x : m2.y)), kWave - 1);
+  const float amax = __uint_as_float(kmax << 16);
+
+  // ---- tau = the k_keep-th largest key; n_gt entries above it, n_eq equal
+  const bool keep_all = k_keep >= K;
+  uint32_t tau = 0;
+  int n_gt = 0, n_eq = K;
+  if (!keep_all) {
+    const int n_pad = 512 * CH - K;  // entries past K, all in bin 0
+#pragma unroll
+    for (int b = 0; b < kBins / kWave; b += 4)
+      *reinterpret_cast<int4*>(&hist[lane * (kBins / kWave) + b]) = make_int4(0, 0, 0, 0);
+    // (each bin index goes through an empty asm statement so that it stays one
+    // bit-field extract followed by one shift-and-add into the LDS address)
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t b0 = __builtin_amdgcn_ubfe(w[c][j], 4, 11), b1 = __builtin_amdgcn_ubfe(w[c][j], 20, 11);
+        asm volatile("" : "+v"(b0), "+v"(b1));
+        atomicAdd(&hist[b0], 1);
+        atomicAdd(&hist[b1], 1);
+      }
+    if (lane == 0 && n_pad > 0) atomicSub(&hist[0], n_pad);
+    int bin1, cum1, c1;
+    find_bin_wave(hist, kBins / kWave, k_keep, lane, bin1, cum1, c1);
+    // pass 2: bits 3..0 of the keys in bin1 (16 bins in words 0..15; every
+    // other key goes to this lane's own bin, so no conflicts)
+    const int need2 = k_keep - cum1;
+    if (lane < 4) *reinterpret_cast<int4*>(&hist[4 * lane]) = make_int4(0, 0, 0, 0);
+    // Per word, with packed 16-bit operations: d = key - 16 bin1 (wrapping
+    // below), then min(d, 16 + lane): a key of the chosen bin lands on its
+    // digit, every other key on a word >= 16 (this lane's own word 16 + lane
+    // unless it lies less than 16 + lane above the bin; the bins past 15 are
+    // never read).
+    const uint32_t lo16 = static_cast<uint32_t>(bin1) << 4;
+    typedef unsigned short us2v __attribute__((ext_vector_type(2)));
+    const us2v base2 = {static_cast<unsigned short>(lo16), static_cast<unsigned short>(lo16)};
+    const us2v disc2 = {static_cast<unsigned short>(16 + lane), static_cast<unsigned short>(16 + lane)};
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const us2v k2 = __builtin_bit_cast(us2v, w[c][j] & 0x7FFF7FFFu);
+        const us2v d2 = __builtin_elementwise_min(k2 - base2, disc2);
+        const uint32_t dd = __builtin_bit_cast(uint32_t, d2);
+        atomicAdd(&hist[dd & 0xFFFFu], 1);
+        atomicAdd(&hist[dd >> 16], 1);
+      }
+    if (lane == 0 && n_pad > 0 && bin1 == 0) atomicSub(&hist[0], n_pad);
+    const int cnt = (lane < 16) ? hist[15 - lane] : 0;
+    const int run = wave_incl_scan(cnt, lane);
+    const int J = __ffsll(static_cast<long long>(__ballot(lane < 16 && run >= need2))) - 1;
+    tau = lo16 | static_cast<uint32_t>(15 - J);
+    n_gt = cum1 + lane_value(run - cnt, J);
+    n_eq = lane_value(cnt, J);
+  }
+  const int need = keep_all ? n_eq : k_keep - n_gt;  // entries equal to tau that survive
+
+  // ---- quantize and write codes (and the keep mask)
+  const float a = fmaxf(amax, 1e-5f);
+  const float inv = div_rn(127.0f, a);
+  int lane_off = 8 * lane;
+  asm volatile("" : "+v"(lane_off));
+  int8_t* out = codes + row;
+  // |h| <= a' keeps |h * fl(127/a')| below 127.5: rne() lands in [-127, 127];
+  // adding 1.5 * 2^23 leaves it, two's complement, in the low mantissa byte.
+  // A dropped entry is quantized as 0.
+  auto q_of = [&](float h, bool keep) { return __float_as_uint(mul_rn(keep ? h : 0.0f, inv) + 12582912.0f); };
+  auto pack4 = [](uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3) {
+    return __builtin_amdgcn_perm(c1, c0, 0x0c0c0400u) | __builtin_amdgcn_perm(c3, c2, 0x04000c0cu);
+  };
+  auto store = [&](int c, const uint32_t (&q)[8], uint32_t kbits) {
+    const int e = c * 512 + lane_off;
+    if (e < K) {
+      *reinterpret_cast<uint2*>(out + e) = make_uint2(pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]));
+      if constexpr (MASK) reinterpret_cast<uint8_t*>(mask)[(row + e) >> 3] = static_cast<uint8_t>(kbits);
+    }
+  };
+  // keep = key >= thr for a whole chunk
+  auto encode_thr = [&](int c, uint32_t thr) {
+    uint32_t q[8];
+    uint32_t kbits = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t v = w[c][j];
+      const bool k0 = (v & 0x7FFFu) >= thr;
+      const bool k1 = __builtin_amdgcn_ubfe(v, 16, 15) >= thr;
+      q[2 * j] = q_of(bf16_lo(v), k0);
+      q[2 * j + 1] = q_of(bf16_hi(v), k1);
+      if constexpr (MASK) kbits |= (static_cast<uint32_t>(k0) << (2 * j)) | (static_cast<uint32_t>(k1) << (2 * j + 1));
+    }
+    store(c, q, kbits);
+  };
+  // when tau = 0 and no mask is asked for, the entries equal to tau are zeros,
+  // whose code is 0 whether they are kept or not
+  if (n_eq == need || (!MASK && tau == 0u)) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) encode_thr(c, tau);
+  } else {
+    int taken = 0;  // entries equal to tau in earlier chunks (index order)
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      if (taken >= need) {  // every later tie is dropped
+        encode_thr(c, tau + 1u);
+        continue;
+      }
+      uint64_t eq[8];
+      int total = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        eq[2 * j] = __ballot((w[c][j] & 0x7FFFu) == tau);
+        eq[2 * j + 1] = __ballot(__builtin_amdgcn_ubfe(w[c][j], 16, 15) == tau);
+        total += __popcll(eq[2 * j]) + __popcll(eq[2 * j + 1]);
+      }
+      if (taken + total <= need) {  // every tie of this chunk survives
+        encode_thr(c, tau);
+        taken += total;
+        continue;
+      }
+      // the cut falls in this chunk: rank = ties at lower indices
+      int rank = taken;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        rank = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(eq[i] >> 32),
+                                         __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(eq[i]), rank));
+      uint32_t q[8];
+      uint32_t kbits = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t v = w[c][i >> 1];
+        const uint32_t k = (i & 1) ? __builtin_amdgcn_ubfe(v, 16, 15) : (v & 0x7FFFu);
+        const bool is_eq = k == tau;
+        const bool keep = k > tau || (is_eq && rank < need);
+        rank += static_cast<int>(is_eq);
+        q[i] = q_of((i & 1) ? bf16_hi(v) : bf16_lo(v), keep);
+        if constexpr (MASK) kbits |= static_cast<uint32_t>(keep) << i;
+      }
+      store(c, q, kbits);
+      taken += total;
+    }
+  }
+  if (lane == 0) scales[m] = div_rn(a, 127.0f);
+}
+
 template <bool BF16, bool GATED, int CH, int NW>
 __global__ __launch_bounds__(NW * kWave) void k_sparse_a8_block(const void* __restrict__ g,
                                                                  const void* __restrict__ u, int K, int k_keep,
@@ -641,6 +832,12 @@ hipError_t launch_t(const void* g, const void* u, int64_t M, int64_t K, int64_t 
     // short rows: a workgroup per row while few rows, else a wave per row
     if (M <= kBlockRowsMax)
       hipLaunchKernelGGL((k_sparse_a8_block<BF16, GATED, 1, 8>), bgrid, bblock, 0, s, g, u, k, kk, codes, scales, mask);
+    else if (BF16 && !GATED && mask)
+      hipLaunchKernelGGL((k_sparse_a8_wave_bf16<8, true>), wgrid, block, 0, s, static_cast<const uint16_t*>(g), m, k, kk,
+                         codes, scales, mask);
+    else if (BF16 && !GATED)
+      hipLaunchKernelGGL((k_sparse_a8_wave_bf16<8, false>), wgrid, block, 0, s, static_cast<const uint16_t*>(g), m, k,
+                         kk, codes, scales, mask);
     else
       hipLaunchKernelGGL((k_sparse_a8_wave<BF16, GATED, 8>), wgrid, block, 0, s, g, u, m, k, kk, codes, scales, mask);
   } else if (K <= 8192) {

@@ -96,6 +96,40 @@ def test_nonzero_count_around_k(k):
     check(f32_dev(x), None, x, None, k, f"nnz around k={k}, 264 rows")
 
 
+def plain_bf16_rows(K: int, M: int = 264) -> synth.Bf16:
+    """bf16 rows without a gate, more than 256 of them (the one-wave-per-row kernel
+    on 16-bit keys): integer values (a handful of magnitudes, so ties at tau straddle
+    the 512-entry chunks), a zero row, a constant row, rows with K/2 - 1, K/2 and
+    K/2 + 1 nonzero entries, rows of bf16 subnormals (every key in the first radix
+    bin) mixed with zeros and with the largest finite magnitude, and Student-t rows."""
+    rs = np.random.default_rng(K + 17)
+    x = rs.integers(-3, 4, size=(M, K)).astype(np.float32)
+    x[0] = 0.0
+    x[1] = -2.0
+    for r, nz in ((2, K // 2 - 1), (3, K // 2), (4, K // 2 + 1)):
+        x[r] = 0.0
+        x[r, rs.choice(K, size=nz, replace=False)] = rs.standard_normal(nz).astype(np.float32)
+    sub = (rs.integers(0, 16, size=(2, K)).astype(np.uint32) << 16).view(np.float32)  # bf16 subnormals and zeros
+    x[5:7] = sub * np.where(rs.random((2, K)) < 0.5, -1.0, 1.0).astype(np.float32)
+    x[6, 7] = np.float32(3.3895314e38)  # largest finite bf16
+    x[8:72] = rs.standard_t(3.0, size=(64, K)).astype(np.float32)
+    return synth.to_bf16(x)
+
+
+@pytest.mark.parametrize("K", [64, 576, 1024, 4032, 4096])
+def test_plain_bf16_rows_ties_zeros_tail(K):
+    """Every keep count class on the 16-bit-key kernel, with and without the keep mask
+    (the mask-free call takes the tau = 0 shortcut); K < 4096 leaves lanes past K."""
+    b = plain_bf16_rows(K)
+    xd = bf16_dev(b)
+    for k in sorted({1, 2, K // 2, K - 1, K}):
+        check(xd, None, b.f32, None, k, f"plain bf16 K={K} k={k}")
+        codes, scales = bw.bw_quantize_sparse_a8(xd, None, k)
+        _, _, q, rsc = sparse8.sparse_a8(b.f32, None, k)
+        assert_same(host(codes), q, f"plain bf16 K={K} k={k} codes (no mask)")
+        assert_same(host(scales).view(np.uint32), rsc.view(np.uint32), f"plain bf16 K={K} k={k} scales (no mask)")
+
+
 def test_full_down_proj_shape_sampled():
     """M=2048, K=11008 bf16 (the benchmark's launch), 64 sampled rows vs the oracle."""
     M, K = 2048, 11008
