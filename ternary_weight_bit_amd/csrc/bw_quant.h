@@ -32,10 +32,11 @@ __device__ __forceinline__ uint32_t e2m1_code(float t) {
 
 // The INT4 value rne(t) of int4_code_absmax as a 6-bit e2m3 field: bit 5 the
 // sign (clear for 0), bits 4..0 the magnitude (e2m3 reads them as |q| / 8).
+// rne(|t|) is 0 exactly when |t| <= 0.5, so the sign bit belongs to t < -0.5,
+// i.e. to the bit patterns above that of -0.5 (0xBF000000) read as unsigned.
 __device__ __forceinline__ uint32_t e2m3_field_absmax(float t) {
   const uint32_t mag = __float_as_uint(fabsf(t) + 12582912.0f) & 0xFu;
-  const uint32_t neg = (__float_as_uint(t) >> 31) & static_cast<uint32_t>(mag != 0u);
-  return mag | (neg << 5);
+  return mag | (__float_as_uint(t) > 0xBF000000u ? 32u : 0u);
 }
 
 // FMT 0 = INT4, 1 = e2m1, 2 = INT4 as an e2m3 field: the code of one element

@@ -59,7 +59,9 @@ __device__ __forceinline__ void store_chunk(uint8_t* __restrict__ row, int64_t c
   } else {
     const uint64_t e = encode8_e2m3(v, inv);
     const uint32_t lo = static_cast<uint32_t>(e), hi = static_cast<uint32_t>(e >> 32);
-    const uint32_t plo = __shfl_xor(lo, 1), phi = __shfl_xor(hi, 1);
+    // the other lane of the pair (DPP quad_perm 1,0,3,2: a VALU move, no LDS)
+    const uint32_t plo = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(lo), 0xB1, 0xF, 0xF, false));
+    const uint32_t phi = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(hi), 0xB1, 0xF, 0xF, false));
     if (valid && (ch & 1) == 0) {
       const uint32_t d0 = lo, d1 = hi | (plo << 16), d2 = (plo >> 16) | (phi << 16);
       uint8_t* g = row + 48 * (ch >> 3) + 16 * ((ch >> 2) & 1);  // this half's first 16 bytes
