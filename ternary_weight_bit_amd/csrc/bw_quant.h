@@ -21,15 +21,6 @@ __device__ __forceinline__ uint32_t int4_code_absmax(float t) {
   return __float_as_uint(t + 12582912.0f) & 0xFu;
 }
 
-// e2m1 code of t: nearest of {0,.5,1,1.5,2,3,4,6}; at a midpoint the
-// neighbour with the even code wins; saturates at 6; sign bit from t.
-__device__ __forceinline__ uint32_t e2m1_code(float t) {
-  const float m = fabsf(t);
-  uint32_t c = (m > 0.25f) + (m >= 0.75f) + (m > 1.25f) + (m >= 1.75f) + (m > 2.5f) + (m >= 3.5f) +
-               (m > 5.0f);
-  return c | ((__float_as_uint(t) >> 31) << 3);
-}
-
 // The INT4 value rne(t) of int4_code_absmax as a 6-bit e2m3 field: bit 5 the
 // sign (clear for 0), bits 4..0 the magnitude (e2m3 reads them as |q| / 8).
 // rne(|t|) is 0 exactly when |t| <= 0.5, so the sign bit belongs to t < -0.5,
@@ -39,12 +30,34 @@ __device__ __forceinline__ uint32_t e2m3_field_absmax(float t) {
   return mag | (__float_as_uint(t) > 0xBF000000u ? 32u : 0u);
 }
 
-// FMT 0 = INT4, 1 = e2m1, 2 = INT4 as an e2m3 field: the code of one element
-// given inv = fl(qmax / a').
+// FMT 0 = INT4, 2 = INT4 as an e2m3 field: the code of one element given
+// inv = fl(qmax / a').
 template <int FMT>
 __device__ __forceinline__ uint32_t act4_code(float x, float inv) {
+  static_assert(FMT == 0 || FMT == 2, "e2m1 codes come in words (act4_word)");
   const float t = mul_rn(x, inv);
-  return FMT == 0 ? int4_code_absmax(t) : FMT == 1 ? e2m1_code(t) : e2m3_field_absmax(t);
+  return FMT == 0 ? int4_code_absmax(t) : e2m3_field_absmax(t);
+}
+
+// Eight 4-bit codes as one word, element i in nibble i: FMT 0 = INT4, 1 =
+// e2m1.  e2m1 is the nearest of {0,.5,1,1.5,2,3,4,6} to t = fl(x * inv), at
+// a midpoint the neighbour with the even code, saturating at 6, with the sign
+// bit of t (zeros included); the f32 -> fp4 conversion instruction (scale 1)
+// rounds exactly so, two elements per instruction into one byte of the word.
+template <int FMT>
+__device__ __forceinline__ uint32_t act4_word(const float (&x)[8], float inv) {
+  static_assert(FMT == 0 || FMT == 1, "4-bit codes");
+  uint32_t w = 0;
+  if constexpr (FMT == 1) {
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, mul_rn(x[0], inv), mul_rn(x[1], inv), 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, mul_rn(x[2], inv), mul_rn(x[3], inv), 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, mul_rn(x[4], inv), mul_rn(x[5], inv), 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, mul_rn(x[6], inv), mul_rn(x[7], inv), 1.0f, 3);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= act4_code<0>(x[i], inv) << (4 * i);
+  }
+  return w;
 }
 
 template <int FMT>

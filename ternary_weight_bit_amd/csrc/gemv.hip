@@ -274,9 +274,10 @@ __global__ __launch_bounds__(256) void k_gemv_quant(const void* __restrict__ X, 
 #pragma unroll
     for (int i = 0; i < CPR; ++i) {
       const int c = tid + 256 * i;
-      uint32_t word = 0;
+      float xe[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) word |= act4_code<FMT>(elem(xv[m][i], e), inv) << (4 * e);
+      for (int e = 0; e < 8; ++e) xe[e] = elem(xv[m][i], e);
+      const uint32_t word = act4_word<FMT>(xe, inv);
       if (m < M && c < nch) {
         *reinterpret_cast<uint32_t*>(s_codes + m * cstride + c * 4) = word;
         if (nb == 0) reinterpret_cast<uint32_t*>(codes + m * (K >> 1))[c] = word;

@@ -25,10 +25,7 @@ constexpr int kRowsPerBlock = kThreads / kWave;
 // a' >= max|v|, so act4_code's INT4 rounding add applies (no clamp needed).
 template <int FMT>
 __device__ __forceinline__ uint32_t encode8(const float (&v)[8], float inv) {
-  uint32_t w = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) w |= act4_code<FMT>(v[i], inv) << (4 * i);
-  return w;
+  return act4_word<FMT>(v, inv);
 }
 
 // Eight INT4 values as e2m3 fields, value i at bits 6i..6i+5 of 48 bits.

@@ -60,6 +60,7 @@ def test_edge_rows(fmt, name):
         np.tile([6, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], K // 8) * np.where(np.arange(K) % 2, 1, -1),
         np.r_[[-0.0] * (K // 2), [1e-5] * (K // 2)],  # negative zeros, row max at the floor
         np.r_[[7.0], np.full(K - 1, 3.5)],
+        np.where(np.arange(K) % 2, 1e-44, -1e-44),    # fp32 subnormal inputs and products, both signs
     ]
     x = np.array(rows, dtype=np.float32)
     check(f32_dev(x), x, fmt, f"edge rows {name}")
@@ -77,13 +78,14 @@ def test_many_rows(fmt, name, M, K):
 
 @pytest.mark.parametrize("fmt,name", FMTS)
 def test_edge_rows_many(fmt, name):
-    """The edge rows repeated over 1032 rows."""
+    """The edge rows repeated over 1161 rows."""
     K = 128
     base = np.array([
         np.zeros(K), np.full(K, -2.5), np.where(np.arange(K) % 2, 1e-30, -1e-30),
         np.where(np.arange(K) % 3 == 0, 3e30, 1.0), np.linspace(-7, 7, K),
         np.tile([6, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], K // 8) * np.where(np.arange(K) % 2, 1, -1),
         np.r_[[-0.0] * (K // 2), [1e-5] * (K // 2)], np.r_[[7.0], np.full(K - 1, 3.5)],
+        np.where(np.arange(K) % 2, 1e-44, -1e-44),
     ], dtype=np.float32)
     x = np.tile(base, (129, 1))
     check(f32_dev(x), x, fmt, f"edge rows x129 {name}")
