@@ -338,6 +338,17 @@ class Bench:
                   [prefill_int4_nibbles]))
         R.append(("_evict_cache_0", None, 0, [self.evict_cache]))
 
+        def prefill_fp4():
+            bw.bw_quantize(self.x_pre, bw.BW_ACT_FP4_E2M1, self.cf, self.sf)
+            bw.bw_bitlinear_a4_grouped(self.cf, self.sf, bw.BW_ACT_FP4_E2M1,
+                                       [(self.wp_11008, self.b_11008), (self.wp_4096, self.b_4096)],
+                                       ys=[self.y_11008, self.y_4096])
+
+        # the pages' FP4 alternative to INT4: e2m1 activation codes (per-token scale)
+        # and the two products on the fp4 x fp4 matrix instruction, same sequence
+        R.append(("a0f_prefill_fp4_sequence", "TOPS", gemm_ops(M, FFN, K) + gemm_ops(M, HIDDEN, K), [prefill_fp4]))
+        R.append(("_evict_cache_1", None, 0, [self.evict_cache]))
+
         def prefill_b158():
             bw.bw_quantize_sparse_a8(self.x_pre, None, K, self.c8_pre, self.s8_pre)
             bw.bw_bitlinear_sparse_a8_grouped(self.c8_pre, self.s8_pre,
@@ -680,7 +691,7 @@ def main():
         avg_ms = float(np.mean(row_ms)) / len(fns)
         rate = amount / (avg_ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
         peak = HBM_PEAK_GBS if unit == "GB/s" else (
-            FP4_PEAK_TOPS if ("fp4" in name or "e2m3" in name or name.startswith("a0_")) else INT8_PEAK_TOPS)
+            FP4_PEAK_TOPS if ("fp4" in name or "e2m3" in name or name.startswith(("a0_", "a0f_"))) else INT8_PEAK_TOPS)
         table[name] = {"avg_us": round(avg_ms * 1e3, 3), "launches_per_step": len(fns), "rate": round(rate, 2),
                        "unit": unit, "frac_of_peak": round(rate / peak, 4), "amount_per_launch": amount,
                        # spread over the timed steps (per launch), to show steps that ran slow
@@ -700,6 +711,9 @@ def main():
     nibbles = None
     if "a0n_prefill_int4_nibbles_sequence" in table:
         nibbles = round(prefill_ops / (row_ms(("a0n_prefill_int4_nibbles_sequence",)) * 1e-3) / 1e12, 2)
+    fp4seq = None
+    if "a0f_prefill_fp4_sequence" in table:
+        fp4seq = round(prefill_ops / (row_ms(("a0f_prefill_fp4_sequence",)) * 1e-3) / 1e12, 2)
     b158 = None
     if "b0_prefill_b158_int8_sequence" in table:
         b158 = round(prefill_ops / (row_ms(("b0_prefill_b158_int8_sequence",)) * 1e-3) / 1e12, 2)
@@ -802,6 +816,11 @@ def main():
         "int4_nibble_sequence": None if nibbles is None else {
             "value": nibbles, "unit": "TOPS",
             "basis": "the same sequence with INT4 nibble codes widened to int8 for the int8 MFMA (row a0n)"},
+        "fp4_sequence": None if fp4seq is None else {
+            "value": fp4seq, "unit": "TOPS", "frac_of_fp4_peak": round(fp4seq / FP4_PEAK_TOPS, 4),
+            "basis": "the same two products with FP4 e2m1 activation codes (the pages' alternative to INT4, "
+                     "per-token scale): e2m1 quantizer + both W1.58 x FP4 products in one grouped launch on the "
+                     "fp4 x fp4 MFMA, back to back (row a0f); a variant beside value, not its basis"},
         "b158_baseline": None if b158 is None else {
             "value": b158, "unit": "TOPS",
             "basis": "same ops / time of INT8 absmax (all entries, no top-k) + the two W1.58A8 products over its "
