@@ -21,22 +21,22 @@ __device__ __forceinline__ uint32_t int4_code_absmax(float t) {
   return __float_as_uint(t + 12582912.0f) & 0xFu;
 }
 
-// The INT4 value rne(t) of int4_code_absmax as a 6-bit e2m3 field: bit 5 the
-// sign (clear for 0), bits 4..0 the magnitude (e2m3 reads them as |q| / 8).
-// rne(|t|) is 0 exactly when |t| <= 0.5, so the sign bit belongs to t < -0.5,
-// i.e. to the bit patterns above that of -0.5 (0xBF000000) read as unsigned.
-__device__ __forceinline__ uint32_t e2m3_field_absmax(float t) {
-  const uint32_t mag = __float_as_uint(fabsf(t) + 12582912.0f) & 0xFu;
-  return mag | (__float_as_uint(t) > 0xBF000000u ? 32u : 0u);
-}
-
-// FMT 0 = INT4, 2 = INT4 as an e2m3 field: the code of one element given
-// inv = fl(qmax / a').
+// FMT 0 = INT4: the code of one element given inv = fl(qmax / a').
 template <int FMT>
 __device__ __forceinline__ uint32_t act4_code(float x, float inv) {
-  static_assert(FMT == 0 || FMT == 2, "e2m1 codes come in words (act4_word)");
-  const float t = mul_rn(x, inv);
-  return FMT == 0 ? int4_code_absmax(t) : e2m3_field_absmax(t);
+  static_assert(FMT == 0, "e2m1 codes come in words (act4_word), e2m3 fields in streams (e2m3_input)");
+  return int4_code_absmax(mul_rn(x, inv));
+}
+
+// INT4 values stored as 6-bit e2m3 fields (bit 5 the sign, clear for 0; bits
+// 4..0 the magnitude |q|, which e2m3 reads as |q| / 8) come from the f32 -> fp6
+// conversion of t / 8: q / 8 lies on e2m3's subnormal grid (step 1/8), so
+// nearest with ties to even gives the field of rne(t).  rne(|t|) is 0 exactly
+// when |t| <= 0.5, i.e. for bit patterns of t up to that of -0.5 (0xBF000000)
+// read as unsigned among the negatives; such a t is passed as |t| so that its
+// zero field has the sign clear.
+__device__ __forceinline__ float e2m3_input(float t) {
+  return __float_as_uint(t) > 0xBF000000u ? t : fabsf(t);
 }
 
 // Eight 4-bit codes as one word, element i in nibble i: FMT 0 = INT4, 1 =

@@ -28,12 +28,31 @@ __device__ __forceinline__ uint32_t encode8(const float (&v)[8], float inv) {
   return act4_word<FMT>(v, inv);
 }
 
-// Eight INT4 values as e2m3 fields, value i at bits 6i..6i+5 of 48 bits.
-__device__ __forceinline__ uint64_t encode8_e2m3(const float (&v)[8], float inv) {
-  uint64_t w = 0;
+// e2m3 fields of the INT4 values of up to four chunks (v[C0 + k], k < 4, of
+// the CPT a thread holds) by one conversion of 32 values.  The conversion
+// writes field j (bits 6j .. 6j+5 of its 192-bit output) from its first
+// operand's element j / 2 when j is even and from its second operand's when j
+// is odd, so value j of the 32 goes there; chunk k then takes bits 48k .. 48k
+// + 47, returned as lo = its bits 0..31 and hi = its bits 32..47.
+template <int CPT, int C0>
+__device__ __forceinline__ void encode_e2m3(const float (&v)[CPT][8], float inv, uint32_t (&lo)[CPT],
+                                            uint32_t (&hi)[CPT]) {
+  constexpr int n = CPT - C0 < 4 ? CPT - C0 : 4;
+  v16f a, b;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) w |= static_cast<uint64_t>(act4_code<2>(v[i], inv)) << (6 * i);
-  return w;
+  for (int j = 0; j < 32; ++j) {
+    const int k = (j >> 3) % n;  // slots past the chunks repeat one (their fields are not used)
+    const float t = e2m3_input(mul_rn(v[C0 + k][j & 7], inv));
+    if (j & 1) b[j >> 1] = t;
+    else a[j >> 1] = t;
+  }
+  const auto r = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(a, b, 8.0f);
+#pragma unroll
+  for (int k = 0; k < n; ++k) {
+    const uint32_t w0 = r[3 * (k >> 1)], w1 = r[3 * (k >> 1) + 1], w2 = r[3 * (k >> 1) + 2];
+    lo[C0 + k] = (k & 1) ? ((w1 >> 16) | (w2 << 16)) : w0;
+    hi[C0 + k] = (k & 1) ? (w2 >> 16) : (w1 & 0xFFFFu);
+  }
 }
 
 // Row bytes of K values: two codes per byte, or e2m3 fields (3 bytes per 4).
@@ -43,31 +62,32 @@ __device__ __forceinline__ int64_t code_row_bytes(int64_t K) {
 }
 
 // Store the codes of chunk ch (values 8ch .. 8ch+7) of a row.  Nibbles: one
-// word.  e2m3 fields: 64 values form a group of 48 bytes, the 24-byte bit
-// streams of values 0..31 (S0) and 32..63 (S1) stored as S0[0:16], S1[0:16],
-// S0[16:24], S1[16:24]; chunk j of a half covers bytes 6j .. 6j+5 of its
-// stream.  The even lane of each lane pair (chunks 2p, 2p+1 of a half) writes
-// their 12 bytes; every lane of the wave must call this (a lane exchange).
+// word.  e2m3 fields (given as the chunk's 48 bits lo | hi << 32): 64 values
+// form a group of 48 bytes, the 24-byte bit streams of values 0..31 (S0) and
+// 32..63 (S1) stored as S0[0:16], S1[0:16], S0[16:24], S1[16:24]; chunk j of a
+// half covers bytes 6j .. 6j+5 of its stream.  The even lane of each lane pair
+// (chunks 2p, 2p+1 of a half) writes their 12 bytes; every lane of the wave
+// must call the e2m3 store (a lane exchange).
 template <int FMT>
 __device__ __forceinline__ void store_chunk(uint8_t* __restrict__ row, int64_t ch, bool valid,
                                             const float (&v)[8], float inv) {
-  if constexpr (FMT != 2) {
-    if (valid) reinterpret_cast<uint32_t*>(row)[ch] = encode8<FMT>(v, inv);
-  } else {
-    const uint64_t e = encode8_e2m3(v, inv);
-    const uint32_t lo = static_cast<uint32_t>(e), hi = static_cast<uint32_t>(e >> 32);
-    // the other lane of the pair (DPP quad_perm 1,0,3,2: a VALU move, no LDS)
-    const uint32_t plo = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(lo), 0xB1, 0xF, 0xF, false));
-    const uint32_t phi = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(hi), 0xB1, 0xF, 0xF, false));
-    if (valid && (ch & 1) == 0) {
-      const uint32_t d0 = lo, d1 = hi | (plo << 16), d2 = (plo >> 16) | (phi << 16);
-      uint8_t* g = row + 48 * (ch >> 3) + 16 * ((ch >> 2) & 1);  // this half's first 16 bytes
-      if ((ch & 2) == 0) {  // stream bytes 0..11
-        *reinterpret_cast<uint3*>(g) = make_uint3(d0, d1, d2);
-      } else {              // stream bytes 12..23: the last word of the first 16, then the last 8
-        reinterpret_cast<uint32_t*>(g)[3] = d0;
-        *reinterpret_cast<uint2*>(row + 48 * (ch >> 3) + 32 + 8 * ((ch >> 2) & 1)) = make_uint2(d1, d2);
-      }
+  static_assert(FMT != 2, "e2m3 fields: store_e2m3");
+  if (valid) reinterpret_cast<uint32_t*>(row)[ch] = encode8<FMT>(v, inv);
+}
+
+__device__ __forceinline__ void store_e2m3(uint8_t* __restrict__ row, int64_t ch, bool valid, uint32_t lo,
+                                           uint32_t hi) {
+  // the other lane of the pair (DPP quad_perm 1,0,3,2: a VALU move, no LDS)
+  const uint32_t plo = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(lo), 0xB1, 0xF, 0xF, false));
+  const uint32_t phi = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(hi), 0xB1, 0xF, 0xF, false));
+  if (valid && (ch & 1) == 0) {
+    const uint32_t d0 = lo, d1 = hi | (plo << 16), d2 = (plo >> 16) | (phi << 16);
+    uint8_t* g = row + 48 * (ch >> 3) + 16 * ((ch >> 2) & 1);  // this half's first 16 bytes
+    if ((ch & 2) == 0) {  // stream bytes 0..11
+      *reinterpret_cast<uint3*>(g) = make_uint3(d0, d1, d2);
+    } else {              // stream bytes 12..23: the last word of the first 16, then the last 8
+      reinterpret_cast<uint32_t*>(g)[3] = d0;
+      *reinterpret_cast<uint2*>(row + 48 * (ch >> 3) + 32 + 8 * ((ch >> 2) & 1)) = make_uint2(d1, d2);
     }
   }
 }
@@ -97,9 +117,15 @@ __global__ __launch_bounds__(kThreads) void k_quantize_act4(const void* __restri
   const float inv = div_rn(qmax, a);
   // nchunk is a multiple of 8: the lanes of a pair leave the loop together
   for (int64_t ch = lane; ch < nchunk; ch += kWave) {
-    float t[8];
-    load8<BF16>(x, row + ch * 8, t);
-    store_chunk<FMT>(out, ch, true, t, inv);
+    float t[1][8];
+    load8<BF16>(x, row + ch * 8, t[0]);
+    if constexpr (FMT == 2) {
+      uint32_t lo[1], hi[1];
+      encode_e2m3<1, 0>(t, inv, lo, hi);
+      store_e2m3(out, ch, true, lo[0], hi[0]);
+    } else {
+      store_chunk<FMT>(out, ch, true, t[0], inv);
+    }
   }
   if (lane == 0) scales[m] = div_rn(a, qmax);
 }
@@ -160,10 +186,21 @@ __global__ __launch_bounds__(kThreads) void k_quantize_act4_row(const void* __re
   const float qmax = act4_qmax<FMT>();
   const float inv = div_rn(qmax, a);
   uint8_t* __restrict__ out = codes + m * code_row_bytes<FMT>(K);
+  if constexpr (FMT == 2) {
+    uint32_t lo[CPT], hi[CPT];
+    encode_e2m3<CPT, 0>(v, inv, lo, hi);
+    if constexpr (CPT > 4) encode_e2m3<CPT, 4>(v, inv, lo, hi);
 #pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    const int64_t ch = tid + c * kThreads;
-    store_chunk<FMT>(out, ch, ch < nchunk, v[c], inv);
+    for (int c = 0; c < CPT; ++c) {
+      const int64_t ch = tid + c * kThreads;
+      store_e2m3(out, ch, ch < nchunk, lo[c], hi[c]);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int64_t ch = tid + c * kThreads;
+      store_chunk<FMT>(out, ch, ch < nchunk, v[c], inv);
+    }
   }
   if (tid == 0) scales[m] = div_rn(a, qmax);
 }

@@ -42,6 +42,37 @@ def test_quantize_e2m3_vs_oracle(M, K, dtype):
     assert_same(host(codes), act4.pack_int4_e2m3(q), f"e2m3 codes {M}x{K}")
 
 
+def e2m3_edge_rows(K: int) -> np.ndarray:
+    """Rows whose scale is exactly 1 (row maximum 7), so that t = x: every halfway
+    case of rne(t) of both signs, the values around -0.5 (the last t whose field is
+    +0 and the first that is -1), negative zeros, fp32 subnormals of both signs;
+    plus a zero row, a constant negative row, tiny and huge magnitudes."""
+    halves = np.array([k + 0.5 for k in range(7)], np.float32)
+    around = np.array([-0.5, np.nextafter(np.float32(-0.5), np.float32(-1)), np.nextafter(np.float32(-0.5), np.float32(0)),
+                       -0.0, 0.0, 0.5, -1e-44, 1e-44, -0.25, -1.0, 1.0, -7.0], np.float32)
+    ties = np.concatenate([[7.0], halves, -halves, around]).astype(np.float32)
+    rows = [
+        np.resize(ties, K),
+        np.resize(ties[::-1], K),
+        np.zeros(K),
+        np.full(K, -2.5),
+        np.where(np.arange(K) % 2, 1e-30, -1e-30),
+        np.where(np.arange(K) % 3 == 0, 3e30, -1.0),
+    ]
+    return np.array(rows, dtype=np.float32)
+
+
+@pytest.mark.parametrize("K", [64, 192, 4096, 16384])
+def test_quantize_e2m3_edge_rows(K):
+    """Ties, signs of zero fields and subnormals on the row kernel (K <= 8192) and
+    the one-wave-per-row kernel (longer rows), bit for bit against the oracle."""
+    x32 = e2m3_edge_rows(K)
+    codes, scales = bw.bw_quantize(f32_dev(x32), E6)
+    q, s = act4.quantize_int4(x32)
+    assert_same(host(scales).view(np.uint32), s.view(np.uint32), f"e2m3 edge scales K={K}")
+    assert_same(host(codes), act4.pack_int4_e2m3(q), f"e2m3 edge codes K={K}")
+
+
 def a4_pair(M, K, N, seed):
     x = synth.to_bf16(synth.normal(seed, (M, K)))
     w = synth.to_bf16(synth.normal(seed + 1, (N, K), 0.02))
