@@ -111,7 +111,8 @@ static bw_status check_gemm(const char* who, const void* codes, const float* sx,
   return ok();
 }
 
-// e2m3 fields are read by the LDS GEMM only (any M); it must take the shape.
+// e2m3 fields are read by the decode GEMV (M <= 16) and the LDS GEMM; the
+// shape must fit the LDS GEMM's 32-bit offsets (it also bounds the GEMV's).
 static bw_status check_e2m3(const char* who, int64_t M, int64_t K, int64_t N) {
   BW_REQUIRE(bw::gemm_lds_supported(3, M, K, N), BW_ERR_UNSUPPORTED,
              "%s: BW_ACT_INT4_E2M3 needs M*3K/4 and N*K/4 below 2^31 bytes (M=%lld K=%lld N=%lld)", who,
@@ -119,11 +120,12 @@ static bw_status check_e2m3(const char* who, int64_t M, int64_t K, int64_t N) {
   return ok();
 }
 
-// One product: e2m3 fields go to the LDS GEMM, the other formats through the
-// GEMV / GEMM dispatch.
+// One product: decode shapes (M <= 16) go to the GEMV in every format; larger
+// batches of e2m3 fields to the LDS GEMM, the other formats through the GEMM
+// dispatch.
 static hipError_t launch_a4(int mode, const void* codes, const float* sx, int64_t M, int64_t K, const uint8_t* w,
                             const float* beta, int64_t N, float* y, void* acc, hipStream_t s) {
-  if (mode == 3) return bw::launch_gemm_lds(mode, codes, sx, M, K, w, beta, N, y, acc, s);
+  if (mode == 3 && M > bw::kGemvMaxM) return bw::launch_gemm_lds(mode, codes, sx, M, K, w, beta, N, y, acc, s);
   return bw::launch_bitlinear(mode, codes, sx, M, K, w, beta, N, y, acc, s);
 }
 
@@ -161,7 +163,7 @@ static bw_status bitlinear_grouped(const char* who, int mode, const void* codes,
     }
     BW_REQUIRE(tiles < (int64_t{1} << 31), BW_ERR_UNSUPPORTED, "%s: %lld tiles in one launch", who, (long long)tiles);
   }
-  bool grouped = M > bw::kGemvMaxM || mode == 3;
+  bool grouped = M > bw::kGemvMaxM;
   int64_t tiles = 0;
   for (int g = 0; g < n && grouped; ++g) {
     grouped = bw::gemm_lds_supported(mode, M, K, N[g]);
@@ -182,7 +184,7 @@ static bw_status bitlinear_grouped(const char* who, int mode, const void* codes,
   }
   for (int g = 0; g < n; ++g) {
     bw_status st = hip_status(
-        bw::launch_bitlinear(mode, codes, x_scales, M, K, w[g], beta[g], N[g], y[g], acc ? acc[g] : nullptr, s), who);
+        launch_a4(mode, codes, x_scales, M, K, w[g], beta[g], N[g], y[g], acc ? acc[g] : nullptr, s), who);
     if (st != BW_OK) return st;
   }
   return ok();

@@ -16,7 +16,10 @@
 //     memory access (no clamped re-reads, no selects after the load).  INT8
 //     activation loads are issued only by the lanes of real rows;
 //   * the tokens (zero-padded to 16) are the rows of 16x16 MFMAs (i8 16x16x64,
-//     or scaled f8f6f4 16x16x128 for e2m1);
+//     or scaled f8f6f4 16x16x128 for e2m1 codes and for INT4 values stored as
+//     e2m3 fields; those use the weights as e2m1 +-2.0 by one mask, so a
+//     4-tile round costs a few VALU operations instead of widening every
+//     nibble and 2-bit code to a byte, and the fp32 sums are exact integers);
 //   * the waves' partial int32/fp32 tiles are summed through LDS (exact) and
 //     the epilogue writes y for the M real rows; optionally it adds a residual
 //     (y = r + W x, the decoder layer's skip connections) and splits the
@@ -39,8 +42,9 @@ namespace {
 
 template <int MODE>
 struct TileOps {
-  static constexpr int AW = (MODE == MODE_INT8) ? 4 : 2;  // 16-byte activation parts per tile
-  using acc_t = typename std::conditional<MODE == MODE_FP4, v4f, v4i>::type;
+  // 16-byte activation parts per tile: 64 codes of 8, 6 (e2m3 fields) or 4 bits
+  static constexpr int AW = (MODE == MODE_INT8) ? 4 : (MODE == MODE_E2M3) ? 3 : 2;
+  using acc_t = typename std::conditional<MODE == MODE_FP4 || MODE == MODE_E2M3, v4f, v4i>::type;
 };
 
 // One 64-k tile of lane group g: activation parts a (this lane's token row) x
@@ -58,6 +62,18 @@ __device__ __forceinline__ void mfma_tile(typename TileOps<MODE>::acc_t& acc, co
     acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_v4i(a[1]), widen_w_a8(wv.y), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_v4i(a[2]), widen_w_a8(wv.z), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_v4i(a[3]), widen_w_a8(wv.w), acc, 0, 0, 0);
+  } else if constexpr (MODE == MODE_E2M3) {
+    // the tile's 48 bytes: the first 16 bytes of the fields of values 0..31,
+    // the same of values 32..63, then the last 8 bytes of each.  An fp6
+    // operand is the first six words of its vector, so each is the
+    // concatenation of one 16-byte part and the tail part (words 6, 7 unused)
+    const v4i p0 = as_v4i(a[0]), p1 = as_v4i(a[1]), p2 = as_v4i(a[2]);
+    const v8i x0 = __builtin_shufflevector(p0, p2, 0, 1, 2, 3, 4, 5, 6, 7);
+    const v8i x1 = __builtin_shufflevector(p1, p2, 0, 1, 2, 3, 6, 7, 4, 5);
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x0, fp4_weights(wv.x, wv.y), acc, 2, 4, 0, kE2m3ActScale, 0,
+                                                           kE2m1WeightScale);
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x1, fp4_weights(wv.z, wv.w), acc, 2, 4, 0, kE2m3ActScale, 0,
+                                                           kE2m1WeightScale);
   } else {
     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fp4_operand(a[0].x, a[0].y, a[0].z, a[0].w),
                                                            fp4_weights(wv.x, wv.y), acc, 4, 4, 0, 127, 0,
@@ -105,6 +121,9 @@ __device__ __forceinline__ void gemv_epilogue(typename TileOps<MODE>::acc_t acc,
     if constexpr (MODE == MODE_FP4) {
       accf = s[e];
       if (acc_dbg) static_cast<float*>(acc_dbg)[m * N + n] = accf;
+    } else if constexpr (MODE == MODE_E2M3) {
+      accf = s[e];  // an exact integer: |sum q*t| <= 8K < 2^24
+      if (acc_dbg) static_cast<int32_t*>(acc_dbg)[m * N + n] = static_cast<int32_t>(accf);
     } else {
       const int32_t a = s[e] >> acc_shift<MODE>();
       if (acc_dbg) static_cast<int32_t*>(acc_dbg)[m * N + n] = a;
@@ -363,6 +382,9 @@ hipError_t launch_gemv_ex(int mode, const void* codes, const float* sx, int64_t 
       break;
     case MODE_FP4:
       launch_modes<MODE_FP4, 4>(A, sx, m, K, w_packed, beta, N, y, acc_dbg, resid, split, s);
+      break;
+    case MODE_E2M3:
+      launch_modes<MODE_E2M3, 4>(A, sx, m, K, w_packed, beta, N, y, acc_dbg, resid, split, s);
       break;
     default:
       launch_modes<MODE_INT8, 8>(A, sx, m, K, w_packed, beta, N, y, acc_dbg, resid, split, s);

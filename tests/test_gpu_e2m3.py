@@ -183,3 +183,29 @@ def test_e2m3_bench_shapes():
     rows = np.array([0, 1, 1000, 2047])
     q, _ = act4.quantize_int4(x.f32[rows])
     assert_same(host(c6)[rows], act4.pack_int4_e2m3(q), "bench-shape codes")
+
+
+@pytest.mark.parametrize("M", [1, 8, 16])
+@pytest.mark.parametrize("K,N", [(4096, 12288), (4096, 22016), (4160, 48), (11008, 4096)])
+def test_e2m3_decode_gemv_equals_int4(M, K, N):
+    """Decode shapes (M <= 16 tokens, the weight-streaming GEMV on the fp6 x fp4
+    instruction): fused q/k/v and gate/up widths at K = 4096 with outlier channels,
+    a K whose 65 tiles split unevenly over the waves, and K = 11008; accumulators
+    and y equal the INT4 nibble path bit for bit."""
+    x = synth.decode_activations(seed=700 + M + K, M=M, K=K)
+    w = synth.weight_tensor(701 + N, N, K)
+    packed, beta = bw.bw_pack_ternary(f32_dev(w), bw.BW_ROLE_A4)
+    c6, s6 = bw.bw_quantize(bf16_dev(x), E6)
+    c4, s4 = bw.bw_quantize(bf16_dev(x), I4)
+    acc6 = torch.empty((M, N), dtype=torch.int32, device=DEV)
+    acc4 = torch.empty((M, N), dtype=torch.int32, device=DEV)
+    y6 = bw.bw_bitlinear_a4(c6, s6, E6, packed, beta, acc_dbg=acc6)
+    y4 = bw.bw_bitlinear_a4(c4, s4, I4, packed, beta, acc_dbg=acc4)
+    assert torch.equal(acc6, acc4), f"decode acc {M}x{K}x{N}"
+    assert torch.equal(y6.view(torch.int32), y4.view(torch.int32)), f"decode y {M}x{K}x{N}"
+    if N <= 4096:  # and the oracle on a few columns
+        q, s = act4.quantize_int4(x.f32)
+        t, b = ternary.quantize_weights(w)
+        cols = np.array([0, 1, N // 2, N - 1])
+        ref = bitlinear.contract(q, t[cols])
+        assert_same(host(acc6)[:, cols], ref.astype(np.int32), f"decode acc vs oracle {M}x{K}x{N}")
