@@ -215,7 +215,13 @@ class Bench:
                 yf=t.empty((M, self.n_gu), dtype=t.float32, device=dev),
                 c8a=t.empty((M, HIDDEN), dtype=t.int8, device=dev), s8a=t.empty(M, dtype=t.float32, device=dev),
                 c8f=t.empty((M, HIDDEN), dtype=t.int8, device=dev), s8f=t.empty(M, dtype=t.float32, device=dev),
+                # the same INT4 values as e2m3 fields, quantized once here (rows a5e)
+                c6a=t.empty((M, HIDDEN * 3 // 4), dtype=t.uint8, device=dev), s6a=t.empty(M, dtype=t.float32, device=dev),
+                c6f=t.empty((M, HIDDEN * 3 // 4), dtype=t.uint8, device=dev), s6f=t.empty(M, dtype=t.float32, device=dev),
             )
+            d = self.dec[M]
+            bw.bw_quantize(xa, bw.BW_ACT_INT4_E2M3, d["c6a"], d["s6a"])
+            bw.bw_quantize(xf, bw.BW_ACT_INT4_E2M3, d["c6f"], d["s6f"])
         # ---------------- decode down_proj / out_proj, one token: sparsified INT8 codes
         # and 32 layers of weights in both the tiled and the K-major layout
         gd, ud = synth.gate_up(S + 31, 1, FFN)
@@ -406,6 +412,19 @@ class Bench:
             R.append((f"a5_gemv_gateup_m{Md}", "GB/s", gemv_bytes(Md, self.n_gu, K),
                       [lambda d=d, gp=gp, gb=gb: bw.bw_bitlinear_a4(d["cf"], d["sf"], bw.BW_ACT_INT4, gp, gb, d["yf"])
                        for _, _, gp, gb in self.layers]))
+            if Md in (1, 8):
+                # the same products over the INT4 values stored as e2m3 fields (fp6 x fp4 GEMV)
+                def gemv6_bytes(M, N, K):
+                    return N * K / 4 + 4 * N + M * K * 3 / 4 + 4 * M + 4 * M * N
+
+                R.append((f"a5e_gemv_qkv_e2m3_m{Md}", "GB/s", gemv6_bytes(Md, self.n_qkv, K),
+                          [lambda d=d, qp=qp, qb=qb: bw.bw_bitlinear_a4(d["c6a"], d["s6a"], bw.BW_ACT_INT4_E2M3, qp,
+                                                                        qb, d["ya"])
+                           for qp, qb, _, _ in self.layers]))
+                R.append((f"a5e_gemv_gateup_e2m3_m{Md}", "GB/s", gemv6_bytes(Md, self.n_gu, K),
+                          [lambda d=d, gp=gp, gb=gb: bw.bw_bitlinear_a4(d["c6f"], d["s6f"], bw.BW_ACT_INT4_E2M3, gp,
+                                                                        gb, d["yf"])
+                           for _, _, gp, gb in self.layers]))
             if Md == DECODE_MS[0]:
                 # read ceilings: the same 32 layers' weight bytes read once in the GEMV's access
                 # pattern, right behind GEMV rows (same cache state: no dirty output lines of the

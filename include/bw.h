@@ -157,7 +157,8 @@ bw_status bw_quantize(const void* x, bw_dtype x_dtype, int64_t M, int64_t K, bw_
  * acc_dbg: NULL, or [M][N] receiving acc (int32 for BW_ACT_INT4 and
  * BW_ACT_INT4_E2M3, fp32 for BW_ACT_FP4_E2M1), for exactness checks.
  * BW_ACT_INT4_E2M3 gives the same acc and y as BW_ACT_INT4 on the same
- * values (bit for bit) from the fp6 x fp4 matrix instruction, at any M; it
+ * values (bit for bit) from the fp6 x fp4 matrix instruction, at any M (the
+ * weight-streaming GEMV up to 16 tokens, the LDS GEMM above); it
  * returns BW_ERR_UNSUPPORTED when M*3K/4 or N*K/4 reaches 2^31 bytes.
  * Shapes: K % 64 == 0, K <= 131072, N % 16 == 0.
  * ------------------------------------------------------------------------ */
