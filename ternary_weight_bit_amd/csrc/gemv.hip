@@ -338,6 +338,8 @@ __global__ __launch_bounds__(256) void k_gemv_quant(const void* __restrict__ X, 
   gemv_epilogue<MODE, WAVES>(acc, part, M, N, nb, sxm, bn, y, acc_dbg, resid, split);
 }
 
+constexpr int64_t kGemvWideN = 16384;
+
 template <int MODE, int WAVES>
 void launch_modes(const uint8_t* A, const float* sx, int m, int64_t K, const uint8_t* w, const float* beta,
                   int64_t N, float* y, void* acc_dbg, const float* resid, int64_t split, hipStream_t s) {
@@ -376,15 +378,21 @@ hipError_t launch_gemv_ex(int mode, const void* codes, const float* sx, int64_t 
                           const float* resid, int64_t split, hipStream_t s) {
   const uint8_t* A = static_cast<const uint8_t*>(codes);
   const int m = static_cast<int>(M);
+  // 4-bit codes: four waves split K; from N = 16384 on (1024 workgroups and
+  // more, e.g. the fused gate/up width) eight waves, measured faster there and
+  // slower on the 768 workgroups of the fused q/k/v width
+  const bool wide = N >= kGemvWideN;
   switch (mode) {
     case MODE_INT4:
-      launch_modes<MODE_INT4, 4>(A, sx, m, K, w_packed, beta, N, y, acc_dbg, resid, split, s);
+      if (wide) launch_modes<MODE_INT4, 8>(A, sx, m, K, w_packed, beta, N, y, acc_dbg, resid, split, s);
+      else launch_modes<MODE_INT4, 4>(A, sx, m, K, w_packed, beta, N, y, acc_dbg, resid, split, s);
       break;
     case MODE_FP4:
       launch_modes<MODE_FP4, 4>(A, sx, m, K, w_packed, beta, N, y, acc_dbg, resid, split, s);
       break;
     case MODE_E2M3:
-      launch_modes<MODE_E2M3, 4>(A, sx, m, K, w_packed, beta, N, y, acc_dbg, resid, split, s);
+      if (wide) launch_modes<MODE_E2M3, 8>(A, sx, m, K, w_packed, beta, N, y, acc_dbg, resid, split, s);
+      else launch_modes<MODE_E2M3, 4>(A, sx, m, K, w_packed, beta, N, y, acc_dbg, resid, split, s);
       break;
     default:
       launch_modes<MODE_INT8, 8>(A, sx, m, K, w_packed, beta, N, y, acc_dbg, resid, split, s);
